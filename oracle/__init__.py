@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for Kimi Delta Attention (ctypes wrapper of kda_oracle.c).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
+smoke check and the CPU-baseline leg of the benchmark may import this
+module.  It shares no code with the HIP path and the HIP path never calls it.
+
+Every function takes numpy arrays of any real dtype, converts them to
+contiguous float64 (bf16 inputs must be expanded to float first; the
+conversion is exact) and returns float64 arrays.  Layouts follow the
+operator's: q, k, g [T, H, d_k]; v, o [T, H, d_v]; beta [T, H];
+states [N, H, d_k, d_v]; cu_seqlens [N + 1].
+
+Parity status: every function here is pinned by tests/test_oracle.py to
+closed forms, special cases and brute-force dense products taken from the
+pages (see that file); none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int64)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from oracle import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.kda_oracle_num_threads.restype = ctypes.c_int
+    lib.kda_oracle_recurrent.argtypes = [_dp] * 5 + [_ip] + [_i64] * 5 + [_dp] * 3
+    lib.kda_oracle_chunked.argtypes = [_dp] * 5 + [_ip] + [_i64] * 6 + [_dp] * 3
+    lib.kda_oracle_decode.argtypes = [_dp] * 7 + [_i64] * 4
+    lib.kda_oracle_chunk_cumsum.argtypes = [_dp, _ip] + [_i64] * 5 + [_dp]
+    lib.kda_oracle_ut_inverse.argtypes = [_dp, _i64, _dp]
+    for f in ("kda_oracle_recurrent", "kda_oracle_chunked", "kda_oracle_decode",
+              "kda_oracle_chunk_cumsum", "kda_oracle_ut_inverse"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
+    return int(_load().kda_oracle_num_threads())
+
+
+def _f64(a):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    return a, a.ctypes.data_as(_dp)
+
+
+def _cu(cu_seqlens):
+    if cu_seqlens is None:
+        return None, None
+    c = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    return c, c.ctypes.data_as(_ip)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} rejected its arguments (code {rc})")
+
+
+def _dims(q, v, num_seqs, cu_seqlens):
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is not None:
+        n = len(cu_seqlens) - 1
+    else:
+        n = 1 if num_seqs is None else int(num_seqs)
+    return T, H, dk, dv, n
+
+
+def recurrent(q, k, v, g, beta, cu_seqlens=None, num_seqs=None,
+              initial_state=None):
+    """Token-by-token recurrence.  Returns (o [T,H,d_v], S_final [N,H,d_k,d_v])."""
+    lib = _load()
+    q, qp = _f64(q); k, kp = _f64(k); v, vp = _f64(v)
+    g, gp = _f64(g); beta, bp = _f64(beta)
+    cu, cp = _cu(cu_seqlens)
+    T, H, dk, dv, n = _dims(q, v, num_seqs, cu)
+    s0, sp = _f64(initial_state)
+    o = np.zeros((T, H, dv))
+    sf = np.zeros((n, H, dk, dv))
+    _check(lib.kda_oracle_recurrent(qp, kp, vp, gp, bp, cp, n, T, H, dk, dv, sp,
+                                    o.ctypes.data_as(_dp), sf.ctypes.data_as(_dp)),
+           "kda_oracle_recurrent")
+    return o, sf
+
+
+def chunked(q, k, v, g, beta, chunk_size, cu_seqlens=None, num_seqs=None,
+            initial_state=None):
+    """Chunk-parallel form (for checking it against `recurrent`)."""
+    lib = _load()
+    q, qp = _f64(q); k, kp = _f64(k); v, vp = _f64(v)
+    g, gp = _f64(g); beta, bp = _f64(beta)
+    cu, cp = _cu(cu_seqlens)
+    T, H, dk, dv, n = _dims(q, v, num_seqs, cu)
+    s0, sp = _f64(initial_state)
+    o = np.zeros((T, H, dv))
+    sf = np.zeros((n, H, dk, dv))
+    _check(lib.kda_oracle_chunked(qp, kp, vp, gp, bp, cp, n, T, H, dk, dv,
+                                  int(chunk_size), sp, o.ctypes.data_as(_dp),
+                                  sf.ctypes.data_as(_dp)),
+           "kda_oracle_chunked")
+    return o, sf
+
+
+def decode(q, k, v, g, beta, state):
+    """One recurrent step on a batch of states.  q,k,g [B,H,d_k]; v [B,H,d_v];
+    beta [B,H]; state [B,H,d_k,d_v].  Returns (o, new_state); the input is not
+    modified."""
+    lib = _load()
+    q, qp = _f64(q); k, kp = _f64(k); v, vp = _f64(v)
+    g, gp = _f64(g); beta, bp = _f64(beta)
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    o = np.zeros((B, H, dv))
+    _check(lib.kda_oracle_decode(qp, kp, vp, gp, bp, st.ctypes.data_as(_dp),
+                                 o.ctypes.data_as(_dp), B, H, dk, dv),
+           "kda_oracle_decode")
+    return o, st
+
+
+def chunk_cumsum(g, chunk_size, cu_seqlens=None, num_seqs=None):
+    """Chunk-local inclusive cumulative sum of g = log(alpha), [T, H, d_k]."""
+    lib = _load()
+    g, gp = _f64(g)
+    cu, cp = _cu(cu_seqlens)
+    T, H, dk = g.shape
+    n = len(cu) - 1 if cu is not None else (1 if num_seqs is None else int(num_seqs))
+    out = np.zeros_like(g)
+    _check(lib.kda_oracle_chunk_cumsum(gp, cp, n, T, H, dk, int(chunk_size),
+                                       out.ctypes.data_as(_dp)),
+           "kda_oracle_chunk_cumsum")
+    return out
+
+
+def ut_inverse(A):
+    """(I + strictly_lower(A))^{-1} by forward substitution."""
+    lib = _load()
+    A, ap = _f64(A)
+    n = A.shape[0]
+    out = np.zeros((n, n))
+    _check(lib.kda_oracle_ut_inverse(ap, n, out.ctypes.data_as(_dp)),
+           "kda_oracle_ut_inverse")
+    return out
