@@ -1,0 +1,139 @@
+// kda_common.hpp -- device-side building blocks shared by the KDA kernels:
+// element types, 16x16 MFMA tiles for gfx950, fragment loads and
+// conversions.
+//
+// Matrix-core tile convention (verified on gfx950 for both instructions):
+// a 16 x 16 output tile D = A (16 x K) * B (K x 16) is accumulated over
+// K-steps of 32.  In each K-step, lane l (0..63) supplies eight A values
+// A[l % 16][8 * (l / 16) + i] and eight B values B[8 * (l / 16) + i][l % 16],
+// i = 0..7, and holds the four outputs D[4 * (l / 16) + i][l % 16], i = 0..3.
+//   bf16: one v_mfma_f32_16x16x32_bf16 per K-step.
+//   fp32: eight v_mfma_f32_16x16x4_f32, instruction i taking element i; each
+//         covers k = 8 * (l / 16) + i over the four lane groups, so the eight
+//         together cover the same 32 values of k.
+// Both A and B fragments are therefore eight CONTIGUOUS elements of a row of
+// a row-major buffer (A stored [m][k], B stored transposed as [n][k]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ f32x4 mma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma_k32(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+// fp32 16x16x16 product step (K = 16): lane l supplies A[l%16][4*(l/16)+i]
+// and B[4*(l/16)+i][l%16] for i = 0..3 through four 16x16x4 instructions.
+__device__ __forceinline__ f32x4 mma_f32_k16(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- conversions -------------------------------------------------------
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ---- 8-element contiguous loads/stores (16 B for bf16, 32 B for fp32) --
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type load8(const T *p);
+
+template <>
+__device__ __forceinline__ bf16x8 load8<bf16>(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <>
+__device__ __forceinline__ f32x8 load8<float>(const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16 *p, const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+  *reinterpret_cast<bf16x8 *>(p) = r;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float (&x)[8]) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T *p, float (&x)[8]) {
+  const typename Frag<T>::type v = load8<T>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = to_f32(v[i]);
+}
+
+// 8 fp32 values converted to a fragment of T.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type frag_from_f32(const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  typename Frag<T>::type r;
+  r[0] = from_f32<T>(a[0]); r[1] = from_f32<T>(a[1]);
+  r[2] = from_f32<T>(a[2]); r[3] = from_f32<T>(a[3]);
+  r[4] = from_f32<T>(b[0]); r[5] = from_f32<T>(b[1]);
+  r[6] = from_f32<T>(b[2]); r[7] = from_f32<T>(b[3]);
+  return r;
+}
+
+// 4 consecutive elements (one D-layout column strip) as fp32 / from fp32.
+template <typename T>
+__device__ __forceinline__ f32x4 load4_f32(const T *p);
+template <>
+__device__ __forceinline__ f32x4 load4_f32<bf16>(const bf16 *p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <>
+__device__ __forceinline__ f32x4 load4_f32<float>(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+template <typename T>
+__device__ __forceinline__ void store4_f32(T *p, f32x4 x);
+template <>
+__device__ __forceinline__ void store4_f32<bf16>(bf16 *p, f32x4 x) {
+  *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+template <>
+__device__ __forceinline__ void store4_f32<float>(float *p, f32x4 x) {
+  *reinterpret_cast<f32x4 *>(p) = x;
+}
+
+// Lane index helpers for the tile convention above.
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+}  // namespace kda

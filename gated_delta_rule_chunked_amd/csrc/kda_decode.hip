@@ -1,0 +1,145 @@
+// kda_decode.hip -- one recurrent KDA step for a batch of fp32 states.
+//
+// Per (sequence, head) with state S (d x d, rows = key channels):
+//   S' = Diag(alpha) S            forget, one rate per key channel
+//   u  = beta (v - S'^T k)        delta-rule correction
+//   o  = S'^T q + (k . q) u       read-out of the updated state
+//   S  = S' + k u^T               erase + write
+// (mkdocs.reaper.mx "Attention lineaire et recurrence", section "Kimi Delta
+// Attention = les trois remedes combines": forget, erase, write; docsaid.org
+// "Kimi Linear", section "KDA : une decroissance propre a chaque canal".)
+// The two reductions only need S^T (alpha * k) and S^T (alpha * q), so each
+// state is streamed through registers once: one coalesced 16-byte read and
+// one 16-byte write per four values.  Decode is bound by HBM bandwidth
+// (about one flop per byte).
+//
+// Block = one state.  Thread t owns float4 column group t % (d/4) and rows
+// r = t / (d/4) + i * (threads / (d/4)); at every step i the block reads or
+// writes a contiguous run of rows.  Column sums are reduced over the lanes of
+// a wavefront with cross-lane shuffles and over wavefronts through LDS.
+#include "kda_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    float *__restrict__ state, T *__restrict__ o) {
+  constexpr int NCQ = D / 4;         // float4 column groups
+  constexpr int NRG = NT / NCQ;      // row groups
+  constexpr int RPT = D / NRG;       // rows per thread
+  constexpr int NW = NT / 64;        // wavefronts
+  static_assert(NT % 64 == 0 && 64 % NCQ == 0 && D % NRG == 0, "decode shape");
+
+  __shared__ f32x4 s_x[NW][NCQ];
+  __shared__ f32x4 s_y[NW][NCQ];
+  __shared__ float s_kq[NW];
+
+  const int64_t p = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cq = tid % NCQ, rg = tid / NCQ;
+  float *S = state + p * D * D;
+  const T *qp = q + p * D;
+  const T *kp = k + p * D;
+  const float *gp = g + p * D;
+
+  f32x4 Sv[RPT];
+  float a[RPT], kr[RPT];
+  f32x4 x = zero4(), y = zero4();
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * NRG;
+    Sv[i] = *reinterpret_cast<const f32x4 *>(S + r * D + 4 * cq);
+    a[i] = __expf(gp[r]);
+    kr[i] = to_f32(kp[r]);
+    const float qr = to_f32(qp[r]);
+    const float ka = a[i] * kr[i], qa = a[i] * qr;
+    x += Sv[i] * ka;
+    y += Sv[i] * qa;
+    kq += kr[i] * qr;
+  }
+  // reduce over the row groups of this wavefront (lanes cq + NCQ * m)
+#pragma unroll
+  for (int off = NCQ; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] += __shfl_xor(x[e], off);
+      y[e] += __shfl_xor(y[e], off);
+    }
+    kq += __shfl_xor(kq, off);
+  }
+  const int wave = tid >> 6, lane = tid & 63;
+  if (lane < NCQ) {
+    s_x[wave][lane] = x;
+    s_y[wave][lane] = y;
+  }
+  // kq: each row group summed its own rows and the shuffles added the row
+  // groups of this wave, so any lane holds the wave's part.
+  if (lane == 0) s_kq[wave] = kq;
+  __syncthreads();
+  f32x4 xs = zero4(), ys = zero4();
+  float kqs = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < NW; ++wv) {
+    xs += s_x[wv][cq];
+    ys += s_y[wv][cq];
+    kqs += s_kq[wv];
+  }
+  const float b = beta[p];
+  f32x4 vv;
+  {
+    const T *vp = v + p * D + 4 * cq;
+    vv = f32x4{to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
+  }
+  const f32x4 u = b * (vv - xs);
+  if (rg == 0) {
+    const f32x4 ov = ys + kqs * u;
+    store4_f32<T>(o + p * D + 4 * cq, ov);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * NRG;
+    *reinterpret_cast<f32x4 *>(S + r * D + 4 * cq) = a[i] * Sv[i] + kr[i] * u;
+  }
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, float *state,
+                                  void *o, int pairs, int d, hipStream_t s) {
+  const T *qq = reinterpret_cast<const T *>(q);
+  const T *kk = reinterpret_cast<const T *>(k);
+  const T *vv = reinterpret_cast<const T *>(v);
+  T *oo = reinterpret_cast<T *>(o);
+  switch (d) {
+    case 32:
+      hipLaunchKernelGGL((decode_kernel<T, 32, 64>), dim3(pairs), dim3(64), 0, s, qq, kk,
+                         vv, g, beta, state, oo);
+      break;
+    case 64:
+      hipLaunchKernelGGL((decode_kernel<T, 64, 256>), dim3(pairs), dim3(256), 0, s, qq,
+                         kk, vv, g, beta, state, oo);
+      break;
+    case 128:
+      hipLaunchKernelGGL((decode_kernel<T, 128, 256>), dim3(pairs), dim3(256), 0, s, qq,
+                         kk, vv, g, beta, state, oo);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state, void *o, int batch, int heads,
+                         int d, kda_dtype dt, hipStream_t stream) {
+  const int pairs = batch * heads;
+  if (dt == KDA_DTYPE_BF16)
+    return launch_decode_t<bf16>(q, k, v, g, beta, state, o, pairs, d, stream);
+  return launch_decode_t<float>(q, k, v, g, beta, state, o, pairs, d, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,86 @@
+// kda_internal.hpp -- host-side plumbing shared by the C ABI and the kernel
+// launchers: the prefill workspace layout and the launcher entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Prefill workspace layout.  Per-chunk products are stored per (chunk, head)
+// tile, tile index = chunk * H + head, so that every tile is one contiguous
+// block; chunk ids enumerate the chunks of sequence 0, then sequence 1, ...
+//   chunk_info  int4 [max_chunks]    (sequence, first token, rows, 0)
+//   seq_first   int  [num_seqs]      first chunk id of each non-empty sequence
+//   gc          fp32 [T, H, D]       chunk-local cumulative log-decay
+//   qt          elem [tiles][C][D]   Q * exp(G)
+//   w           elem [tiles][C][D]   WY factor W = T Diag(beta) (K * exp(G))
+//   ut          elem [tiles][D][C]   WY factor U = T Diag(beta) V, transposed
+//   ket         elem [tiles][D][CK]  K * exp(G_last - G), transposed
+//   p           elem [tiles][C][CK]  lower-triangular (Q*exp(G)) (K*exp(-G))^T
+// CK = max(C, 32) is the token extent padded to one 32-wide matrix-core
+// K-step (the padding columns are zero).
+struct FwdLayout {
+  int64_t max_chunks = 0;
+  int64_t tiles = 0;
+  size_t chunk_info = 0, seq_first = 0, gc = 0, qt = 0, w = 0, ut = 0, ket = 0,
+         p = 0, total = 0;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// max_chunks: chunk count bound valid for any split of T tokens into N
+// sequences (sum of ceil(len_i / C) <= (T + N (C - 1)) / C).
+inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
+                            int64_t C, size_t elem) {
+  FwdLayout L;
+  const int64_t CK = C < 32 ? 32 : C;
+  L.max_chunks = (T + N * (C - 1)) / C;
+  L.tiles = L.max_chunks * H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  L.chunk_info = take(sizeof(int) * 4 * (size_t)L.max_chunks);
+  L.seq_first = take(sizeof(int) * (size_t)N);
+  L.gc = take(sizeof(float) * (size_t)(T * H * D));
+  L.qt = take(elem * (size_t)(L.tiles * C * D));
+  L.w = take(elem * (size_t)(L.tiles * C * D));
+  L.ut = take(elem * (size_t)(L.tiles * D * C));
+  L.ket = take(elem * (size_t)(L.tiles * D * CK));
+  L.p = take(elem * (size_t)(L.tiles * C * CK));
+  L.total = off;
+  return L;
+}
+
+// Arguments common to the three prefill launches.
+struct FwdArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const int *cu_seqlens;  // device, or nullptr for equal lengths
+  int num_seqs, num_heads, d, chunk;
+  int64_t total_tokens;
+  int seq_len;            // equal-length sequences: tokens per sequence
+  int64_t grid_chunks;    // chunk ids to launch (exact when equal lengths)
+  const float *s0;
+  float *s_final;
+  void *o;
+  char *ws;
+  FwdLayout lay;
+  hipStream_t stream;
+};
+
+hipError_t launch_chunk_cumsum(const FwdArgs &a);
+hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
+hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
+hipError_t launch_decode(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta, float *state,
+                         void *o, int batch, int heads, int d, kda_dtype dt,
+                         hipStream_t stream);
+
+}  // namespace kda

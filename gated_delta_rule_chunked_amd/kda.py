@@ -1,0 +1,186 @@
+"""Python binding of libkda.so (include/kda.h): argument marshalling only.
+
+Torch provides device memory and the current HIP stream; every step of the
+operator runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or the tensors are not on a ROCm device, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkda.so")
+
+KDA_SUCCESS = 0
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    """A KDA call returned a non-success status, or the library is missing."""
+
+
+def library():
+    """Load libkda.so (once).  Raises KdaError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise KdaError(
+            f"{library_path} is not built; run "
+            "`python -m gated_delta_rule_chunked_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(library_path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_version.restype = ctypes.c_int
+    lib.kda_fwd_chunked_workspace_size.restype = sz
+    lib.kda_fwd_chunked_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_fwd_chunked.restype = ctypes.c_int
+    lib.kda_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                    ctypes.c_int, vp, vp, vp, vp, sz, vp]
+    lib.kda_fwd_chunked_stage.restype = ctypes.c_int
+    lib.kda_fwd_chunked_stage.argtypes = [ctypes.c_int] + lib.kda_fwd_chunked.argtypes
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                    ctypes.c_int, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != KDA_SUCCESS:
+        name = library().kda_status_string(status).decode()
+        raise KdaError(f"{what} failed: {name}")
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t == torch.float32:
+        return KDA_DTYPE_F32
+    raise KdaError(f"unsupported operand dtype {t}; use bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise KdaError(f"{name} must be a ROCm device tensor")
+    if not t.is_contiguous():
+        raise KdaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise KdaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise KdaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int,
+                   chunk_size: int, dtype: torch.dtype) -> int:
+    """Bytes of workspace fwd_chunked needs (0 = unsupported sizes)."""
+    return int(library().kda_fwd_chunked_workspace_size(
+        total_tokens, num_seqs, num_heads, head_dim, head_dim, chunk_size,
+        _dtype_code(dtype)))
+
+
+STAGES = {"cumsum": 0, "intra": 1, "inter": 2}
+
+
+def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                log_alpha: torch.Tensor, beta: torch.Tensor,
+                cu_seqlens: Optional[torch.Tensor] = None,
+                num_seqs: Optional[int] = None,
+                initial_state: Optional[torch.Tensor] = None,
+                chunk_size: int = 64, output_final_state: bool = True,
+                out: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                stage: Optional[str] = None,
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill (kda_fwd_chunked).
+
+    q, k: [T, H, d] and v: [T, H, d] (bf16 or fp32, same dtype);
+    log_alpha: [T, H, d] fp32; beta: [T, H] fp32;
+    cu_seqlens: int32 [N+1] device tensor, or None for `num_seqs` (default 1)
+    equal-length sequences; initial_state: fp32 [N, H, d, d] or None.
+    Returns (o [T, H, d] in v's dtype, final_state fp32 [N, H, d, d] or None).
+    `final_state` may be passed as the same tensor as `initial_state` to
+    update states in place.  `stage` ("cumsum", "intra" or "inter") runs only
+    that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
+    and `final_state` of a preceding call with the same arguments.
+    """
+    T, H, d = q.shape
+    dt = _dtype_code(q.dtype)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (T, H, d))
+    _need(log_alpha, "log_alpha", torch.float32, (T, H, d))
+    _need(beta, "beta", torch.float32, (T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n = cu_seqlens.numel() - 1
+    else:
+        n = 1 if num_seqs is None else int(num_seqs)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, d, d))
+    dev = q.device
+    o = out if out is not None else torch.empty((T, H, d), dtype=v.dtype, device=dev)
+    _need(o, "out", v.dtype, (T, H, d))
+    fs = None
+    if output_final_state:
+        fs = final_state if final_state is not None else torch.empty(
+            (n, H, d, d), dtype=torch.float32, device=dev)
+        _need(fs, "final_state", torch.float32, (n, H, d, d))
+    need = workspace_size(T, n, H, d, chunk_size, q.dtype)
+    if need == 0:
+        raise KdaError(f"unsupported sizes T={T} N={n} H={H} d={d} chunk={chunk_size} "
+                       f"dtype={q.dtype}")
+    if workspace is None or workspace.numel() < need:
+        if stage is not None:
+            raise KdaError("a single stage needs the workspace of a full call")
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), n,
+            T, H, d, d, chunk_size, dt, _ptr(initial_state), _ptr(fs), _ptr(o),
+            _ptr(workspace), workspace.numel(), _stream(dev))
+    if stage is None:
+        _check(library().kda_fwd_chunked(*args), "kda_fwd_chunked")
+    else:
+        if stage not in STAGES:
+            raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
+        _check(library().kda_fwd_chunked_stage(STAGES[stage], *args),
+               f"kda_fwd_chunked_stage({stage})")
+    return o, fs
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                log_alpha: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent KDA step (kda_decode_step); `state` is updated in place.
+
+    q, k, v: [B, H, d] (bf16 or fp32); log_alpha: [B, H, d] fp32;
+    beta: [B, H] fp32; state: [B, H, d, d] fp32.  Returns o [B, H, d].
+    """
+    B, H, d = q.shape
+    dt = _dtype_code(q.dtype)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (B, H, d))
+    _need(log_alpha, "log_alpha", torch.float32, (B, H, d))
+    _need(beta, "beta", torch.float32, (B, H))
+    _need(state, "state", torch.float32, (B, H, d, d))
+    o = out if out is not None else torch.empty((B, H, d), dtype=v.dtype, device=q.device)
+    _need(o, "out", v.dtype, (B, H, d))
+    _check(library().kda_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o), B, H,
+        d, d, dt, _stream(q.device)), "kda_decode_step")
+    return o

@@ -1,0 +1,184 @@
+/*
+ * kda.h -- C ABI of the Kimi Delta Attention (KDA) operator for AMD MI355X
+ * (gfx950).
+ *
+ * KDA is the gated delta rule with one decay per key channel.  For each
+ * sequence and head, with a state S of d_k x d_v values (rows = key
+ * channels, multiplied from the left):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * (docsaid.org "Kimi Linear -- L'oubli canal par canal", section "KDA : une
+ * decroissance propre a chaque canal", second display equation; the
+ * read-out is taken on the updated state.)  The decay is passed as its
+ * logarithm g = log(alpha) <= 0, per token, head and key channel.  The
+ * operator does not normalise q or k and applies no 1/sqrt(d) scale: the
+ * layer above L2-normalises q and k and produces beta with a sigmoid and
+ * alpha with its gate (same page, section "Les autres pieces").
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major and contiguous.  The
+ *     caller owns and allocates every buffer, the workspace included; the
+ *     library allocates nothing, keeps no state between calls and may be
+ *     called from several host threads on different streams.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return.  Errors raised while the kernels run surface at
+ *     the caller's next synchronisation, as for any HIP launch.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     failure nothing is enqueued and the status says why.  Device data
+ *     (cu_seqlens contents, tensor values) is never read on the host.
+ *   - dtype selects the type of q, k, v and o: KDA_DTYPE_BF16 (bf16
+ *     operands on the matrix cores with fp32 accumulation) or
+ *     KDA_DTYPE_F32 (fp32 throughout).  log_alpha, beta and the states are
+ *     always fp32.
+ *   - Supported head sizes: d_k == d_v in {32, 64, 128} for bf16 and
+ *     {32, 64} for fp32; other shapes return KDA_ERROR_NOT_SUPPORTED.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_SUCCESS = 0,
+  KDA_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, bad size, small workspace */
+  KDA_ERROR_NOT_SUPPORTED = 2, /* valid request this build has no kernel for */
+  KDA_ERROR_LAUNCH_FAILED = 3  /* the HIP runtime refused a kernel launch */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+/* Static, human-readable name of a status; never NULL. */
+const char *kda_status_string(kda_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int kda_version(void);
+
+/*
+ * Bytes of device workspace kda_fwd_chunked needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  The value depends only on the
+ * arguments, never on cu_seqlens contents: for varlen calls it covers the
+ * largest chunk count any split of total_tokens into num_seqs sequences can
+ * produce.
+ */
+size_t kda_fwd_chunked_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t d_k,
+                                      int32_t d_v, int32_t chunk_size,
+                                      kda_dtype dtype);
+
+/*
+ * Chunked prefill over one or more packed sequences.
+ *
+ * Splits every sequence into chunks of chunk_size tokens (the last chunk of
+ * a sequence may be shorter; chunks never straddle sequences), carries the
+ * state from chunk to chunk, and inside a chunk replaces the token-by-token
+ * updates with dense products: the decay-scaled K K^T and Q K^T blocks, the
+ * UT-transform inverse (I + A)^{-1} of the strictly lower A by forward
+ * substitution, and the WY factors W and U (fr.news.hada.io Kimi Linear
+ * summary, section "Algorithme parallele par chunks"; mkdocs.reaper.mx
+ * "Attention lineaire et recurrence", section "Le calcul par blocs"; the
+ * result equals the recurrence up to rounding).
+ *
+ *   q, k        [total_tokens, H, d_k]  dtype
+ *   v           [total_tokens, H, d_v]  dtype
+ *   log_alpha   [total_tokens, H, d_k]  fp32, g = log(alpha), finite, <= 0
+ *   beta        [total_tokens, H]       fp32, in [0, 1]
+ *   cu_seqlens  [num_seqs + 1] int32 device array of sequence offsets
+ *               (0 = cu[0] <= cu[1] <= ... <= cu[num_seqs] = total_tokens),
+ *               or NULL for num_seqs sequences of total_tokens/num_seqs
+ *               tokens each.  Empty sequences are allowed.  Contents that
+ *               break these rules are undefined behaviour.
+ *   initial_state [num_seqs, H, d_k, d_v] fp32, or NULL for zero states.
+ *               May be the same buffer as final_state (updated in place).
+ *   final_state [num_seqs, H, d_k, d_v] fp32, or NULL to skip it.  An empty
+ *               sequence's final state is its initial state.
+ *   o           [total_tokens, H, d_v]  dtype (output)
+ *   workspace   device buffer of at least kda_fwd_chunked_workspace_size()
+ *               bytes, 256-byte aligned; contents on entry are ignored and
+ *               are clobbered.  Calls that share a workspace must be
+ *               ordered (same stream or synchronised).
+ *   stream      hipStream_t or NULL.
+ *
+ * Precondition of the chunk algorithm (mkdocs.reaper.mx, section "Le piege
+ * numerique de la decroissance cumulee"): inside any chunk the summed
+ * log-decay of every channel must stay above -80, so that exp(-G) stays in
+ * fp32/bf16 range.  Larger decays give inf/NaN outputs; use a smaller
+ * chunk_size for such inputs.
+ *
+ * q, k, v, o and the states must be 16-byte aligned; log_alpha 16-byte;
+ * beta and cu_seqlens 4-byte.  chunk_size must be 16, 32 or 64.
+ * total_tokens may be 0 (then q, k, v, log_alpha, beta and o may be NULL).
+ */
+kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const int32_t *cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t num_heads,
+                           int32_t d_k, int32_t d_v, int32_t chunk_size,
+                           kda_dtype dtype, const float *initial_state,
+                           float *final_state, void *o, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * The three kernels of kda_fwd_chunked, in launch order.  Exposed so that a
+ * caller can time or schedule them separately.
+ */
+typedef enum {
+  KDA_STAGE_CUMSUM = 0, /* chunk table + chunk-local cumulative log-decay  */
+  KDA_STAGE_INTRA = 1,  /* per-chunk A, P, UT inverse, WY factors W and U  */
+  KDA_STAGE_INTER = 2   /* state carried over chunks: o and final_state    */
+} kda_fwd_stage;
+
+/*
+ * Enqueues one stage of kda_fwd_chunked with the same arguments and the
+ * same validation.  kda_fwd_chunked == CUMSUM, INTRA, INTER in order on one
+ * stream and one workspace.  A stage reads what the earlier stages left in
+ * the workspace, so it must follow them (stream order) with identical
+ * arguments; re-running a stage on an unchanged workspace reproduces its
+ * outputs (INTER is not idempotent when initial_state aliases final_state).
+ */
+kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void *k,
+                                 const void *v, const float *log_alpha,
+                                 const float *beta, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, int64_t total_tokens,
+                                 int32_t num_heads, int32_t d_k, int32_t d_v,
+                                 int32_t chunk_size, kda_dtype dtype,
+                                 const float *initial_state, float *final_state,
+                                 void *o, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * One recurrent decode step for a batch of states, updated in place.
+ * For each (b, h): S' = Diag(alpha) S; u = beta (v - S'^T k);
+ * o = S'^T q + (k . q) u; S <- S' + k u^T -- the same update and read-out as
+ * above for a single token (mkdocs.reaper.mx "Attention lineaire et
+ * recurrence", section "Kimi Delta Attention = les trois remedes combines";
+ * docsaid.org "Calculer le cache a la main": the state size does not depend
+ * on the context length).  Each state is read once and written once.
+ *
+ *   q, k        [batch, H, d_k]  dtype
+ *   v           [batch, H, d_v]  dtype
+ *   log_alpha   [batch, H, d_k]  fp32 (finite, <= 0)
+ *   beta        [batch, H]       fp32
+ *   state       [batch, H, d_k, d_v] fp32, read and overwritten
+ *   o           [batch, H, d_v]  dtype (output)
+ *
+ * q, k, v, o, log_alpha and state must be 16-byte aligned; beta 4-byte.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           float *state, void *o, int32_t batch,
+                           int32_t num_heads, int32_t d_k, int32_t d_v,
+                           kda_dtype dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,134 @@
+"""CPU-only checks of the C ABI library: it loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments on the host before any HIP
+call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "gated_delta_rule_chunked_amd", "libkda.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gated_delta_rule_chunked_amd import build
+        build.build()
+    from gated_delta_rule_chunked_amd import kda
+    return kda.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_fwd_chunked", "kda_fwd_chunked_stage", "kda_decode_step",
+              "kda_fwd_chunked_workspace_size", "kda_status_string", "kda_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kda.h but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_string(0) == b"KDA_SUCCESS"
+    assert lib.kda_status_string(1) == b"KDA_ERROR_INVALID_VALUE"
+    assert lib.kda_status_string(2) == b"KDA_ERROR_NOT_SUPPORTED"
+    assert lib.kda_status_string(3) == b"KDA_ERROR_LAUNCH_FAILED"
+    assert lib.kda_status_string(77) == b"KDA_UNKNOWN_STATUS"
+    assert lib.kda_version() >= 100
+
+
+def test_workspace_size(lib):
+    ws = lib.kda_fwd_chunked_workspace_size
+    assert ws(4096, 2, 8, 128, 128, 64, 1) > 0
+    assert ws(4096, 2, 8, 96, 96, 64, 1) == 0      # unsupported head size
+    assert ws(4096, 2, 8, 128, 128, 48, 1) == 0    # unsupported chunk
+    assert ws(4096, 2, 8, 128, 128, 64, 0) == 0    # fp32 needs d <= 64
+    assert ws(4096, 2, 8, 128, 64, 64, 1) == 0     # d_k != d_v
+    assert ws(-1, 2, 8, 128, 128, 64, 1) == 0
+    assert ws(0, 1, 1, 32, 32, 16, 0) > 0
+    # varlen bound: more sequences never need less workspace
+    assert ws(4096, 16, 8, 128, 128, 64, 1) >= ws(4096, 2, 8, 128, 128, 64, 1)
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def _fwd(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=None, n=2, T=256, H=2, dk=128,
+             dv=128, C=64, dt=1, s0=None, sf=None, o=FAKE, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(over)
+    return lib.kda_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"],
+                               a["T"], a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["s0"],
+                               a["sf"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fwd_rejects_bad_arguments_on_host(lib):
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, o=None) == 1
+    assert _fwd(lib, ws=None) == 1
+    assert _fwd(lib, wsb=16) == 1                    # workspace too small
+    assert _fwd(lib, q=ctypes.c_void_p((1 << 20) + 2)) == 1  # misaligned
+    assert _fwd(lib, ws=ctypes.c_void_p((1 << 20) + 64)) == 1
+    assert _fwd(lib, T=255) == 1                     # 255 % 2 sequences
+    assert _fwd(lib, n=0) == 1
+    assert _fwd(lib, H=0) == 1
+    assert _fwd(lib, T=-5) == 1
+    assert _fwd(lib, dt=7) == 1
+    assert _fwd(lib, dk=96, dv=96) == 2
+    assert _fwd(lib, dk=128, dv=64) == 2
+    assert _fwd(lib, C=128) == 2
+    assert _fwd(lib, dt=0) == 2                      # fp32 with d = 128
+
+
+def test_stage_rejects_bad_stage_and_arguments(lib):
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 256, 2, 128, 128, 64, 1, None, None,
+            FAKE, FAKE, 1 << 40, None)
+    assert lib.kda_fwd_chunked_stage(3, *args) == 1
+    assert lib.kda_fwd_chunked_stage(-1, *args) == 1
+    bad = list(args)
+    bad[0] = None
+    assert lib.kda_fwd_chunked_stage(1, *bad) == 1
+    bad = list(args)
+    bad[9] = bad[10] = 96
+    assert lib.kda_fwd_chunked_stage(2, *bad) == 2
+
+
+def _dec(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, st=FAKE, o=FAKE, B=4, H=2, dk=128,
+             dv=128, dt=1, stream=None)
+    a.update(over)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["st"], a["o"],
+                               a["B"], a["H"], a["dk"], a["dv"], a["dt"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments_on_host(lib):
+    assert _dec(lib, st=None) == 1
+    assert _dec(lib, o=None) == 1
+    assert _dec(lib, B=0) == 1
+    assert _dec(lib, dt=3) == 1
+    assert _dec(lib, st=ctypes.c_void_p((1 << 20) + 4)) == 1
+    assert _dec(lib, dk=48, dv=48) == 2
+    assert _dec(lib, dk=128, dv=32) == 2
+
+
+def test_binding_fails_loudly_without_device():
+    """The Python binding never falls back to a CPU path."""
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_chunked_amd import kda
+    x = torch.zeros((4, 1, 32), dtype=torch.float32)
+    with pytest.raises(kda.KdaError):
+        kda.fwd_chunked(x, x, x, x, torch.zeros((4, 1)))
+    with pytest.raises(kda.KdaError):
+        kda.decode_step(x, x, x, x, torch.zeros((4, 1)), torch.zeros((4, 1, 32, 32)))

@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerance: normwise max relative error max|x - ref| / max|ref| per output
+tensor, <= 1e-4 for fp32 operands and <= 2e-2 for bf16 operands (fp32
+accumulation and state).  Inputs come from the seeded generators; the oracle
+sees exactly the bits the device sees.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+from gated_delta_rule_chunked_amd import inputs as kin  # noqa: E402
+from kda_testutil import TOL, from_device, relerr, upload_prefill, to_device, f32_device  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _kda():
+    import gated_delta_rule_chunked_amd as kda
+    return kda
+
+
+def _run_gpu(w, chunk=None, in_place=False):
+    kda = _kda()
+    d = upload_prefill(w)
+    chunk = chunk or w.chunk_size
+    s0 = d["initial_state"]
+    kw = {}
+    if in_place and s0 is not None:
+        kw["final_state"] = s0
+    o, s = kda.fwd_chunked(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                           cu_seqlens=d["cu_seqlens"], num_seqs=d["num_seqs"],
+                           initial_state=s0, chunk_size=chunk, **kw)
+    torch.cuda.synchronize()
+    return from_device(o), from_device(s)
+
+
+def _oracle(w, heads=None):
+    q, k, v, g, b, s0 = w.f64()
+    if heads is not None:
+        q, k, v, g, b = q[:, heads], k[:, heads], v[:, heads], g[:, heads], b[:, heads]
+        s0 = None if s0 is None else s0[:, heads]
+    cu = None if w.cu_seqlens is None else w.cu_seqlens.astype(np.int64)
+    return oracle.recurrent(q, k, v, g, b, cu_seqlens=cu, num_seqs=w.num_seqs,
+                            initial_state=s0)
+
+
+def _check(w, o, s, heads=None, tol=None):
+    tol = tol if tol is not None else TOL[w.dtype]
+    o_ref, s_ref = _oracle(w, heads)
+    if heads is not None:
+        o, s = o[:, heads], s[:, heads]
+    eo, es = relerr(o, o_ref), relerr(s, s_ref)
+    print(f"  relerr o={eo:.3e} S={es:.3e} (tol {tol:g})", flush=True)
+    assert eo <= tol, f"output error {eo:.3e} > {tol}"
+    assert es <= tol, f"final-state error {es:.3e} > {tol}"
+    return eo, es
+
+
+@pytest.mark.parametrize("wid", [0, 1])
+def test_workload_full_parity(wid):
+    """Tiny fp32 (d=32, C=16) and the B=2, H=8, T=2048 bf16 prefill, every
+    output and final state against the oracle."""
+    print(f"[parity] workload {wid}", flush=True)
+    w = kin.workload(wid)
+    o, s = _run_gpu(w)
+    _check(w, o, s)
+
+
+def test_long_context_sampled_heads():
+    """B=1, H=32, T=32768 (512 chunks per chain): three heads checked in full."""
+    print("[parity] workload 2 (long), heads 0, 13, 31", flush=True)
+    w = kin.workload(2)
+    o, s = _run_gpu(w)
+    _check(w, o, s, heads=[0, 13, 31])
+
+
+def test_varlen_sampled_heads():
+    """16 packed sequences of U[512, 8192] tokens, H=16, initial states."""
+    print("[parity] workload 3 (varlen), heads 0, 9", flush=True)
+    w = kin.workload(3)
+    o, s = _run_gpu(w)
+    _check(w, o, s, heads=[0, 9])
+
+
+@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
+                                     (kin.F32, 32), (kin.F32, 64)])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_ragged_varlen_shapes(dtype, d, chunk):
+    """Several tiles, ragged tails, an empty sequence and a one-token sequence,
+    initial states, every head size and chunk size."""
+    print(f"[parity] ragged dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill(100 + d + chunk, H=3, d=d, dtype=dtype, chunk_size=chunk,
+                         lengths=[130, 0, 1, 64, 77], s0_std=0.05)
+    o, s = _run_gpu(w)
+    _check(w, o, s)
+    np.testing.assert_array_equal(s[1], w.initial_state[1])
+
+
+def test_chunk_size_invariance():
+    """The chunk form is exact: C = 16, 32 and 64 all match the oracle and
+    each other within the bf16 tolerance."""
+    print("[parity] chunk-size invariance", flush=True)
+    w = kin.make_prefill(7, B=2, T=500, H=4, d=128, dtype=kin.BF16, chunk_size=64)
+    outs = {}
+    for c in (16, 32, 64):
+        o, s = _run_gpu(w, chunk=c)
+        _check(w, o, s)
+        outs[c] = (o, s)
+    e = (relerr(outs[16][0], outs[64][0]), relerr(outs[16][1], outs[64][1]))
+    print("  C=16 vs C=64 o, S:", ["%.2e" % x for x in e])
+    assert max(e) < 2e-2
+
+
+def test_in_place_state_and_split_call():
+    """final_state may alias initial_state; a prefill split in two calls with
+    the state carried equals one call."""
+    print("[parity] in-place + split call", flush=True)
+    kda = _kda()
+    w = kin.make_prefill(11, B=1, T=300, H=2, d=128, dtype=kin.BF16, chunk_size=64,
+                         s0_std=0.05)
+    d = upload_prefill(w)
+    o_full, s_full = kda.fwd_chunked(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                                     initial_state=d["initial_state"])
+    st = d["initial_state"].clone()
+    cut = 137
+    o1, _ = kda.fwd_chunked(d["q"][:cut].contiguous(), d["k"][:cut].contiguous(),
+                            d["v"][:cut].contiguous(), d["log_alpha"][:cut].contiguous(),
+                            d["beta"][:cut].contiguous(), initial_state=st, final_state=st)
+    o2, _ = kda.fwd_chunked(d["q"][cut:].contiguous(), d["k"][cut:].contiguous(),
+                            d["v"][cut:].contiguous(), d["log_alpha"][cut:].contiguous(),
+                            d["beta"][cut:].contiguous(), initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    o_split = np.concatenate([from_device(o1), from_device(o2)])
+    o_ref, s_ref = _oracle(w)
+    e = (relerr(o_split, o_ref), relerr(from_device(st), s_ref),
+         relerr(o_split, from_device(o_full)))
+    print("  split o, split S, split-vs-single o:", ["%.2e" % x for x in e])
+    assert max(e) < 2e-2
+
+
+def test_deterministic():
+    """No atomics: two runs give identical bits."""
+    w = kin.workload(1)
+    o1, s1 = _run_gpu(w)
+    o2, s2 = _run_gpu(w)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_zero_tokens():
+    """total_tokens = 0: no output rows, final state = initial state."""
+    kda = _kda()
+    H, d = 2, 128
+    e = torch.empty((0, H, d), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, H, d), dtype=torch.float32, device="cuda")
+    b = torch.empty((0, H), dtype=torch.float32, device="cuda")
+    s0 = torch.randn((3, H, d, d), device="cuda")
+    cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    o, s = kda.fwd_chunked(e, e, e, g, b, cu_seqlens=cu, initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, d)
+    assert torch.equal(s, s0)
+
+
+# ---------------------------------------------------------------- decode
+
+def _decode_case(seed, B, H, d, dtype, steps):
+    st0 = kin.decode_states(B, H, d, seed=seed)
+    ins = [kin.decode_step(s, B, H, d, dtype=dtype, seed_base=seed) for s in range(steps)]
+    return st0, ins
+
+
+@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
+                                     (kin.F32, 128), (kin.F32, 32)])
+def test_decode_steps_parity(dtype, d):
+    """A few dependent decode steps on a small batch, every output and the
+    final states against the oracle."""
+    print(f"[parity] decode dtype={dtype} d={d}", flush=True)
+    kda = _kda()
+    B, H, steps = 5, 3, 6
+    st0, ins = _decode_case(40 + d, B, H, d, dtype, steps)
+    state = f32_device(st0)
+    ref = st0.astype(np.float64)
+    tol = TOL[dtype]
+    for x in ins:
+        o = kda.decode_step(to_device(x.q, dtype), to_device(x.k, dtype),
+                            to_device(x.v, dtype), f32_device(x.g), f32_device(x.beta), state)
+        q, k, v, g, b = x.f64()
+        o_ref, ref = oracle.decode(q, k, v, g, b, ref)
+        eo = relerr(from_device(o), o_ref)
+        assert eo <= tol, f"decode output error {eo:.3e}"
+    es = relerr(from_device(state), ref)
+    print(f"  decode relerr last o={eo:.3e} S={es:.3e}", flush=True)
+    assert es <= tol, f"decode state error {es:.3e}"
+
+
+def test_decode_matches_one_token_prefill():
+    """A decode step equals a one-token prefill from the same state."""
+    kda = _kda()
+    B, H, d = 4, 2, 128
+    st0, (x,) = _decode_case(9, B, H, d, kin.BF16, 1)
+    state = f32_device(st0)
+    o_dec = kda.decode_step(to_device(x.q, kin.BF16), to_device(x.k, kin.BF16),
+                            to_device(x.v, kin.BF16), f32_device(x.g), f32_device(x.beta),
+                            state)
+    q = to_device(x.q, kin.BF16).reshape(B, H, d)
+    o_pre, s_pre = kda.fwd_chunked(q, to_device(x.k, kin.BF16), to_device(x.v, kin.BF16),
+                                   f32_device(x.g), f32_device(x.beta), num_seqs=B,
+                                   initial_state=f32_device(st0), chunk_size=16)
+    torch.cuda.synchronize()
+    q64, k64, v64, g64, b64 = x.f64()
+    o_ref, s_ref = oracle.decode(q64, k64, v64, g64, b64, st0)
+    e = [relerr(from_device(o_dec), o_ref), relerr(from_device(state), s_ref),
+         relerr(from_device(o_pre), o_ref), relerr(from_device(s_pre), s_ref),
+         relerr(from_device(o_dec), from_device(o_pre))]
+    print("  decode o/S, prefill o/S, decode-vs-prefill o:", ["%.2e" % x for x in e])
+    # decode runs in fp32; the one-token prefill rounds its matrix-core
+    # operands (Ke, U - W S) to bf16, hence the two bars
+    assert e[0] < 1e-4 and e[1] < 1e-5
+    assert max(e[2:]) < 2e-2
