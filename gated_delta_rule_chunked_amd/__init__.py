@@ -9,7 +9,7 @@ Submodules are loaded on first use so that ``gated_delta_rule_chunked_amd.inputs
 (the seeded input generators) can be imported without torch or the library.
 """
 _BINDING_NAMES = ("fwd_chunked", "decode_step", "workspace_size", "library",
-                  "KdaError", "library_path")
+                  "KdaError", "library_path", "bind_fwd", "bind_decode")
 
 __all__ = list(_BINDING_NAMES)
 

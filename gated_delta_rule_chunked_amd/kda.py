@@ -98,29 +98,10 @@ def workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: i
 STAGES = {"cumsum": 0, "intra": 1, "inter": 2}
 
 
-def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                log_alpha: torch.Tensor, beta: torch.Tensor,
-                cu_seqlens: Optional[torch.Tensor] = None,
-                num_seqs: Optional[int] = None,
-                initial_state: Optional[torch.Tensor] = None,
-                chunk_size: int = 64, output_final_state: bool = True,
-                out: Optional[torch.Tensor] = None,
-                final_state: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None,
-                stage: Optional[str] = None,
-                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked KDA prefill (kda_fwd_chunked).
-
-    q, k: [T, H, d] and v: [T, H, d] (bf16 or fp32, same dtype);
-    log_alpha: [T, H, d] fp32; beta: [T, H] fp32;
-    cu_seqlens: int32 [N+1] device tensor, or None for `num_seqs` (default 1)
-    equal-length sequences; initial_state: fp32 [N, H, d, d] or None.
-    Returns (o [T, H, d] in v's dtype, final_state fp32 [N, H, d, d] or None).
-    `final_state` may be passed as the same tensor as `initial_state` to
-    update states in place.  `stage` ("cumsum", "intra" or "inter") runs only
-    that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
-    and `final_state` of a preceding call with the same arguments.
-    """
+def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chunk_size,
+              output_final_state, out, final_state, workspace, allow_alloc_ws=True):
+    """Checks the tensors of a prefill call, allocates missing outputs and
+    returns (ctypes argument tuple, o, final_state, workspace)."""
     T, H, d = q.shape
     dt = _dtype_code(q.dtype)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -147,20 +128,106 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise KdaError(f"unsupported sizes T={T} N={n} H={H} d={d} chunk={chunk_size} "
                        f"dtype={q.dtype}")
     if workspace is None or workspace.numel() < need:
-        if stage is not None:
+        if not allow_alloc_ws:
             raise KdaError("a single stage needs the workspace of a full call")
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), n,
             T, H, d, d, chunk_size, dt, _ptr(initial_state), _ptr(fs), _ptr(o),
             _ptr(workspace), workspace.numel(), _stream(dev))
+    return args, o, fs, workspace
+
+
+def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                log_alpha: torch.Tensor, beta: torch.Tensor,
+                cu_seqlens: Optional[torch.Tensor] = None,
+                num_seqs: Optional[int] = None,
+                initial_state: Optional[torch.Tensor] = None,
+                chunk_size: int = 64, output_final_state: bool = True,
+                out: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                stage: Optional[str] = None,
+                ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill (kda_fwd_chunked).
+
+    q, k: [T, H, d] and v: [T, H, d] (bf16 or fp32, same dtype);
+    log_alpha: [T, H, d] fp32; beta: [T, H] fp32;
+    cu_seqlens: int32 [N+1] device tensor, or None for `num_seqs` (default 1)
+    equal-length sequences; initial_state: fp32 [N, H, d, d] or None.
+    Returns (o [T, H, d] in v's dtype, final_state fp32 [N, H, d, d] or None).
+    `final_state` may be passed as the same tensor as `initial_state` to
+    update states in place.  `stage` ("cumsum", "intra" or "inter") runs only
+    that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
+    and `final_state` of a preceding call with the same arguments.
+    """
+    if stage is not None and stage not in STAGES:
+        raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
+    args, o, fs, _ = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
+                               initial_state, chunk_size, output_final_state, out,
+                               final_state, workspace, allow_alloc_ws=stage is None)
     if stage is None:
         _check(library().kda_fwd_chunked(*args), "kda_fwd_chunked")
     else:
-        if stage not in STAGES:
-            raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
         _check(library().kda_fwd_chunked_stage(STAGES[stage], *args),
                f"kda_fwd_chunked_stage({stage})")
     return o, fs
+
+
+class BoundCall:
+    """A C-ABI call with its arguments marshalled once.
+
+    Calling the object re-issues the same call on the stream captured at
+    bind time and raises KdaError on a non-success status.  The tensors the
+    arguments point to are kept alive by `tensors`.
+    """
+
+    def __init__(self, fn, args, what, tensors):
+        self._fn, self._args, self._what = fn, args, what
+        self.tensors = tensors
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != KDA_SUCCESS:
+            _check(st, self._what)
+
+
+def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
+             initial_state=None, chunk_size=64, output_final_state=True,
+             out=None, final_state=None, workspace=None):
+    """Validate and marshal a kda_fwd_chunked call once, for repeated calls.
+
+    Nothing is launched here.  Returns (call, stage_calls, o, final_state):
+    `call()` runs the whole prefill and `stage_calls[name]()` one of its
+    kernels ("cumsum", "intra", "inter"; kda_fwd_chunked_stage) on the same
+    workspace.
+    """
+    args, o, fs, ws = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
+                                initial_state, chunk_size, output_final_state, out,
+                                final_state, workspace)
+    keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws)
+    lib = library()
+    call = BoundCall(lib.kda_fwd_chunked, args, "kda_fwd_chunked", keep)
+    stages = {name: BoundCall(lib.kda_fwd_chunked_stage, (sid,) + args,
+                              f"kda_fwd_chunked_stage({name})", keep)
+              for name, sid in STAGES.items()}
+    return call, stages, o, fs
+
+
+def bind_decode(q, k, v, log_alpha, beta, state, out=None):
+    """Validate and marshal a kda_decode_step call once.  Returns (call, o);
+    each `call()` advances `state` by one step in place."""
+    B, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (B, H, d))
+    _need(log_alpha, "log_alpha", torch.float32, (B, H, d))
+    _need(beta, "beta", torch.float32, (B, H))
+    _need(state, "state", torch.float32, (B, H, d, d))
+    o = out if out is not None else torch.empty((B, H, d), dtype=v.dtype, device=q.device)
+    _need(o, "out", v.dtype, (B, H, d))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
+            B, H, d, d, _dtype_code(q.dtype), _stream(q.device))
+    return BoundCall(library().kda_decode_step, args, "kda_decode_step",
+                     (q, k, v, log_alpha, beta, state, o)), o
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -222,7 +222,9 @@ def test_decode_matches_one_token_prefill():
          relerr(from_device(o_pre), o_ref), relerr(from_device(s_pre), s_ref),
          relerr(from_device(o_dec), from_device(o_pre))]
     print("  decode o/S, prefill o/S, decode-vs-prefill o:", ["%.2e" % x for x in e])
-    # decode runs in fp32; the one-token prefill rounds its matrix-core
-    # operands (Ke, U - W S) to bf16, hence the two bars
-    assert e[0] < 1e-4 and e[1] < 1e-5
+    # decode runs in fp32 and only rounds o to bf16 (unit roundoff 2^-8);
+    # the state stays fp32.  The one-token prefill rounds its matrix-core
+    # operands (S, Ke, U - W S) to bf16, hence the bf16 bar there.
+    assert e[0] < 2.0 ** -8 + 1e-5, "decode o beyond bf16 output rounding"
+    assert e[1] < 1e-5, "decode state beyond fp32 rounding"
     assert max(e[2:]) < 2e-2
