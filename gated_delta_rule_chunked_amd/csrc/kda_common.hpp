@@ -109,6 +109,20 @@ __device__ __forceinline__ typename Frag<T>::type frag_from_f32(const float *p) 
   return r;
 }
 
+// 4 consecutive elements kept in the element type (convert at use, so that a
+// prefetching load does not force an early wait).
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type load4(const T *p) {
+  return *reinterpret_cast<const typename Vec4<T>::type *>(p);
+}
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 v) {
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 to_f32x4(f32x4 v) { return v; }
+
 // 4 consecutive elements (one D-layout column strip) as fp32 / from fp32.
 template <typename T>
 __device__ __forceinline__ f32x4 load4_f32(const T *p);
@@ -130,6 +144,83 @@ __device__ __forceinline__ void store4_f32<bf16>(bf16 *p, f32x4 x) {
 template <>
 __device__ __forceinline__ void store4_f32<float>(float *p, f32x4 x) {
   *reinterpret_cast<f32x4 *>(p) = x;
+}
+
+// ---- contraction order of the register-resident state chain -----------
+// A 16 x 16 output tile leaves lane l holding rows 4 * (l / 16) + i,
+// i = 0..3, while a K-step wants lane l to supply k = 8 * (l / 16) + i,
+// i = 0..7.  Because a contraction may visit k in any order (as long as
+// both operands agree), two stacked output tiles (rows 0..15 and 16..31 of
+// a 32-group) can serve directly as one K-step operand if, within every
+// group of 32, storage position p = 8 * g + j holds index
+// j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4).  Matrices that meet such
+// register-held operands in a product are stored with their contraction
+// index in this order.
+__host__ __device__ constexpr int kperm_pos(int idx) {  // index -> position
+  return (idx & ~31) + ((idx & 31) < 16 ? 8 * ((idx & 15) >> 2) + (idx & 3)
+                                         : 8 * ((idx & 15) >> 2) + 4 + (idx & 3));
+}
+__host__ __device__ constexpr int kperm_idx(int pos) {  // position -> index
+  return (pos & ~31) + (((pos & 7) < 4) ? 4 * ((pos & 31) >> 3) + (pos & 3)
+                                        : 16 + 4 * ((pos & 31) >> 3) + (pos & 3));
+}
+
+// Two output-tile row quads (rows 4g..4g+3 of tiles 2s and 2s+1) packed as
+// one K-step operand fragment in the order above.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type pack_quads(f32x4 a, f32x4 b) {
+  typename Frag<T>::type r;
+  r[0] = from_f32<T>(a[0]); r[1] = from_f32<T>(a[1]);
+  r[2] = from_f32<T>(a[2]); r[3] = from_f32<T>(a[3]);
+  r[4] = from_f32<T>(b[0]); r[5] = from_f32<T>(b[1]);
+  r[6] = from_f32<T>(b[2]); r[7] = from_f32<T>(b[3]);
+  return r;
+}
+
+// ---- fragment-major workspace storage -------------------------------------
+// An operand that one kernel writes and another feeds to the matrix cores is
+// stored in the order its fragments are loaded, so that each wavefront load
+// is one contiguous run (1 KiB for bf16) instead of 16 half-used cache lines.
+// K-step operand (rows, contraction positions pos in [0, K), K % 32 == 0):
+// the 8-element fragment of lane l for row block rb and K-step ks is run
+// (rb * K/32 + ks) * 64 + l, lane l covering row 16 rb + l % 16 and
+// positions 32 ks + 8 (l / 16) + e.
+__host__ __device__ constexpr int frag_off(int row, int pos, int K) {
+  return ((row >> 4) * (K >> 5) + (pos >> 5)) * 512 +
+         ((((pos & 31) >> 3) << 4) + (row & 15)) * 8 + (pos & 7);
+}
+// Output-tile operand (tokens t in [0, C), columns c): the 4 values lane l
+// holds of 16x16 tile (column block c / 16, token block t / 16) are run
+// (c/16 * C/16 + t/16) * 64 + l, lane l covering column 16 (c/16) + l % 16
+// and tokens 16 (t/16) + 4 (l / 16) + i.
+__host__ __device__ constexpr int tile_off(int t, int c, int C) {
+  return ((c >> 4) * (C >> 4) + (t >> 4)) * 256 +
+         ((((t & 15) >> 2) << 4) + (c & 15)) * 4 + (t & 3);
+}
+
+// Two 4-element vectors joined into one 8-element fragment.
+__device__ __forceinline__ bf16x8 join4(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x8 join4(f32x4 a, f32x4 b) {
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type vec4_from_f32(f32x4 x) {
+  typename Vec4<T>::type r;
+  r[0] = from_f32<T>(x[0]); r[1] = from_f32<T>(x[1]);
+  r[2] = from_f32<T>(x[2]); r[3] = from_f32<T>(x[3]);
+  return r;
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
+// carries a workgroup-scope release fence, which waits for every outstanding
+// global load as well and so would drain loads issued ahead of their use.
+// Here each wave's LDS writes complete (lgkmcnt 0) before it joins the
+// barrier; the memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Lane index helpers for the tile convention above.

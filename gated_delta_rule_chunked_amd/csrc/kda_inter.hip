@@ -14,228 +14,267 @@
 //   S   <- Diag(e^{G_n}) S + Ke^T Unew   (state after the chunk)
 //
 // Every product multiplies S from the left, so the d_v columns of S evolve
-// independently: a workgroup owns one (sequence, head, column slice of width
-// BV) and runs over that sequence's chunks.  The fp32 state slice lives in
-// registers (distributed as 16x16 matrix-core output tiles over the four
-// wavefronts) and is mirrored in LDS in the operand type for the next
-// chunk's products; Unew passes through LDS once per chunk.  Two barriers
-// per chunk.  Workgroups of the same (sequence, head) are placed on the same
-// XCD so that their shared reads of W, Qt, P and Ke hit one L2.
+// independently: a workgroup owns one (sequence, head, 16-column slice) and
+// walks that sequence's chunks.  Its four wavefronts split the rows: wave w
+// computes token block w of Unew and O and channel blocks w*CBW.. of S, so
+// all four SIMDs issue matrix-core work and each wave loads only its quarter
+// of W, Qt, P and Ke.  The blocks meet through two tiny LDS exchanges per
+// chunk (Unew after its product, S after the update), each a plain lane-for-
+// lane copy: the intra-chunk kernel stores W, Qt (channels) and Ke^T, P
+// (tokens) with their contraction index in the kperm order of
+// kda_common.hpp, in which a 16x16 output tile held by one wave is already
+// half of another wave's K-step operand.  The fp32 state stays in registers.
+//
+// The intra-chunk kernel stores all of these operands fragment-major
+// (frag_off / tile_off), so every load below is one contiguous run per wave.
+// Loads are the bottleneck of a serial chain: each wave keeps PF chunks of
+// its operands in flight (a ring of register buffers, the loop unrolled by
+// PF), requesting chunk c + PF right after the last use of chunk c's group.
+// The requests are unconditional (chunks past the end re-read the last one)
+// and fenced with scheduling barriers so the compiler keeps them in place.
+// Workgroups of one (sequence, head) share blockIdx % 8 and therefore one
+// XCD and its L2, which serves the same W/Qt/Ke/P rows to all slices.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 
-template <typename T, int D, int C, int BV>
-struct InterCfg {
-  static constexpr int NRB = C / 16;       // 16-token blocks of a chunk
-  static constexpr int NSRB = D / 16;      // 16-channel blocks of the state
-  static constexpr int NCBV = BV / 16;     // 16-column blocks of the slice
+template <typename T, int D, int C>
+struct InterOps {
+  using F = typename Frag<T>::type;
+  using V4 = typename Vec4<T>::type;
+  static constexpr int NCB = D / 16;
   static constexpr int CK = C < 32 ? 32 : C;
-  static constexpr int PAD = 16 / (int)sizeof(T);
-  static constexpr int LDS_S = D + PAD;    // sST [BV][LDS_S]  (S transposed)
-  static constexpr int LDU = CK + PAD;     // sUnT [BV][LDU]   (Unew transposed)
-  static constexpr int NUJ = (NRB + 3) / 4;
-  static constexpr int NSJ = (NSRB + 3) / 4;
-  static_assert(D % BV == 0 && BV % 16 == 0, "slice shape");
+  static constexpr int KD = D / 32;
+  static constexpr int KC = CK / 32;
+  static constexpr int CBW = (NCB + 3) / 4;  // state channel blocks per wave
+  // one chunk's operands for one wave
+  struct Buf {
+    F wA[KD];       // W rows of the wave's token block (K = channels)
+    F qA[KD];       // Qt rows of the wave's token block
+    F pA[KC];       // P rows of the wave's token block (K = tokens)
+    V4 uv;          // U of the wave's token block, output-tile layout
+    F kA[CBW][KC];  // Ke^T rows of the wave's channel blocks (K = tokens)
+    f32x4 gv[CBW];  // e^{G_n} of the wave's channel rows
+  };
 };
 
-template <typename T, int D, int C, int BV>
+template <typename T, int D, int C, int PF>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *__restrict__ qt, const T *__restrict__ w, const T *__restrict__ ut,
     const T *__restrict__ ket, const T *__restrict__ pm,
-    const float *__restrict__ gc, const int *__restrict__ cu,
+    const float *__restrict__ gam, const int *__restrict__ cu,
     const int *__restrict__ seq_first, int N, int H, int seq_len,
     const float *__restrict__ s0, float *__restrict__ s_final,
     T *__restrict__ o) {
-  using Cfg = InterCfg<T, D, C, BV>;
-  constexpr int NRB = Cfg::NRB, NSRB = Cfg::NSRB, NCBV = Cfg::NCBV, CK = Cfg::CK;
-  constexpr int LDS_S = Cfg::LDS_S, LDU = Cfg::LDU, NUJ = Cfg::NUJ, NSJ = Cfg::NSJ;
-  constexpr int NS = D / BV;
+  using Ops = InterOps<T, D, C>;
+  using F = typename Ops::F;
+  using V4 = typename Ops::V4;
+  using Buf = typename Ops::Buf;
+  constexpr int NRB = C / 16, NCB = Ops::NCB, CK = Ops::CK, KD = Ops::KD, KC = Ops::KC;
+  constexpr int CBW = Ops::CBW, NS = D / 16;
 
-  __shared__ __align__(16) T sST[BV * LDS_S];
-  __shared__ __align__(16) T sUnT[BV * LDU];
+  __shared__ V4 sS[NCB][64];     // S (operand type), one output tile per channel block
+  __shared__ V4 sU[2 * KC][64];  // Unew (operand type), one tile per token block
 
-  // XCD-aware placement: consecutive workgroup ids go to different XCDs, so
-  // the NS slices of one (sequence, head) get ids that share id % 8.
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int slice = local % NS, unit = local / NS;
   const int pair = unit * 8 + xcd;
   if (pair >= N * H) return;
   const int seq = pair / H, h = pair % H;
-  int t0, t1;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());  // scalar: branches stay uniform
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col0 = slice * 16;
+  // Roles.  With C = 64 and d % 64 == 0 every wave owns a token block and
+  // CBW channel blocks and nothing below branches.  Smaller shapes leave some
+  // waves without a block; those still load (clamped, in-bounds) operands so
+  // that every load stays unconditional, and skip only the arithmetic.
+  constexpr bool ALL_RB = NRB >= 4;
+  constexpr bool ALL_CB = NCB % 4 == 0;
+  const bool has_rb = ALL_RB || wv < NRB;
+  const int rb = ALL_RB ? wv : min(wv, NRB - 1);
+
+  int t0, len, first;
   if (cu) {
     t0 = cu[seq];
-    t1 = cu[seq + 1];
+    len = cu[seq + 1] - t0;
+    first = len > 0 ? seq_first[seq] : 0;
   } else {
     t0 = seq * seq_len;
-    t1 = t0 + seq_len;
+    len = seq_len;
+    first = seq * ((seq_len + C - 1) / C);
   }
-  const int len = t1 - t0;
   const int nch = (len + C - 1) / C;
-  const int first = nch == 0 ? 0 : (cu ? seq_first[seq] : seq * ((seq_len + C - 1) / C));
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int lr = lane & 15, lg = lane >> 4;
-  const int col0 = slice * BV;
   const int64_t rs = (int64_t)H * D;
 
-  // ---- initial state slice into registers and LDS ----
-  f32x4 S[NSJ][NCBV];
-  const int64_t sbase = (int64_t)pair * D * D;
+  // the wave's state rows: S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
+  f32x4 S[CBW];
+  const int64_t sbase = (int64_t)pair * D * D + col0 + lr;
 #pragma unroll
-  for (int j = 0; j < NSJ; ++j) {
-    const int srb = wave + 4 * j;
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = wv * CBW + j;
+    f32x4 x = zero4();
+    if (cb < NCB) {
+      if (s0) {
 #pragma unroll
-    for (int cb = 0; cb < NCBV; ++cb) {
-      f32x4 x = zero4();
-      if (srb < NSRB && s0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          x[i] = s0[sbase + (int64_t)(16 * srb + 4 * lg + i) * D + col0 + 16 * cb + lr];
+        for (int i = 0; i < 4; ++i) x[i] = s0[sbase + (int64_t)(16 * cb + 4 * lg + i) * D];
       }
-      S[j][cb] = x;
-      if (srb < NSRB) store4_f32<T>(sST + (16 * cb + lr) * LDS_S + 16 * srb + 4 * lg, x);
+      sS[cb][lane] = vec4_from_f32<T>(x);
     }
+    S[j] = x;
   }
-  if (CK > C) {
-    for (int e = tid; e < BV * (CK - C); e += 256)
-      sUnT[(e / (CK - C)) * LDU + C + e % (CK - C)] = from_f32<T>(0.f);
-  }
+  for (int e = tid; e < (2 * KC - NRB) * 64; e += 256)  // padding token blocks stay zero
+    sU[NRB + e / 64][e % 64] = vec4_from_f32<T>(zero4());
   __syncthreads();
 
-  for (int ci = 0; ci < nch; ++ci) {
-    const int64_t tile = (int64_t)(first + ci) * H + h;
+  auto tile_of = [&](int ci) { return (int64_t)(first + ci) * H + h; };
+  auto load_wu = [&](Buf &B, int ci) {
+    const int64_t tile = tile_of(ci);
+    const T *wt = w + tile * (C * D) + (rb * KD * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) B.wA[ks] = load8<T>(wt + ks * 512);
+    B.uv = load4<T>(ut + tile * (D * C) + ((slice * NRB + rb) * 64 + lane) * 4);
+  };
+  auto load_qp = [&](Buf &B, int ci) {
+    const int64_t tile = tile_of(ci);
+    const T *qq = qt + tile * (C * D) + (rb * KD * 64 + lane) * 8;
+    const T *pp = pm + tile * (C * CK) + (rb * KC * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) B.qA[ks] = load8<T>(qq + ks * 512);
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) B.pA[ks] = load8<T>(pp + ks * 512);  // upper blocks are zero
+  };
+  auto load_kg = [&](Buf &B, int ci) {
+    const int64_t tile = tile_of(ci);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = ALL_CB ? wv * CBW + j : min(wv * CBW + j, NCB - 1);
+      const T *kk = ket + tile * (D * CK) + (cb * KC * 64 + lane) * 8;
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) B.kA[j][ks] = load8<T>(kk + ks * 512);
+      B.gv[j] = *reinterpret_cast<const f32x4 *>(gam + tile * D + 16 * cb + 4 * lg);
+    }
+  };
+  auto load_all = [&](Buf &B, int ci) {
+    load_wu(B, ci);
+    load_qp(B, ci);
+    load_kg(B, ci);
+  };
+
+  auto step = [&](Buf &B, int ci) {
+    const int nxt = min(ci + PF, nch - 1);
     const int tc = t0 + ci * C;
     const int rows = min(C, len - ci * C);
-    const T *w_t = w + tile * (C * D);
-    const T *q_t = qt + tile * (C * D);
-    const T *u_t = ut + tile * (D * C);
-    const T *k_t = ket + tile * (D * CK);
-    const T *p_t = pm + tile * (C * CK);
 
-    // (a) Unew = U - W S and O = Qt S for this wave's token blocks
-    f32x4 accO[NUJ][NCBV];
+    // S entering the chunk, as K-step operands over channels
+    F sb[KD];
 #pragma unroll
-    for (int j = 0; j < NUJ; ++j) {
-      const int rb = wave + 4 * j;
+    for (int ks = 0; ks < KD; ++ks) sb[ks] = join4(sS[2 * ks][lane], sS[2 * ks + 1][lane]);
+
+    // Unew = U - W S for the wave's token block (two accumulators in flight)
+    if (has_rb) {
+      f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-      for (int cb = 0; cb < NCBV; ++cb) accO[j][cb] = zero4();
-      if (rb >= NRB) continue;
-      typename Frag<T>::type aw[D / 32], aq[D / 32];
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        aw[ks] = load8<T>(w_t + (16 * rb + lr) * D + 32 * ks + 8 * lg);
-        aq[ks] = load8<T>(q_t + (16 * rb + lr) * D + 32 * ks + 8 * lg);
+      for (int ks = 0; ks < KD; ++ks) {
+        if (ks & 1) a1 = mma_k32(B.wA[ks], sb[ks], a1);
+        else a0 = mma_k32(B.wA[ks], sb[ks], a0);
       }
+      sU[rb][lane] = vec4_from_f32<T>(to_f32x4(B.uv) - (a0 + a1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_wu(B, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+
+    // Unew of the whole chunk as K-step operands over tokens
+    F ub[KC];
 #pragma unroll
-      for (int cb = 0; cb < NCBV; ++cb) {
-        f32x4 ws = zero4(), acco = zero4();
+    for (int ks = 0; ks < KC; ++ks) ub[ks] = join4(sU[2 * ks][lane], sU[2 * ks + 1][lane]);
+
+    // S <- Diag(e^{G_n}) S + Ke^T Unew for the wave's channel blocks
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const auto bs = load8<T>(sST + (16 * cb + lr) * LDS_S + 32 * ks + 8 * lg);
-          ws = mma_k32(aw[ks], bs, ws);
-          acco = mma_k32(aq[ks], bs, acco);
-        }
-        const f32x4 u = load4_f32<T>(u_t + (col0 + 16 * cb + lr) * C + 16 * rb + 4 * lg);
-        store4_f32<T>(sUnT + (16 * cb + lr) * LDU + 16 * rb + 4 * lg, u - ws);
-        accO[j][cb] = acco;
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (ALL_CB || cb < NCB) {
+        f32x4 acc = S[j] * B.gv[j];
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[ks], acc);
+        S[j] = acc;
+        sS[cb][lane] = vec4_from_f32<T>(acc);
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    load_kg(B, nxt);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // (c) O += P Unew, store the output rows of this wave
+    // O = Qt S + P Unew for the wave's token block
+    if (has_rb) {
+      f32x4 oc = zero4();
 #pragma unroll
-    for (int j = 0; j < NUJ; ++j) {
-      const int rb = wave + 4 * j;
-      if (rb >= NRB) continue;
+      for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[ks], oc);
 #pragma unroll
-      for (int cb = 0; cb < NCBV; ++cb) {
-        f32x4 acco = accO[j][cb];
+      for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
+      T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
+      if (rows == C) {
 #pragma unroll
-        for (int ks = 0; ks < CK / 32; ++ks) {
-          if (32 * ks > 16 * rb + 15) break;  // P is lower triangular
-          const auto ap = load8<T>(p_t + (16 * rb + lr) * CK + 32 * ks + 8 * lg);
-          const auto bu = load8<T>(sUnT + (16 * cb + lr) * LDU + 32 * ks + 8 * lg);
-          acco = mma_k32(ap, bu, acco);
-        }
+        for (int i = 0; i < 4; ++i) op[i * rs] = from_f32<T>(oc[i]);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * rb + 4 * lg + i;
-          if (r < rows)
-            o[(int64_t)(tc + r) * rs + (int64_t)h * D + col0 + 16 * cb + lr] = from_f32<T>(acco[i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (16 * rb + 4 * lg + i < rows) op[i * rs] = from_f32<T>(oc[i]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_qp(B, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
 
-    // (d) S <- Diag(e^{G_n}) S + Ke^T Unew
-    const float *g_last = gc + (int64_t)(tc + rows - 1) * rs + (int64_t)h * D;
-#pragma unroll
-    for (int j = 0; j < NSJ; ++j) {
-      const int srb = wave + 4 * j;
-      if (srb >= NSRB) continue;
-      const f32x4 gl = *reinterpret_cast<const f32x4 *>(g_last + 16 * srb + 4 * lg);
-      const f32x4 gam = f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
-      typename Frag<T>::type ak[CK / 32];
-#pragma unroll
-      for (int ks = 0; ks < CK / 32; ++ks)
-        ak[ks] = load8<T>(k_t + (16 * srb + lr) * CK + 32 * ks + 8 * lg);
-#pragma unroll
-      for (int cb = 0; cb < NCBV; ++cb) {
-        f32x4 acc = S[j][cb] * gam;
-#pragma unroll
-        for (int ks = 0; ks < CK / 32; ++ks) {
-          const auto bu = load8<T>(sUnT + (16 * cb + lr) * LDU + 32 * ks + 8 * lg);
-          acc = mma_k32(ak[ks], bu, acc);
-        }
-        S[j][cb] = acc;
-        store4_f32<T>(sST + (16 * cb + lr) * LDS_S + 16 * srb + 4 * lg, acc);
-      }
-    }
-    __syncthreads();
+  static_assert(PF == 3, "the chunk loop below is unrolled for three buffers");
+  Buf B0, B1, B2;
+  if (nch > 0) {
+    load_all(B0, 0);
+    load_all(B1, min(1, nch - 1));
+    load_all(B2, min(2, nch - 1));
+  }
+  for (int ci = 0; ci < nch; ci += 3) {
+    step(B0, ci);
+    if (ci + 1 < nch) step(B1, ci + 1);
+    if (ci + 2 < nch) step(B2, ci + 2);
   }
 
   if (s_final) {
 #pragma unroll
-    for (int j = 0; j < NSJ; ++j) {
-      const int srb = wave + 4 * j;
-      if (srb >= NSRB) continue;
-#pragma unroll
-      for (int cb = 0; cb < NCBV; ++cb)
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          s_final[sbase + (int64_t)(16 * srb + 4 * lg + i) * D + col0 + 16 * cb + lr] = S[j][cb][i];
+          s_final[sbase + (int64_t)(16 * cb + 4 * lg + i) * D] = S[j][i];
+      }
     }
   }
 }
 
-template <typename T, int D, int C, int BV>
-static hipError_t launch_inter_t(const FwdArgs &a) {
-  constexpr int NS = D / BV;
+template <typename T, int D, int C>
+static hipError_t launch_inter_c(const FwdArgs &a) {
+  constexpr int NS = D / 16;
   const int pairs = a.num_seqs * a.num_heads;
   const int units = (pairs + 7) / 8;
   const dim3 grid((unsigned)(8 * units * NS));
   char *ws = a.ws;
-  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, BV>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3>), grid, dim3(256), 0, a.stream,
                      reinterpret_cast<const T *>(ws + a.lay.qt),
                      reinterpret_cast<const T *>(ws + a.lay.w),
                      reinterpret_cast<const T *>(ws + a.lay.ut),
                      reinterpret_cast<const T *>(ws + a.lay.ket),
                      reinterpret_cast<const T *>(ws + a.lay.p),
-                     reinterpret_cast<const float *>(ws + a.lay.gc), a.cu_seqlens,
+                     reinterpret_cast<const float *>(ws + a.lay.gam), a.cu_seqlens,
                      reinterpret_cast<const int *>(ws + a.lay.seq_first), a.num_seqs,
                      a.num_heads, a.seq_len, a.s0, a.s_final, reinterpret_cast<T *>(a.o));
   return hipGetLastError();
-}
-
-// Column-slice width: narrow slices when few (sequence, head) pairs exist so
-// that the launch still spreads over the compute units.
-template <typename T, int D, int C>
-static hipError_t launch_inter_c(const FwdArgs &a) {
-  const int pairs = a.num_seqs * a.num_heads;
-  if (pairs * (D / 16) <= 2048) return launch_inter_t<T, D, C, 16>(a);
-  return launch_inter_t<T, D, C, 32>(a);
 }
 
 template <typename T, int D>

@@ -21,13 +21,19 @@ namespace kda {
 //   ut          elem [tiles][D][C]   WY factor U = T Diag(beta) V, transposed
 //   ket         elem [tiles][D][CK]  K * exp(G_last - G), transposed
 //   p           elem [tiles][C][CK]  lower-triangular (Q*exp(G)) (K*exp(-G))^T
+//   gam         fp32 [tiles][D]      exp(G_last), the chunk's total decay
 // CK = max(C, 32) is the token extent padded to one 32-wide matrix-core
-// K-step (the padding columns are zero).
+// K-step (the padding columns are zero).  The contraction index of qt and w
+// (channels) and of ket and p (tokens) is taken in the kperm order of
+// kda_common.hpp, the order in which the inter-chunk kernel holds the state
+// and the corrected values in registers, and every tile is stored
+// fragment-major (frag_off / tile_off in kda_common.hpp) so that the
+// inter-chunk kernel reads it with contiguous loads.
 struct FwdLayout {
   int64_t max_chunks = 0;
   int64_t tiles = 0;
   size_t chunk_info = 0, seq_first = 0, gc = 0, qt = 0, w = 0, ut = 0, ket = 0,
-         p = 0, total = 0;
+         p = 0, gam = 0, total = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -54,6 +60,7 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
   L.ut = take(elem * (size_t)(L.tiles * D * C));
   L.ket = take(elem * (size_t)(L.tiles * D * CK));
   L.p = take(elem * (size_t)(L.tiles * C * CK));
+  L.gam = take(sizeof(float) * (size_t)(L.tiles * D));
   L.total = off;
   return L;
 }

@@ -30,6 +30,9 @@
 //     T_ij = -T_ii sum_m A_im T_mj, on fp32 MFMA
 //  4. W and U on the matrix cores (K = tokens), T rounded to the operand type
 //  5. Ke written transposed through LDS
+// Qt, W (channels), Ke^T and P (tokens) are stored with their contraction
+// index in kperm order (kda_common.hpp) for the inter-chunk kernel, which
+// also receives exp(G_last) per channel.
 // LDS is reused between phases: the row-major Qt/Kt/Kh copies of phases 1-2
 // become T and the transposed Diag(beta)Kt, Diag(beta)V copies of phase 4.
 #include "kda_common.hpp"
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const float *__restrict__ gc, const float *__restrict__ beta,
     const int4 *__restrict__ chunk_info, int H, T *__restrict__ qt_out,
     T *__restrict__ w_out, T *__restrict__ ut_out, T *__restrict__ ket_out,
-    T *__restrict__ p_out) {
+    T *__restrict__ p_out, float *__restrict__ gam_out) {
   using Cfg = IntraCfg<T, D, C>;
   constexpr int NRB = Cfg::NRB, NCB = Cfg::NCB, CK = Cfg::CK;
   constexpr int LDR = Cfg::LDR, LDT = Cfg::LDT, LDA = Cfg::LDA;
@@ -99,6 +102,13 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
     gl[0] = a[0]; gl[1] = a[1]; gl[2] = a[2]; gl[3] = a[3];
     gl[4] = b[0]; gl[5] = b[1]; gl[6] = b[2]; gl[7] = b[3];
+  }
+  if (tid < GPR) {
+    float *gp = gam_out + tile * D + ch0;
+    *reinterpret_cast<f32x4 *>(gp) =
+        f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
+    *reinterpret_cast<f32x4 *>(gp + 4) =
+        f32x4{__expf(gl[4]), __expf(gl[5]), __expf(gl[6]), __expf(gl[7])};
   }
   T kb_reg[NPASS][8], vb_reg[NPASS][8], ke_reg[NPASS][8];
   T *qt_tile = qt_out + tile * (C * D);
@@ -136,7 +146,10 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     store8<T>(sQ + r * LDR + ch0, qt);
     store8<T>(sK + r * LDR + ch0, kt);
     store8<T>(sKh + r * LDR + ch0, kh);
-    store8<T>(qt_tile + r * D + ch0, qt);
+    // channels ch0..ch0+3 and ch0+4..ch0+7 are two contiguous runs in kperm order
+    store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0), D), f32x4{qt[0], qt[1], qt[2], qt[3]});
+    store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0 + 4), D),
+                  f32x4{qt[4], qt[5], qt[6], qt[7]});
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kb_reg[j][e] = from_f32<T>(kbv[e]);
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * rb + 4 * lg + i;
       accA[i] = (col < row) ? sBeta[row] * accA[i] : 0.f;
-      p_tile[row * CK + col] = from_f32<T>((col <= row) ? accP[i] : 0.f);
+      p_tile[frag_off(row, kperm_pos(col), CK)] = from_f32<T>((col <= row) ? accP[i] : 0.f);
     }
     a_keep[j] = accA;
     a_rb[j] = rb;
@@ -185,8 +198,8 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   }
   // zero the strictly-upper tiles of P and its padding columns
   for (int e = tid; e < C * CK; e += 256) {
-    const int row = e / CK, col = e % CK;
-    if (col >= C || (col / 16) > (row / 16)) p_tile[e] = from_f32<T>(0.f);
+    const int row = e / CK, col = kperm_idx(e % CK);
+    if (col >= C || (col / 16) > (row / 16)) p_tile[frag_off(row, e % CK, CK)] = from_f32<T>(0.f);
   }
   __syncthreads();
 
@@ -286,9 +299,10 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const int col = 16 * cb + lr;
     if (which == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w_tile[(16 * rb + 4 * lg + i) * D + col] = from_f32<T>(acc[i]);
+      for (int i = 0; i < 4; ++i)
+        w_tile[frag_off(16 * rb + 4 * lg + i, kperm_pos(col), D)] = from_f32<T>(acc[i]);
     } else {
-      store4_f32<T>(ut_tile + col * C + 16 * rb + 4 * lg, acc);
+      store4_f32<T>(ut_tile + tile_off(16 * rb + 4 * lg, col, C), acc);
     }
   }
   __syncthreads();
@@ -300,12 +314,12 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const int r = j * RPP + tid / GPR;
     if (r >= C) continue;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sKeT[(ch0 + e) * LDT + r] = ke_reg[j][e];
+    for (int e = 0; e < 8; ++e) sKeT[(ch0 + e) * LDT + kperm_pos(r)] = ke_reg[j][e];
   }
   if (CK > C) {
     for (int e = tid; e < D * (CK - C); e += 256) {
       const int ch = e / (CK - C), r = C + e % (CK - C);
-      sKeT[ch * LDT + r] = from_f32<T>(0.f);
+      sKeT[ch * LDT + kperm_pos(r)] = from_f32<T>(0.f);
     }
   }
   __syncthreads();
@@ -313,7 +327,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   constexpr int V8 = CK / 8;  // 8-element vectors per row
   for (int e = tid; e < D * V8; e += 256) {
     const int ch = e / V8, x = (e % V8) * 8;
-    *reinterpret_cast<typename Frag<T>::type *>(ket_tile + ch * CK + x) =
+    *reinterpret_cast<typename Frag<T>::type *>(ket_tile + frag_off(ch, x, CK)) =
         load8<T>(sKeT + ch * LDT + x);
   }
 }
@@ -334,7 +348,7 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
                      reinterpret_cast<const int4 *>(ws + a.lay.chunk_info), a.num_heads,
                      reinterpret_cast<T *>(ws + a.lay.qt), reinterpret_cast<T *>(ws + a.lay.w),
                      reinterpret_cast<T *>(ws + a.lay.ut), reinterpret_cast<T *>(ws + a.lay.ket),
-                     reinterpret_cast<T *>(ws + a.lay.p));
+                     reinterpret_cast<T *>(ws + a.lay.p), reinterpret_cast<float *>(ws + a.lay.gam));
   return hipGetLastError();
 }
 
