@@ -5,8 +5,9 @@
 
 Headline: chunked prefill, B=2 sequences x T=2048 tokens, H=8 heads,
 d_k=d_v=128, chunk 64, bf16 q/k/v, fp32 log-decay/beta/state, zero initial
-state.  One step = one kda_fwd_chunked call (cumulative log-decay ->
-intra-chunk UT/WY -> inter-chunk state pass) over that batch; `value` is
+state.  One step = one kda_fwd_chunked call (intra-chunk kernel:
+cumulative log-decay + UT/WY factors -> inter-chunk state pass) over that
+batch; `value` is
 prefill tokens/s over K timed steps with every input resident in HBM.
 
 Also reported on the same JSON line:
@@ -72,14 +73,12 @@ def state_bytes(d):
 
 def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0):
     """Algorithmic HBM bytes of one launch of a prefill kernel: what it must
-    read and write given the three-kernel split (workspace tensors count)."""
+    read and write given the two-kernel split (workspace tensors count)."""
     CK = max(C, 32)
-    if stage == "cumsum":     # read g, write the cumulative G
-        return token_heads * 8 * d
-    if stage == "intra":      # read q, k, v, G, beta; write Qt, W, U, Ke, P
-        return token_heads * (3 * E * d + 4 * d + 4 + 4 * E * d + E * CK)
-    if stage == "inter":      # read Qt, W, U, Ke, P; write o; states
-        return (token_heads * (5 * E * d + E * CK) +
+    if stage == "intra":      # read q, k, v, g, beta; write Qt, W, U, Ke, P, e^G_n
+        return token_heads * (3 * E * d + 4 * d + 4 + 4 * E * d + E * CK + 4 * d / C)
+    if stage == "inter":      # read Qt, W, U, Ke, P, e^G_n; write o; states
+        return (token_heads * (5 * E * d + E * CK + 4 * d / C) +
                 pairs * state_bytes(d) * (2 if with_s0 else 1))
     raise ValueError(stage)
 
@@ -135,10 +134,10 @@ def time_prefill(torch, kda, w, steps, warmup, per_kernel=True):
     ms = e0.elapsed_time(e1) / steps
     res = dict(ms_per_step=ms, wall_ms_per_step=1e3 * t_wall / steps)
     if per_kernel:
-        # the three kernels of the same call, each bracketed by events on
+        # the two kernels of the same call, each bracketed by events on
         # the launch stream, over the same number of passes
-        names = ("cumsum", "intra", "inter")
-        ev = [_events(torch, 4) for _ in range(steps)]
+        names = ("intra", "inter")
+        ev = [_events(torch, len(names) + 1) for _ in range(steps)]
         for i in range(steps):
             ev[i][0].record()
             for j, nm in enumerate(names):

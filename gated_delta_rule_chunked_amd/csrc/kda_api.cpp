@@ -1,7 +1,6 @@
 // kda_api.cpp -- the C ABI declared in include/kda.h: host-side argument
 // validation, workspace layout and the ordered launches of the prefill
-// kernels (cumulative log-decay -> intra-chunk -> inter-chunk) and of the
-// decode kernel.  Nothing here allocates memory or keeps state.
+// kernels (intra-chunk -> inter-chunk) and of the decode kernel.  Nothing here allocates memory or keeps state.
 #include <hip/hip_runtime.h>
 
 #include "kda.h"
@@ -120,9 +119,8 @@ kda_status fwd_run(unsigned mask, const void *q, const void *k, const void *v,
   a.lay = lay;
   a.stream = reinterpret_cast<hipStream_t>(stream);
 
-  if ((mask & 1u) && launch_chunk_cumsum(a) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
-  if ((mask & 2u) && launch_intra(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
-  if ((mask & 4u) && launch_inter(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
+  if ((mask & 1u) && launch_intra(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
+  if ((mask & 2u) && launch_inter(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   return KDA_SUCCESS;
 }
 
@@ -137,7 +135,7 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            int32_t d_v, int32_t chunk_size, kda_dtype dtype,
                            const float *initial_state, float *final_state, void *o,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  return fwd_run(7u, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, total_tokens,
+  return fwd_run(3u, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, total_tokens,
                  num_heads, d_k, d_v, chunk_size, dtype, initial_state, final_state, o,
                  workspace, workspace_bytes, stream);
 }
@@ -149,8 +147,7 @@ kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void 
                                  int32_t d_v, int32_t chunk_size, kda_dtype dtype,
                                  const float *initial_state, float *final_state, void *o,
                                  void *workspace, size_t workspace_bytes, void *stream) {
-  if (stage != KDA_STAGE_CUMSUM && stage != KDA_STAGE_INTRA && stage != KDA_STAGE_INTER)
-    return KDA_ERROR_INVALID_VALUE;
+  if (stage != KDA_STAGE_INTRA && stage != KDA_STAGE_INTER) return KDA_ERROR_INVALID_VALUE;
   return fwd_run(1u << (unsigned)stage, q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
                  total_tokens, num_heads, d_k, d_v, chunk_size, dtype, initial_state,
                  final_state, o, workspace, workspace_bytes, stream);

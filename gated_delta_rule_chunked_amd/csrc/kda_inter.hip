@@ -216,14 +216,17 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
       for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[ks], oc);
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
+      // convert before any branch: matrix-core results are read only in
+      // straight-line code after the instructions that produce them
+      const V4 ov = vec4_from_f32<T>(oc);
       T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
       if (rows == C) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) op[i * rs] = from_f32<T>(oc[i]);
+        for (int i = 0; i < 4; ++i) op[i * rs] = ov[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * rb + 4 * lg + i < rows) op[i * rs] = from_f32<T>(oc[i]);
+          if (16 * rb + 4 * lg + i < rows) op[i * rs] = ov[i];
       }
     }
     __builtin_amdgcn_sched_barrier(0);

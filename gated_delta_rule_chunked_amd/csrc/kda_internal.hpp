@@ -13,9 +13,7 @@ namespace kda {
 // Prefill workspace layout.  Per-chunk products are stored per (chunk, head)
 // tile, tile index = chunk * H + head, so that every tile is one contiguous
 // block; chunk ids enumerate the chunks of sequence 0, then sequence 1, ...
-//   chunk_info  int4 [max_chunks]    (sequence, first token, rows, 0)
 //   seq_first   int  [num_seqs]      first chunk id of each non-empty sequence
-//   gc          fp32 [T, H, D]       chunk-local cumulative log-decay
 //   qt          elem [tiles][C][D]   Q * exp(G)
 //   w           elem [tiles][C][D]   WY factor W = T Diag(beta) (K * exp(G))
 //   ut          elem [tiles][D][C]   WY factor U = T Diag(beta) V, transposed
@@ -32,8 +30,7 @@ namespace kda {
 struct FwdLayout {
   int64_t max_chunks = 0;
   int64_t tiles = 0;
-  size_t chunk_info = 0, seq_first = 0, gc = 0, qt = 0, w = 0, ut = 0, ket = 0,
-         p = 0, gam = 0, total = 0;
+  size_t seq_first = 0, qt = 0, w = 0, ut = 0, ket = 0, p = 0, gam = 0, total = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -52,9 +49,7 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
     off += (bytes + 255) & ~size_t(255);
     return at;
   };
-  L.chunk_info = take(sizeof(int) * 4 * (size_t)L.max_chunks);
   L.seq_first = take(sizeof(int) * (size_t)N);
-  L.gc = take(sizeof(float) * (size_t)(T * H * D));
   L.qt = take(elem * (size_t)(L.tiles * C * D));
   L.w = take(elem * (size_t)(L.tiles * C * D));
   L.ut = take(elem * (size_t)(L.tiles * D * C));
@@ -65,7 +60,7 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
   return L;
 }
 
-// Arguments common to the three prefill launches.
+// Arguments common to the two prefill launches.
 struct FwdArgs {
   const void *q, *k, *v;
   const float *g, *beta;
@@ -82,7 +77,6 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
-hipError_t launch_chunk_cumsum(const FwdArgs &a);
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
 hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
 hipError_t launch_decode(const void *q, const void *k, const void *v,

@@ -1,13 +1,16 @@
-// kda_intra.hip -- intra-chunk kernel: decay-scaled blocks, UT transform and
-// WY factors for one (chunk, head) tile.
+// kda_intra.hip -- per-chunk kernel: chunk location, chunk-local cumulative
+// log-decay, decay-scaled blocks, UT transform and WY factors for one
+// (chunk, head) tile.
 //
-// For a chunk of n <= C tokens with chunk-local cumulative log-decay G
-// (rows = tokens, columns = key channels), the token-by-token delta updates
-// of the chunk are packed into dense factors (fr.news.hada.io Kimi Linear
-// summary, section "Algorithme parallele par chunks": WY representation,
-// UT transform, row-by-row forward substitution, intra-chunk work on the
-// matrix units; section "Un volume de calcul reduit": both low-rank vectors
-// are tied to k, so only two chunk matrices are needed):
+// For a chunk of n <= C tokens the token-by-token delta updates are packed
+// into dense factors (fr.news.hada.io Kimi Linear summary, section
+// "Algorithme parallele par chunks": WY representation, UT transform,
+// row-by-row forward substitution, intra-chunk work on the matrix units;
+// section "Un volume de calcul reduit": both low-rank vectors are tied to k,
+// so only two chunk matrices are needed).  With G_r = g_1 + ... + g_r the
+// chunk-local cumulative log-decay of every key channel (mkdocs.reaper.mx
+// "Attention lineaire et recurrence", section "Le piege numerique de la
+// decroissance cumulee"; it restarts at every chunk and sequence start):
 //
 //   Qt = Q * e^G,  Kt = K * e^G,  Kh = K * e^-G,  Ke = K * e^(G_n - G)
 //   A  = strictly_lower(Diag(beta) Kt Kh^T)       (decay-scaled K K^T)
@@ -15,227 +18,320 @@
 //   T  = (I + A)^-1                               (forward substitution)
 //   W  = T Diag(beta) Kt,   U = T Diag(beta) V    (WY factors)
 //
-// (* = per-channel product.)  These follow from unrolling the recurrence
-// over the chunk; the inter-chunk kernel then uses U - W S, Qt S + P(U - W S)
-// and e^(G_n) S + Ke^T (U - W S).  The chunk-start reference of Kh requires
-// G_n > -80 per channel (exp(80) is far inside fp32/bf16 range), the bound
-// quoted in mkdocs.reaper.mx, section "Le piege numerique de la decroissance
-// cumulee".
+// (* = per-channel product.)  The inter-chunk kernel then uses U - W S,
+// Qt S + P (U - W S) and e^(G_n) S + Ke^T (U - W S).  The chunk-start
+// reference of Kh needs G_n > -80 per channel (e^80 is far inside fp32 and
+// bf16 range), the bound quoted in the same section of mkdocs.reaper.mx.
 //
-// One workgroup of 4 wavefronts per tile.  Phases (barrier-separated):
-//  1. elementwise scaling (fp32 exp), 16-byte loads, operands to LDS
-//  2. A and P tiles on the matrix cores (16x16 output tiles, K = d)
-//  3. T in LDS, fp32: 16x16 diagonal blocks by forward substitution (one
-//     wave per block), then the off-diagonal blocks block-row by block-row,
-//     T_ij = -T_ii sum_m A_im T_mj, on fp32 MFMA
-//  4. W and U on the matrix cores (K = tokens), T rounded to the operand type
-//  5. Ke written transposed through LDS
-// Qt, W (channels), Ke^T and P (tokens) are stored with their contraction
-// index in kperm order (kda_common.hpp) for the inter-chunk kernel, which
-// also receives exp(G_last) per channel.
-// LDS is reused between phases: the row-major Qt/Kt/Kh copies of phases 1-2
-// become T and the transposed Diag(beta)Kt, Diag(beta)V copies of phase 4.
+// One workgroup of 4 wavefronts per tile:
+//  1. Thread t owns 4 channels x RPT consecutive tokens.  It loads its g, q,
+//     k, v (coalesced along channels), sums g down its tokens, adds the
+//     totals of the token groups above it (LDS), forms the scaled rows in
+//     fp32, stores Qt and Ke^T straight to the workspace and stages Kt, Kh,
+//     Qt row-major in LDS.
+//  2. A and P^T tiles on the matrix cores (K = d); A (masked, beta-scaled)
+//     goes to LDS in fp32, P is produced as P^T tiles so that each lane
+//     stores 4 consecutive positions of one P row.
+//  3. Diag(beta) Kt and Diag(beta) V are staged transposed (each thread
+//     writes its token run of a channel at once); T = (I + A)^-1 in fp32 LDS:
+//     16 x 16 diagonal blocks by forward substitution, then the blocks below
+//     them block-row by block-row on fp32 matrix cores.
+//  4. W^T = (Diag(beta) Kt)^T T^T and U = T Diag(beta) V on the matrix cores,
+//     T rounded to the operand type; each wave reuses its T fragments for
+//     all of its tiles.
+// Every workspace tensor is written in the fragment-major, kperm-ordered
+// layout the inter-chunk kernel loads (kda_common.hpp), together with
+// exp(G_n) per channel.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 
+// Locates chunk id `c` among the sequences: s_loc = (sequence, first token,
+// rows), rows = 0 when c lies past the last chunk.  The workgroup of head 0
+// that owns the first chunk of a sequence records it in seq_first.
+__device__ void locate_chunk(int c, int h, const int *cu, int N, int seq_len, int C,
+                             int *s_loc, int *s_scan, int *seq_first) {
+  const int tid = threadIdx.x;
+  if (cu == nullptr) {
+    if (tid == 0) {
+      const int per = (seq_len + C - 1) / C;
+      const int s = c / per, i = c % per;
+      s_loc[0] = s;
+      s_loc[1] = s * seq_len + i * C;
+      s_loc[2] = (s < N) ? min(C, seq_len - i * C) : 0;
+      if (h == 0 && i == 0 && s < N) seq_first[s] = c;
+    }
+    __syncthreads();
+    return;
+  }
+  if (tid == 0) { s_loc[0] = 0; s_loc[1] = 0; s_loc[2] = 0; s_loc[3] = 0; }
+  int base = 0;
+  for (int s0 = 0; s0 < N; s0 += blockDim.x) {
+    const int s = s0 + tid;
+    int len = 0, start = 0;
+    if (s < N) {
+      start = cu[s];
+      len = cu[s + 1] - start;
+    }
+    const int nc = (len + C - 1) / C;
+    __syncthreads();
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+      const int add = (tid >= off) ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int incl = base + s_scan[tid];
+    const int excl = incl - nc;
+    if (s < N && nc > 0) {
+      if (c >= excl && c < incl) {
+        const int i = c - excl;
+        s_loc[0] = s;
+        s_loc[1] = start + i * C;
+        s_loc[2] = min(C, len - i * C);
+        s_loc[3] = 1;
+      }
+      if (h == 0 && c == excl) seq_first[s] = c;
+    }
+    base += s_scan[blockDim.x - 1];
+    __syncthreads();
+    if (s_loc[3]) break;
+  }
+  __syncthreads();
+}
+
 template <typename T, int D, int C>
 struct IntraCfg {
-  static constexpr int NRB = C / 16;              // 16-row blocks of the chunk
-  static constexpr int NCB = D / 16;              // 16-col blocks of a head
-  static constexpr int CK = C < 32 ? 32 : C;      // token extent per K-step
-  static constexpr int PAD = 16 / (int)sizeof(T); // 16-byte row padding
-  static constexpr int LDR = D + PAD;             // [C][D] row stride
-  static constexpr int LDT = CK + PAD;            // [D][CK] row stride
-  static constexpr int LDA = CK + 4;              // fp32 [C][CK] row stride
-  static constexpr int GPR = D / 8;               // threads per row, phase 1
-  static constexpr int RPP = 256 / GPR;           // rows per pass
-  static constexpr int NPASS = (C + RPP - 1) / RPP;
+  static constexpr int NRB = C / 16;               // 16-token blocks of the chunk
+  static constexpr int NCB = D / 16;               // 16-channel blocks of a head
+  static constexpr int CK = C < 32 ? 32 : C;       // token extent per K-step
+  static constexpr int NKB = CK / 16;              // token blocks incl. padding
+  static constexpr int KD = D / 32;                // K-steps over channels
+  static constexpr int KC = CK / 32;               // K-steps over tokens
+  static constexpr int CG = D / 4;                 // 4-channel groups (phase 1)
+  static constexpr int RG = 256 / CG;              // token groups (phase 1)
+  static constexpr int RPT = (C + RG - 1) / RG;    // tokens per thread (phase 1)
+  static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding
+  static constexpr int LDR = D + PAD;              // row-major [C][D] stride
+  static constexpr int LDT = CK + PAD;             // transposed [D][CK] stride
+  static constexpr int LDA = CK + 4;               // fp32 [C][CK] stride
   static constexpr int BYTES_ROW = C * LDR * (int)sizeof(T);
   static constexpr int BYTES_TR = D * LDT * (int)sizeof(T);
-  static constexpr int BYTES_X = (2 * BYTES_ROW > 2 * BYTES_TR) ? 2 * BYTES_ROW : 2 * BYTES_TR;
+  static constexpr int BYTES_X = (3 * BYTES_ROW > 2 * BYTES_TR) ? 3 * BYTES_ROW : 2 * BYTES_TR;
   static constexpr int BYTES_A = C * LDA * 4;
-  static constexpr int BYTES_Y = (BYTES_ROW > BYTES_A) ? BYTES_ROW : BYTES_A;
+  static constexpr int BYTES_TOT = RG * CG * 16;   // phase-1 token-group totals (alias A)
+  static constexpr int BYTES_Y = BYTES_A > BYTES_TOT ? BYTES_A : BYTES_TOT;
   static constexpr int LDS_BYTES = BYTES_X + BYTES_Y + C * 4;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(C % 16 == 0 && D % 32 == 0, "tile shape");
+  static_assert(C % 16 == 0 && D % 32 == 0 && RPT * RG >= C, "tile shape");
+  static_assert(RPT == 1 || RPT == 2 || RPT % 4 == 0, "token runs per thread");
 };
+
+// L consecutive elements stored from fp32 (L = 1, 2 or 4).
+template <typename T, int L>
+__device__ __forceinline__ void store_run(T *p, const float *x) {
+  if constexpr (L == 4) {
+    store4_f32<T>(p, f32x4{x[0], x[1], x[2], x[3]});
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) p[i] = from_f32<T>(x[i]);
+  }
+}
+
+// L consecutive elements of one type, in 16-byte pieces when they fill them.
+template <typename T, int L>
+__device__ __forceinline__ void store_elems(T *p, const T *x) {
+  constexpr int V = 16 / (int)sizeof(T);
+  if constexpr (L % V == 0) {
+#pragma unroll
+    for (int j = 0; j < L; j += V) {
+      typename Frag<T>::type r;  // 8 elements for bf16; 8 fp32 = two pieces
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = x[j + i];
+        *reinterpret_cast<typename Frag<T>::type *>(p + j) = r;
+      } else {
+        *reinterpret_cast<f32x4 *>(p + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L; ++i) p[i] = x[i];
+  }
+}
 
 template <typename T, int D, int C>
 __global__ __launch_bounds__(256) void intra_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ gc, const float *__restrict__ beta,
-    const int4 *__restrict__ chunk_info, int H, T *__restrict__ qt_out,
-    T *__restrict__ w_out, T *__restrict__ ut_out, T *__restrict__ ket_out,
-    T *__restrict__ p_out, float *__restrict__ gam_out) {
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const int *__restrict__ cu, int N, int H, int seq_len, int *__restrict__ seq_first,
+    T *__restrict__ qt_out, T *__restrict__ w_out, T *__restrict__ ut_out,
+    T *__restrict__ ket_out, T *__restrict__ p_out, float *__restrict__ gam_out) {
   using Cfg = IntraCfg<T, D, C>;
-  constexpr int NRB = Cfg::NRB, NCB = Cfg::NCB, CK = Cfg::CK;
+  using F = typename Frag<T>::type;
+  constexpr int NRB = Cfg::NRB, NCB = Cfg::NCB, CK = Cfg::CK, NKB = Cfg::NKB;
+  constexpr int KD = Cfg::KD, KC = Cfg::KC, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
   constexpr int LDR = Cfg::LDR, LDT = Cfg::LDT, LDA = Cfg::LDA;
-  constexpr int GPR = Cfg::GPR, RPP = Cfg::RPP, NPASS = Cfg::NPASS;
+  constexpr int RUN = RPT < 4 ? RPT : 4;  // contiguous kperm positions per token run
 
   extern __shared__ __align__(16) char smem[];
-  T *sK = reinterpret_cast<T *>(smem);                       // [C][LDR]
-  T *sKh = reinterpret_cast<T *>(smem + Cfg::BYTES_ROW);     // [C][LDR]
-  T *sKbT = reinterpret_cast<T *>(smem);                     // [D][LDT] (later)
-  T *sVbT = reinterpret_cast<T *>(smem + Cfg::BYTES_TR);     // [D][LDT] (later)
-  T *sQ = reinterpret_cast<T *>(smem + Cfg::BYTES_X);        // [C][LDR]
-  float *sT = reinterpret_cast<float *>(smem + Cfg::BYTES_X);  // [C][LDA] (later)
+  T *sKt = reinterpret_cast<T *>(smem);                          // [C][LDR]
+  T *sKh = reinterpret_cast<T *>(smem + Cfg::BYTES_ROW);         // [C][LDR]
+  T *sQt = reinterpret_cast<T *>(smem + 2 * Cfg::BYTES_ROW);     // [C][LDR]
+  T *sBKt = reinterpret_cast<T *>(smem);                         // [D][LDT] (phase 3+)
+  T *sBVt = reinterpret_cast<T *>(smem + Cfg::BYTES_TR);         // [D][LDT] (phase 3+)
+  float *sA = reinterpret_cast<float *>(smem + Cfg::BYTES_X);    // [C][LDA] (phase 2+)
+  f32x4 *sTot = reinterpret_cast<f32x4 *>(smem + Cfg::BYTES_X);  // [RG][CG] (phase 1)
   float *sBeta = reinterpret_cast<float *>(smem + Cfg::BYTES_X + Cfg::BYTES_Y);
+  __shared__ int s_loc[4];
+  __shared__ int s_scan[256];
 
   const int c = blockIdx.x, h = blockIdx.y;
-  const int4 info = chunk_info[c];
-  const int t0 = info.y, n = info.z;
+  locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
+  const int t0 = s_loc[1], n = s_loc[2];
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t rs = (int64_t)H * D;  // token stride of [T, H, D] tensors
   const int64_t base = (int64_t)t0 * rs + (int64_t)h * D;
 
-  // ---------------- phase 1: elementwise scaling ----------------
-  const int ch0 = (tid % GPR) * 8;
-  float gl[8];
+  // ---------------- phase 1: cumulative decay and scaled rows ---------------
+  const int cg = tid % CG, rg = tid / CG;
+  const int ch0 = 4 * cg, r0 = rg * RPT;
+  f32x4 Gv[RPT];
   {
-    const float *p = gc + base + (int64_t)(n - 1) * rs + ch0;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-    gl[0] = a[0]; gl[1] = a[1]; gl[2] = a[2]; gl[3] = a[3];
-    gl[4] = b[0]; gl[5] = b[1]; gl[6] = b[2]; gl[7] = b[3];
+    f32x4 run = zero4();
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j;
+      if (r < n) run += *reinterpret_cast<const f32x4 *>(g + base + (int64_t)r * rs + ch0);
+      Gv[j] = run;
+    }
+    sTot[rg * CG + cg] = run;
   }
-  if (tid < GPR) {
-    float *gp = gam_out + tile * D + ch0;
-    *reinterpret_cast<f32x4 *>(gp) =
-        f32x4{__expf(gl[0]), __expf(gl[1]), __expf(gl[2]), __expf(gl[3])};
-    *reinterpret_cast<f32x4 *>(gp + 4) =
-        f32x4{__expf(gl[4]), __expf(gl[5]), __expf(gl[6]), __expf(gl[7])};
+  __syncthreads();
+  f32x4 pre = zero4(), tot = zero4();
+#pragma unroll 4
+  for (int i = 0; i < RG; ++i) {
+    const f32x4 x = sTot[i * CG + cg];
+    if (i < rg) pre += x;
+    tot += x;
   }
-  T kb_reg[NPASS][8], vb_reg[NPASS][8], ke_reg[NPASS][8];
+  if (rg == 0)
+    *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) =
+        f32x4{__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
+
   T *qt_tile = qt_out + tile * (C * D);
+  T *ke_tile = ket_out + tile * (D * CK);
+  T bk[4][RPT], bv[4][RPT];  // Diag(beta) Kt, Diag(beta) V per channel (phase 3)
+  float ke[4][RPT];          // Ke per channel
 #pragma unroll
-  for (int j = 0; j < NPASS; ++j) {
-    const int r = j * RPP + tid / GPR;
-    if (r >= C) continue;
-    float qt[8], kt[8], kh[8], kbv[8], vbv[8], kev[8];
-    if (r < n) {
-      const int64_t off = base + (int64_t)r * rs + ch0;
-      float G[8], qv[8], kv[8], vv[8];
-      load8_f32<float>(gc + off, G);
-      load8_f32<T>(q + off, qv);
-      load8_f32<T>(k + off, kv);
-      load8_f32<T>(v + off, vv);
-      const float br = beta[(int64_t)(t0 + r) * H + h];
-      if (tid % GPR == 0) sBeta[r] = br;
+  for (int j = 0; j < RPT; ++j) {
+    const int r = r0 + j;
+    if (r < C) {
+      f32x4 qv = zero4(), kv = zero4(), vv = zero4();
+      float br = 0.f;
+      if (r < n) {
+        const int64_t off = base + (int64_t)r * rs + ch0;
+        qv = to_f32x4(load4<T>(q + off));
+        kv = to_f32x4(load4<T>(k + off));
+        vv = to_f32x4(load4<T>(v + off));
+        br = beta[(int64_t)(t0 + r) * H + h];
+      }
+      if (cg == 0) sBeta[r] = br;
+      const f32x4 G = Gv[j] + pre;
+      f32x4 qt, kt, kh;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
         const float eg = __expf(G[e]);
-        const float eng = __expf(-G[e]);
-        const float ee = __expf(gl[e] - G[e]);
         qt[e] = qv[e] * eg;
         kt[e] = kv[e] * eg;
-        kh[e] = kv[e] * eng;
-        kbv[e] = br * kt[e];
-        vbv[e] = br * vv[e];
-        kev[e] = kv[e] * ee;
+        kh[e] = kv[e] * __expf(-G[e]);
+        ke[e][j] = kv[e] * __expf(tot[e] - G[e]);
+        bk[e][j] = from_f32<T>(br * kt[e]);
+        bv[e][j] = from_f32<T>(br * vv[e]);
       }
-    } else {
-      if (tid % GPR == 0) sBeta[r] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qt[e] = kt[e] = kh[e] = kbv[e] = vbv[e] = kev[e] = 0.f;
-    }
-    store8<T>(sQ + r * LDR + ch0, qt);
-    store8<T>(sK + r * LDR + ch0, kt);
-    store8<T>(sKh + r * LDR + ch0, kh);
-    // channels ch0..ch0+3 and ch0+4..ch0+7 are two contiguous runs in kperm order
-    store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0), D), f32x4{qt[0], qt[1], qt[2], qt[3]});
-    store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0 + 4), D),
-                  f32x4{qt[4], qt[5], qt[6], qt[7]});
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kb_reg[j][e] = from_f32<T>(kbv[e]);
-      vb_reg[j][e] = from_f32<T>(vbv[e]);
-      ke_reg[j][e] = from_f32<T>(kev[e]);
+      store4_f32<T>(sKt + r * LDR + ch0, kt);
+      store4_f32<T>(sKh + r * LDR + ch0, kh);
+      store4_f32<T>(sQt + r * LDR + ch0, qt);
+      // 4 consecutive channels are 4 consecutive kperm positions
+      store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0), D), qt);
     }
   }
-  __syncthreads();
-
-  // ---------------- phase 2: A and P on the matrix cores ----------------
-  constexpr int NLOW = NRB * (NRB + 1) / 2;  // lower tiles incl. diagonal
-  constexpr int NAW = (NLOW + 3) / 4;        // per wave
-  f32x4 a_keep[NAW];
-  int a_rb[NAW], a_cb[NAW];
-  T *p_tile = p_out + tile * (C * CK);
+  // Ke^T rows (channels) in token runs of up to 4 consecutive kperm positions
+  if (r0 < C) {
 #pragma unroll
-  for (int j = 0; j < NAW; ++j) {
-    a_rb[j] = -1;
-    a_cb[j] = 0;
-    a_keep[j] = zero4();
-    const int idx = wave + 4 * j;
-    if (idx >= NLOW) continue;
-    int rb = 0, rem = idx;
-    while (rem > rb) { rem -= rb + 1; ++rb; }
-    const int cb = rem;
-    f32x4 accA = zero4(), accP = zero4();
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const int kk = 32 * ks + 8 * lg;
-      const auto bk = load8<T>(sKh + (16 * cb + lr) * LDR + kk);
-      const auto ak = load8<T>(sK + (16 * rb + lr) * LDR + kk);
-      const auto aq = load8<T>(sQ + (16 * rb + lr) * LDR + kk);
-      accA = mma_k32(ak, bk, accA);
-      accP = mma_k32(aq, bk, accP);
-    }
-    const int col = 16 * cb + lr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * rb + 4 * lg + i;
-      accA[i] = (col < row) ? sBeta[row] * accA[i] : 0.f;
-      p_tile[frag_off(row, kperm_pos(col), CK)] = from_f32<T>((col <= row) ? accP[i] : 0.f);
-    }
-    a_keep[j] = accA;
-    a_rb[j] = rb;
-    a_cb[j] = cb;
+      for (int j = 0; j < RPT; j += RUN)
+        store_run<T, RUN>(ke_tile + frag_off(ch0 + e, kperm_pos(r0 + j), CK), &ke[e][j]);
   }
-  // zero the strictly-upper tiles of P and its padding columns
-  for (int e = tid; e < C * CK; e += 256) {
-    const int row = e / CK, col = kperm_idx(e % CK);
-    if (col >= C || (col / 16) > (row / 16)) p_tile[frag_off(row, e % CK, CK)] = from_f32<T>(0.f);
-  }
-  __syncthreads();
-
-  // ---------------- phase 3a: A into sT, transposed operands ----------------
-  for (int e = tid; e < C * LDA; e += 256) sT[e] = 0.f;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < NAW; ++j) {
-    if (a_rb[j] < 0) continue;
-    const int col = 16 * a_cb[j] + lr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sT[(16 * a_rb[j] + 4 * lg + i) * LDA + col] = a_keep[j][i];
-  }
-#pragma unroll
-  for (int j = 0; j < NPASS; ++j) {
-    const int r = j * RPP + tid / GPR;
-    if (r >= C) continue;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sKbT[(ch0 + e) * LDT + r] = kb_reg[j][e];
-      sVbT[(ch0 + e) * LDT + r] = vb_reg[j][e];
-    }
-  }
-  if (CK > C) {  // zero the padding tokens of the transposed operands
+  if (CK > C) {  // padding tokens of Ke^T are zero
     for (int e = tid; e < D * (CK - C); e += 256) {
       const int ch = e / (CK - C), r = C + e % (CK - C);
-      sKbT[ch * LDT + r] = from_f32<T>(0.f);
-      sVbT[ch * LDT + r] = from_f32<T>(0.f);
+      ke_tile[frag_off(ch, kperm_pos(r), CK)] = from_f32<T>(0.f);
     }
   }
   __syncthreads();
 
-  // ---------------- phase 3b: diagonal blocks, forward substitution -------
-  if (wave < NRB && lane < 16) {
-    const int b0 = 16 * wave;
-    const int jcol = lane;
+  // ---------------- phase 2: A and P^T on the matrix cores ------------------
+  // Every tile is computed, also those above the diagonal (masked to zero
+  // below; padding token blocks read a clamped in-chunk row): a branch
+  // between a matrix-core instruction and the reads of its result has been
+  // seen to return a stale register on gfx950, so results are only ever read
+  // in straight-line code after the instructions that produce them.
+  T *p_tile = p_out + tile * (C * CK);
+  for (int idx = wv; idx < NRB * NKB; idx += 4) {
+    const int rb = idx / NKB, cb = idx % NKB;
+    const int hrow = min(16 * cb + lr, C - 1);
+    f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) {
+      const int kk = 32 * ks + 8 * lg;
+      const F fk = load8<T>(sKt + (16 * rb + lr) * LDR + kk);
+      const F fh = load8<T>(sKh + hrow * LDR + kk);
+      const F fq = load8<T>(sQt + (16 * rb + lr) * LDR + kk);
+      accA = mma_k32(fk, fh, accA);  // A[16 rb + 4 lg + i][16 cb + lr]
+      accP = mma_k32(fh, fq, accP);  // P[16 rb + lr][16 cb + 4 lg + i]
+    }
+    const int acol = 16 * cb + lr;
+    f32x4 bta;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bta[i] = sBeta[16 * rb + 4 * lg + i];
+    const f32x4 av = accA * bta;  // branch-free: masks are selects
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int arow = 16 * rb + 4 * lg + i;
+      sA[arow * LDA + acol] = (acol < arow) ? av[i] : 0.f;
+      accP[i] = (16 * cb + 4 * lg + i <= 16 * rb + lr) ? accP[i] : 0.f;
+    }
+    store4_f32<T>(p_tile + frag_off(16 * rb + lr, kperm_pos(16 * cb + 4 * lg), CK), accP);
+  }
+  __syncthreads();
+
+  // ---------------- phase 3: staged B operands, T = (I + A)^-1 ---------------
+  if (r0 < C) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      store_elems<T, RPT>(sBKt + (ch0 + e) * LDT + r0, bk[e]);
+      store_elems<T, RPT>(sBVt + (ch0 + e) * LDT + r0, bv[e]);
+    }
+  }
+  if (CK > C) {
+    for (int e = tid; e < D * (CK - C); e += 256) {
+      const int ch = e / (CK - C), r = C + e % (CK - C);
+      sBKt[ch * LDT + r] = from_f32<T>(0.f);
+      sBVt[ch * LDT + r] = from_f32<T>(0.f);
+    }
+  }
+  // diagonal 16 x 16 blocks: lane j of wave b computes column j of T_bb
+  if (wv < NRB && lane < 16) {
+    const int b0 = 16 * wv, jcol = lane;
     float tcol[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m) tcol[m] = (m == jcol) ? 1.f : 0.f;
@@ -243,92 +339,63 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     for (int r = 1; r < 16; ++r) {
       float s = 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s += sT[(b0 + r) * LDA + b0 + m] * tcol[m];
+      for (int m = 0; m < r; ++m) s += sA[(b0 + r) * LDA + b0 + m] * tcol[m];
       if (jcol < r) tcol[r] = -s;
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) sT[(b0 + m) * LDA + b0 + jcol] = tcol[m];
+    for (int m = 0; m < 16; ++m) sA[(b0 + m) * LDA + b0 + jcol] = tcol[m];
   }
   __syncthreads();
-
-  // ---------------- phase 3c: off-diagonal blocks -------------------------
-  // T_ij = -T_ii X,  X = sum_{m=j}^{i-1} A_im T_mj, for block row i, j < i.
+  // blocks below the diagonal: T_ij = -T_ii X, X = sum_{m=j}^{i-1} A_im T_mj
 #pragma unroll
   for (int bi = 1; bi < NRB; ++bi) {
     f32x4 X = zero4();
-    const int bj = wave;
+    const int bj = wv;
     if (bj < bi) {
       for (int m = bj; m < bi; ++m) {
-        const f32x4 af = *reinterpret_cast<const f32x4 *>(
-            sT + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
+        const f32x4 af =
+            *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
         f32x4 bf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bf[i] = sT[(16 * m + 4 * lg + i) * LDA + 16 * bj + lr];
+        for (int i = 0; i < 4; ++i) bf[i] = sA[(16 * m + 4 * lg + i) * LDA + 16 * bj + lr];
         X = mma_f32_k16(af, bf, X);
       }
     }
     __syncthreads();
     if (bj < bi) {
-      const f32x4 af = *reinterpret_cast<const f32x4 *>(
-          sT + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
+      const f32x4 af =
+          *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
       const f32x4 Y = mma_f32_k16(af, X, zero4());
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * lg + i) * LDA + 16 * bj + lr] = -Y[i];
+      for (int i = 0; i < 4; ++i) sA[(16 * bi + 4 * lg + i) * LDA + 16 * bj + lr] = -Y[i];
     }
     __syncthreads();
   }
 
-  // ---------------- phase 4: W = T Diag(beta)Kt, U = T Diag(beta)V ---------
+  // ---------------- phase 4: W^T and U on the matrix cores -------------------
+  // For token block rb the T fragment (row 16 rb + lr, K-slot 8 lg..) is the
+  // A operand of U = T (Diag(beta) V) and the B operand of
+  // W^T = (Diag(beta) Kt)^T T^T.
   T *w_tile = w_out + tile * (C * D);
   T *ut_tile = ut_out + tile * (D * C);
-  constexpr int NWU = 2 * NRB * NCB;
-  for (int idx = wave; idx < NWU; idx += 4) {
-    const int which = idx / (NRB * NCB);  // 0 = W, 1 = U
-    const int rb = (idx % (NRB * NCB)) / NCB;
-    const int cb = idx % NCB;
-    const T *bsrc = which ? sVbT : sKbT;
-    f32x4 acc = zero4();
+  for (int rb = wv; rb < NRB; rb += 4) {
+    F tf[KC];
 #pragma unroll
-    for (int ks = 0; ks < CK / 32; ++ks) {
-      if (32 * ks > 16 * rb + 15) break;  // T is lower triangular
-      const int kk = 32 * ks + 8 * lg;
-      const auto a = frag_from_f32<T>(sT + (16 * rb + lr) * LDA + kk);
-      const auto b = load8<T>(bsrc + (16 * cb + lr) * LDT + kk);
-      acc = mma_k32(a, b, acc);
+    for (int ks = 0; ks < KC; ++ks)
+      tf[ks] = frag_from_f32<T>(sA + (16 * rb + lr) * LDA + 32 * ks + 8 * lg);
+#pragma unroll 2
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 accW = zero4(), accU = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {  // all K-steps: T is zero above its diagonal
+        const int kk = 32 * ks + 8 * lg;
+        accW = mma_k32(load8<T>(sBKt + (16 * cb + lr) * LDT + kk), tf[ks], accW);
+        accU = mma_k32(tf[ks], load8<T>(sBVt + (16 * cb + lr) * LDT + kk), accU);
+      }
+      // accW[i] = W[16 rb + lr][16 cb + 4 lg + i]; accU[i] = U[16 rb + 4 lg + i][16 cb + lr]
+      store4_f32<T>(w_tile + frag_off(16 * rb + lr, kperm_pos(16 * cb + 4 * lg), D), accW);
+      store4_f32<T>(ut_tile + tile_off(16 * rb + 4 * lg, 16 * cb + lr, C), accU);
     }
-    const int col = 16 * cb + lr;
-    if (which == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w_tile[frag_off(16 * rb + 4 * lg + i, kperm_pos(col), D)] = from_f32<T>(acc[i]);
-    } else {
-      store4_f32<T>(ut_tile + tile_off(16 * rb + 4 * lg, col, C), acc);
-    }
-  }
-  __syncthreads();
-
-  // ---------------- phase 5: Ke transposed, through LDS --------------------
-  T *sKeT = sKbT;
-#pragma unroll
-  for (int j = 0; j < NPASS; ++j) {
-    const int r = j * RPP + tid / GPR;
-    if (r >= C) continue;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sKeT[(ch0 + e) * LDT + kperm_pos(r)] = ke_reg[j][e];
-  }
-  if (CK > C) {
-    for (int e = tid; e < D * (CK - C); e += 256) {
-      const int ch = e / (CK - C), r = C + e % (CK - C);
-      sKeT[ch * LDT + kperm_pos(r)] = from_f32<T>(0.f);
-    }
-  }
-  __syncthreads();
-  T *ket_tile = ket_out + tile * (D * CK);
-  constexpr int V8 = CK / 8;  // 8-element vectors per row
-  for (int e = tid; e < D * V8; e += 256) {
-    const int ch = e / V8, x = (e % V8) * 8;
-    *reinterpret_cast<typename Frag<T>::type *>(ket_tile + frag_off(ch, x, CK)) =
-        load8<T>(sKeT + ch * LDT + x);
   }
 }
 
@@ -343,9 +410,8 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
   char *ws = a.ws;
   hipLaunchKernelGGL(kern, grid, dim3(256), Cfg::LDS_BYTES, a.stream,
                      reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
-                     reinterpret_cast<const T *>(a.v),
-                     reinterpret_cast<const float *>(ws + a.lay.gc), a.beta,
-                     reinterpret_cast<const int4 *>(ws + a.lay.chunk_info), a.num_heads,
+                     reinterpret_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.num_seqs,
+                     a.num_heads, a.seq_len, reinterpret_cast<int *>(ws + a.lay.seq_first),
                      reinterpret_cast<T *>(ws + a.lay.qt), reinterpret_cast<T *>(ws + a.lay.w),
                      reinterpret_cast<T *>(ws + a.lay.ut), reinterpret_cast<T *>(ws + a.lay.ket),
                      reinterpret_cast<T *>(ws + a.lay.p), reinterpret_cast<float *>(ws + a.lay.gam));

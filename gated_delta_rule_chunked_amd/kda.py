@@ -95,7 +95,7 @@ def workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: i
         _dtype_code(dtype)))
 
 
-STAGES = {"cumsum": 0, "intra": 1, "inter": 2}
+STAGES = {"intra": 0, "inter": 1}
 
 
 def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chunk_size,
@@ -156,7 +156,7 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     equal-length sequences; initial_state: fp32 [N, H, d, d] or None.
     Returns (o [T, H, d] in v's dtype, final_state fp32 [N, H, d, d] or None).
     `final_state` may be passed as the same tensor as `initial_state` to
-    update states in place.  `stage` ("cumsum", "intra" or "inter") runs only
+    update states in place.  `stage` ("intra" or "inter") runs only
     that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
     and `final_state` of a preceding call with the same arguments.
     """
@@ -198,8 +198,7 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
 
     Nothing is launched here.  Returns (call, stage_calls, o, final_state):
     `call()` runs the whole prefill and `stage_calls[name]()` one of its
-    kernels ("cumsum", "intra", "inter"; kda_fwd_chunked_stage) on the same
-    workspace.
+    kernels ("intra", "inter"; kda_fwd_chunked_stage) on the same workspace.
     """
     args, o, fs, ws = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
                                 initial_state, chunk_size, output_final_state, out,

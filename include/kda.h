@@ -126,19 +126,19 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            size_t workspace_bytes, void *stream);
 
 /*
- * The three kernels of kda_fwd_chunked, in launch order.  Exposed so that a
+ * The two kernels of kda_fwd_chunked, in launch order.  Exposed so that a
  * caller can time or schedule them separately.
  */
 typedef enum {
-  KDA_STAGE_CUMSUM = 0, /* chunk table + chunk-local cumulative log-decay  */
-  KDA_STAGE_INTRA = 1,  /* per-chunk A, P, UT inverse, WY factors W and U  */
-  KDA_STAGE_INTER = 2   /* state carried over chunks: o and final_state    */
+  KDA_STAGE_INTRA = 0, /* per chunk: cumulative log-decay, A, P, UT inverse,
+                          WY factors W and U                             */
+  KDA_STAGE_INTER = 1  /* state carried over chunks: o and final_state   */
 } kda_fwd_stage;
 
 /*
  * Enqueues one stage of kda_fwd_chunked with the same arguments and the
- * same validation.  kda_fwd_chunked == CUMSUM, INTRA, INTER in order on one
- * stream and one workspace.  A stage reads what the earlier stages left in
+ * same validation.  kda_fwd_chunked == INTRA then INTER on one stream and
+ * one workspace.  A stage reads what the earlier stages left in
  * the workspace, so it must follow them (stream order) with identical
  * arguments; re-running a stage on an unchanged workspace reproduces its
  * outputs (INTER is not idempotent when initial_state aliases final_state).

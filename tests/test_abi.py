@@ -95,14 +95,14 @@ def test_fwd_rejects_bad_arguments_on_host(lib):
 def test_stage_rejects_bad_stage_and_arguments(lib):
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, 256, 2, 128, 128, 64, 1, None, None,
             FAKE, FAKE, 1 << 40, None)
-    assert lib.kda_fwd_chunked_stage(3, *args) == 1
+    assert lib.kda_fwd_chunked_stage(2, *args) == 1  # stages are 0 (intra) and 1 (inter)
     assert lib.kda_fwd_chunked_stage(-1, *args) == 1
     bad = list(args)
     bad[0] = None
-    assert lib.kda_fwd_chunked_stage(1, *bad) == 1
+    assert lib.kda_fwd_chunked_stage(0, *bad) == 1
     bad = list(args)
     bad[9] = bad[10] = 96
-    assert lib.kda_fwd_chunked_stage(2, *bad) == 2
+    assert lib.kda_fwd_chunked_stage(1, *bad) == 2
 
 
 def _dec(lib, **over):
