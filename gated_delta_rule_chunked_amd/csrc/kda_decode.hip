@@ -13,6 +13,10 @@
 // one 16-byte write per four values.  Decode is bound by HBM bandwidth
 // (about one flop per byte).
 //
+// The state is streamed with nontemporal loads and stores: it is touched
+// once per step and would only evict other data from the caches (measured
+// about 7% faster on MI355X than plain accesses for 256 x 32 states).
+//
 // Block = one state.  Thread t owns float4 column group t % (d/4) and rows
 // r = t / (d/4) + i * (threads / (d/4)); at every step i the block reads or
 // writes a contiguous run of rows.  Column sums are reduced over the lanes of
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + i * NRG;
-    Sv[i] = *reinterpret_cast<const f32x4 *>(S + r * D + 4 * cq);
+    Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + r * D + 4 * cq));
     a[i] = __expf(gp[r]);
     kr[i] = to_f32(kp[r]);
     const float qr = to_f32(qp[r]);
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + i * NRG;
-    *reinterpret_cast<f32x4 *>(S + r * D + 4 * cq) = a[i] * Sv[i] + kr[i] * u;
+    __builtin_nontemporal_store(a[i] * Sv[i] + kr[i] * u, reinterpret_cast<f32x4 *>(S + r * D + 4 * cq));
   }
 }
 

@@ -201,15 +201,29 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   const int64_t base = (int64_t)t0 * rs + (int64_t)h * D;
 
   // ---------------- phase 1: cumulative decay and scaled rows ---------------
+  // Every load of the phase is issued up front and unconditionally (rows past
+  // the chunk end re-read its last row and are masked to zero afterwards), so
+  // a thread waits for one memory round trip instead of one per row.
   const int cg = tid % CG, rg = tid / CG;
   const int ch0 = 4 * cg, r0 = rg * RPT;
   f32x4 Gv[RPT];
+  typename Vec4<T>::type qr[RPT], kr[RPT], vr[RPT];
+  float brr[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = min(r0 + j, n - 1);
+    const int64_t off = base + (int64_t)r * rs + ch0;
+    Gv[j] = *reinterpret_cast<const f32x4 *>(g + off);
+    qr[j] = load4<T>(q + off);
+    kr[j] = load4<T>(k + off);
+    vr[j] = load4<T>(v + off);
+    brr[j] = beta[(int64_t)(t0 + r) * H + h];
+  }
   {
     f32x4 run = zero4();
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int r = r0 + j;
-      if (r < n) run += *reinterpret_cast<const f32x4 *>(g + base + (int64_t)r * rs + ch0);
+      run += (r0 + j < n) ? Gv[j] : zero4();
       Gv[j] = run;
     }
     sTot[rg * CG + cg] = run;
@@ -234,15 +248,11 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   for (int j = 0; j < RPT; ++j) {
     const int r = r0 + j;
     if (r < C) {
-      f32x4 qv = zero4(), kv = zero4(), vv = zero4();
-      float br = 0.f;
-      if (r < n) {
-        const int64_t off = base + (int64_t)r * rs + ch0;
-        qv = to_f32x4(load4<T>(q + off));
-        kv = to_f32x4(load4<T>(k + off));
-        vv = to_f32x4(load4<T>(v + off));
-        br = beta[(int64_t)(t0 + r) * H + h];
-      }
+      const bool live = r < n;
+      const f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
+      const f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
+      const f32x4 vv = live ? to_f32x4(vr[j]) : zero4();
+      const float br = live ? brr[j] : 0.f;
       if (cg == 0) sBeta[r] = br;
       const f32x4 G = Gv[j] + pre;
       f32x4 qt, kt, kh;
@@ -286,7 +296,10 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   // seen to return a stale register on gfx950, so results are only ever read
   // in straight-line code after the instructions that produce them.
   T *p_tile = p_out + tile * (C * CK);
-  for (int idx = wv; idx < NRB * NKB; idx += 4) {
+#pragma unroll
+  for (int it = 0; it < (NRB * NKB + 3) / 4; ++it) {
+    const int idx = wv + 4 * it;
+    if (idx >= NRB * NKB) break;
     const int rb = idx / NKB, cb = idx % NKB;
     const int hrow = min(16 * cb + lr, C - 1);
     f32x4 accA = zero4(), accP = zero4();
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks)
       tf[ks] = frag_from_f32<T>(sA + (16 * rb + lr) * LDA + 32 * ks + 8 * lg);
-#pragma unroll 2
+#pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       f32x4 accW = zero4(), accU = zero4();
 #pragma unroll
