@@ -216,9 +216,10 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
       for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[ks], oc);
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
-      // convert before any branch: matrix-core results are read only in
-      // straight-line code after the instructions that produce them
-      const V4 ov = vec4_from_f32<T>(oc);
+      // read (and convert) before any branch: matrix-core results are read
+      // only in straight-line code after the instructions that produce them;
+      // "+ 0" makes it a real VALU read also when T is fp32
+      const V4 ov = vec4_from_f32<T>(oc + 0.f);
       T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
       if (rows == C) {
 #pragma unroll
