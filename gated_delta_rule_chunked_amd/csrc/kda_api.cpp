@@ -35,6 +35,8 @@ kda_status check_fwd_sizes(int64_t total_tokens, int32_t num_seqs, int32_t num_h
     return KDA_ERROR_NOT_SUPPORTED;
   const int64_t max_chunks = (total_tokens + (int64_t)num_seqs * (chunk_size - 1)) / chunk_size;
   if (max_chunks > (int64_t)1 << 30 || num_heads > 65535) return KDA_ERROR_NOT_SUPPORTED;
+  // one workgroup per (chunk, head) tile on a 1-D grid
+  if (max_chunks * num_heads > (int64_t)1 << 22) return KDA_ERROR_NOT_SUPPORTED;
   return KDA_SUCCESS;
 }
 

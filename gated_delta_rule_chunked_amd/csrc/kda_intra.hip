@@ -105,6 +105,10 @@ __device__ void locate_chunk(int c, int h, const int *cu, int N, int seq_len, in
 
 template <typename T, int D, int C>
 struct IntraCfg {
+  // 4 wavefronts; two workgroups fit a CU (LDS bound).  8-wavefront
+  // workgroups, with half the rows per thread, measured slower on MI355X.
+  static constexpr int NT = 256;
+  static constexpr int NW = NT / 64;               // wavefronts per workgroup
   static constexpr int NRB = C / 16;               // 16-token blocks of the chunk
   static constexpr int NCB = D / 16;               // 16-channel blocks of a head
   static constexpr int CK = C < 32 ? 32 : C;       // token extent per K-step
@@ -112,7 +116,7 @@ struct IntraCfg {
   static constexpr int KD = D / 32;                // K-steps over channels
   static constexpr int KC = CK / 32;               // K-steps over tokens
   static constexpr int CG = D / 4;                 // 4-channel groups (phase 1)
-  static constexpr int RG = 256 / CG;              // token groups (phase 1)
+  static constexpr int RG = NT / CG;               // token groups (phase 1)
   static constexpr int RPT = (C + RG - 1) / RG;    // tokens per thread (phase 1)
   static constexpr int PAD = 16 / (int)sizeof(T);  // 16-byte row padding
   static constexpr int LDR = D + PAD;              // row-major [C][D] stride
@@ -120,7 +124,7 @@ struct IntraCfg {
   static constexpr int LDA = CK + 4;               // fp32 [C][CK] stride
   static constexpr int BYTES_ROW = C * LDR * (int)sizeof(T);
   static constexpr int BYTES_TR = D * LDT * (int)sizeof(T);
-  static constexpr int BYTES_X = (3 * BYTES_ROW > 2 * BYTES_TR) ? 3 * BYTES_ROW : 2 * BYTES_TR;
+  static constexpr int BYTES_X = (BYTES_ROW > BYTES_TR ? BYTES_ROW : BYTES_TR) * 3;
   static constexpr int BYTES_A = C * LDA * 4;
   static constexpr int BYTES_TOT = RG * CG * 16;   // phase-1 token-group totals (alias A)
   static constexpr int BYTES_Y = BYTES_A > BYTES_TOT ? BYTES_A : BYTES_TOT;
@@ -128,24 +132,41 @@ struct IntraCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(C % 16 == 0 && D % 32 == 0 && RPT * RG >= C, "tile shape");
   static_assert(RPT == 1 || RPT == 2 || RPT % 4 == 0, "token runs per thread");
+  static constexpr int NP = NRB * (NKB / 2);       // phase-2 (token block, key-block pair)
+  static constexpr int NQB = NRB * KD;             // 16 x 32 fragment blocks of Qt
+  static constexpr int NEB = NCB * KC;             // 16 x 32 fragment blocks of Ke^T
+  // phase 4: NW / NRB waves share a token block, CPW channel blocks each
+  static constexpr int WPR = NW / NRB;
+  static constexpr int CPW = (NCB + WPR - 1) / WPR;
+  static_assert(NW % NRB == 0, "phase-4 wave split");
 };
 
-// L consecutive elements stored from fp32 (L = 1, 2 or 4).
-template <typename T, int L>
-__device__ __forceinline__ void store_run(T *p, const float *x) {
-  if constexpr (L == 4) {
-    store4_f32<T>(p, f32x4{x[0], x[1], x[2], x[3]});
-  } else {
-#pragma unroll
-    for (int i = 0; i < L; ++i) p[i] = from_f32<T>(x[i]);
-  }
+// 8 consecutive elements from two fp32 quads (16 bytes for bf16).
+template <typename T>
+__device__ __forceinline__ void store8_f32(T *p, f32x4 a, f32x4 b) {
+  *reinterpret_cast<typename Frag<T>::type *>(p) = pack_quads<T>(a, b);
 }
 
-// L consecutive elements of one type, in 16-byte pieces when they fill them.
+// One lane's run of a fragment-major block: the 8 kperm positions 8 g .. 8 g + 7
+// of a 32-group hold indices 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, so
+// the run is two quads of a row-major LDS row, written as 8 consecutive
+// elements; a wavefront writes one contiguous 16 x 32 block.
+template <typename T>
+__device__ __forceinline__ void copy_run(T *dst, const T *row32) {
+  *reinterpret_cast<typename Frag<T>::type *>(dst) = join4(load4<T>(row32), load4<T>(row32 + 16));
+}
+
+// L consecutive elements of one type, in 16- or 8-byte pieces when they fill
+// them (p is aligned to the piece size).
 template <typename T, int L>
 __device__ __forceinline__ void store_elems(T *p, const T *x) {
   constexpr int V = 16 / (int)sizeof(T);
-  if constexpr (L % V == 0) {
+  if constexpr (sizeof(T) == 2 && L % V != 0 && L % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < L; j += 4)
+      *reinterpret_cast<typename Vec4<T>::type *>(p + j) =
+          typename Vec4<T>::type{x[j], x[j + 1], x[j + 2], x[j + 3]};
+  } else if constexpr (L % V == 0) {
 #pragma unroll
     for (int j = 0; j < L; j += V) {
       typename Frag<T>::type r;  // 8 elements for bf16; 8 fp32 = two pieces
@@ -164,7 +185,7 @@ __device__ __forceinline__ void store_elems(T *p, const T *x) {
 }
 
 template <typename T, int D, int C>
-__global__ __launch_bounds__(256) void intra_chunk_kernel(
+__global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int *__restrict__ cu, int N, int H, int seq_len, int *__restrict__ seq_first,
@@ -172,10 +193,10 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     T *__restrict__ ket_out, T *__restrict__ p_out, float *__restrict__ gam_out) {
   using Cfg = IntraCfg<T, D, C>;
   using F = typename Frag<T>::type;
+  constexpr int NT = Cfg::NT, NW = Cfg::NW;
   constexpr int NRB = Cfg::NRB, NCB = Cfg::NCB, CK = Cfg::CK, NKB = Cfg::NKB;
   constexpr int KD = Cfg::KD, KC = Cfg::KC, CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
   constexpr int LDR = Cfg::LDR, LDT = Cfg::LDT, LDA = Cfg::LDA;
-  constexpr int RUN = RPT < 4 ? RPT : 4;  // contiguous kperm positions per token run
 
   extern __shared__ __align__(16) char smem[];
   T *sKt = reinterpret_cast<T *>(smem);                          // [C][LDR]
@@ -183,13 +204,16 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   T *sQt = reinterpret_cast<T *>(smem + 2 * Cfg::BYTES_ROW);     // [C][LDR]
   T *sBKt = reinterpret_cast<T *>(smem);                         // [D][LDT] (phase 3+)
   T *sBVt = reinterpret_cast<T *>(smem + Cfg::BYTES_TR);         // [D][LDT] (phase 3+)
+  T *sKeT = reinterpret_cast<T *>(smem + 2 * Cfg::BYTES_TR);     // [D][LDT] (phase 3+)
   float *sA = reinterpret_cast<float *>(smem + Cfg::BYTES_X);    // [C][LDA] (phase 2+)
   f32x4 *sTot = reinterpret_cast<f32x4 *>(smem + Cfg::BYTES_X);  // [RG][CG] (phase 1)
   float *sBeta = reinterpret_cast<float *>(smem + Cfg::BYTES_X + Cfg::BYTES_Y);
   __shared__ int s_loc[4];
-  __shared__ int s_scan[256];
+  __shared__ int s_scan[NT];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  // heads vary fastest over the grid: the tiles resident together then read
+  // whole token rows of the [T, H, d] inputs instead of one head's slice
+  const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
   const int t0 = s_loc[1], n = s_loc[2];
   if (n == 0) return;
@@ -240,10 +264,9 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) =
         f32x4{__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
 
-  T *qt_tile = qt_out + tile * (C * D);
-  T *ke_tile = ket_out + tile * (D * CK);
-  T bk[4][RPT], bv[4][RPT];  // Diag(beta) Kt, Diag(beta) V per channel (phase 3)
-  float ke[4][RPT];          // Ke per channel
+  // Per channel of this thread's token run: Diag(beta) Kt, Diag(beta) V and
+  // Ke, staged transposed in phase 3.
+  T bk[4][RPT], bv[4][RPT], ke[4][RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int r = r0 + j;
@@ -262,68 +285,66 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
         qt[e] = qv[e] * eg;
         kt[e] = kv[e] * eg;
         kh[e] = kv[e] * __expf(-G[e]);
-        ke[e][j] = kv[e] * __expf(tot[e] - G[e]);
+        ke[e][j] = from_f32<T>(kv[e] * __expf(tot[e] - G[e]));
         bk[e][j] = from_f32<T>(br * kt[e]);
         bv[e][j] = from_f32<T>(br * vv[e]);
       }
       store4_f32<T>(sKt + r * LDR + ch0, kt);
       store4_f32<T>(sKh + r * LDR + ch0, kh);
       store4_f32<T>(sQt + r * LDR + ch0, qt);
-      // 4 consecutive channels are 4 consecutive kperm positions
-      store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0), D), qt);
-    }
-  }
-  // Ke^T rows (channels) in token runs of up to 4 consecutive kperm positions
-  if (r0 < C) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int j = 0; j < RPT; j += RUN)
-        store_run<T, RUN>(ke_tile + frag_off(ch0 + e, kperm_pos(r0 + j), CK), &ke[e][j]);
-  }
-  if (CK > C) {  // padding tokens of Ke^T are zero
-    for (int e = tid; e < D * (CK - C); e += 256) {
-      const int ch = e / (CK - C), r = C + e % (CK - C);
-      ke_tile[frag_off(ch, kperm_pos(r), CK)] = from_f32<T>(0.f);
     }
   }
   __syncthreads();
 
-  // ---------------- phase 2: A and P^T on the matrix cores ------------------
+  // ---------------- phase 2: Qt out; A and P on the matrix cores ------------
+  // Qt leaves from LDS one contiguous 16 x 32 fragment block per wavefront
+  // store (rows past the chunk end are zero).
+  T *qt_tile = qt_out + tile * (C * D);
+  for (int b = wv; b < Cfg::NQB; b += NW) {
+    const int rb = b / KD, ks = b % KD;
+    copy_run<T>(qt_tile + b * 512 + lane * 8, sQt + (16 * rb + lr) * LDR + 32 * ks + 4 * lg);
+  }
+  // Each wave takes a token block and a pair of key blocks 2m, 2m + 1, whose
+  // P columns are adjacent kperm positions: one 16-byte store per lane.
   // Every tile is computed, also those above the diagonal (masked to zero
-  // below; padding token blocks read a clamped in-chunk row): a branch
-  // between a matrix-core instruction and the reads of its result has been
-  // seen to return a stale register on gfx950, so results are only ever read
-  // in straight-line code after the instructions that produce them.
+  // below; padding key blocks read a clamped in-chunk row): a branch between a
+  // matrix-core instruction and the reads of its result has been seen to
+  // return a stale register on gfx950, so results are only ever read in
+  // straight-line code after the instructions that produce them.
   T *p_tile = p_out + tile * (C * CK);
 #pragma unroll
-  for (int it = 0; it < (NRB * NKB + 3) / 4; ++it) {
-    const int idx = wv + 4 * it;
-    if (idx >= NRB * NKB) break;
-    const int rb = idx / NKB, cb = idx % NKB;
-    const int hrow = min(16 * cb + lr, C - 1);
-    f32x4 accA = zero4(), accP = zero4();
+  for (int it = 0; it < (Cfg::NP + NW - 1) / NW; ++it) {
+    const int idx = wv + NW * it;
+    if (idx >= Cfg::NP) break;
+    const int rb = idx / (NKB / 2), m = idx % (NKB / 2);
+    const int hrow0 = min(32 * m + lr, C - 1), hrow1 = min(32 * m + 16 + lr, C - 1);
+    f32x4 accA0 = zero4(), accA1 = zero4(), accP0 = zero4(), accP1 = zero4();
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) {
       const int kk = 32 * ks + 8 * lg;
       const F fk = load8<T>(sKt + (16 * rb + lr) * LDR + kk);
-      const F fh = load8<T>(sKh + hrow * LDR + kk);
       const F fq = load8<T>(sQt + (16 * rb + lr) * LDR + kk);
-      accA = mma_k32(fk, fh, accA);  // A[16 rb + 4 lg + i][16 cb + lr]
-      accP = mma_k32(fh, fq, accP);  // P[16 rb + lr][16 cb + 4 lg + i]
+      const F fh0 = load8<T>(sKh + hrow0 * LDR + kk);
+      const F fh1 = load8<T>(sKh + hrow1 * LDR + kk);
+      accA0 = mma_k32(fk, fh0, accA0);  // A[16 rb + 4 lg + i][32 m + lr]
+      accA1 = mma_k32(fk, fh1, accA1);  // A[16 rb + 4 lg + i][32 m + 16 + lr]
+      accP0 = mma_k32(fh0, fq, accP0);  // P[16 rb + lr][32 m + 4 lg + i]
+      accP1 = mma_k32(fh1, fq, accP1);  // P[16 rb + lr][32 m + 16 + 4 lg + i]
     }
-    const int acol = 16 * cb + lr;
     f32x4 bta;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bta[i] = sBeta[16 * rb + 4 * lg + i];
-    const f32x4 av = accA * bta;  // branch-free: masks are selects
+    const f32x4 av0 = accA0 * bta, av1 = accA1 * bta;  // branch-free: masks are selects
+    const int prow = 16 * rb + lr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int arow = 16 * rb + 4 * lg + i;
-      sA[arow * LDA + acol] = (acol < arow) ? av[i] : 0.f;
-      accP[i] = (16 * cb + 4 * lg + i <= 16 * rb + lr) ? accP[i] : 0.f;
+      sA[arow * LDA + 32 * m + lr] = (32 * m + lr < arow) ? av0[i] : 0.f;
+      sA[arow * LDA + 32 * m + 16 + lr] = (32 * m + 16 + lr < arow) ? av1[i] : 0.f;
+      accP0[i] = (32 * m + 4 * lg + i <= prow) ? accP0[i] : 0.f;
+      accP1[i] = (32 * m + 16 + 4 * lg + i <= prow) ? accP1[i] : 0.f;
     }
-    store4_f32<T>(p_tile + frag_off(16 * rb + lr, kperm_pos(16 * cb + 4 * lg), CK), accP);
+    store8_f32<T>(p_tile + frag_off(prow, 32 * m + 8 * lg, CK), accP0, accP1);
   }
   __syncthreads();
 
@@ -333,13 +354,15 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
     for (int e = 0; e < 4; ++e) {
       store_elems<T, RPT>(sBKt + (ch0 + e) * LDT + r0, bk[e]);
       store_elems<T, RPT>(sBVt + (ch0 + e) * LDT + r0, bv[e]);
+      store_elems<T, RPT>(sKeT + (ch0 + e) * LDT + r0, ke[e]);
     }
   }
-  if (CK > C) {
-    for (int e = tid; e < D * (CK - C); e += 256) {
+  if (CK > C) {  // padding tokens are zero
+    for (int e = tid; e < D * (CK - C); e += NT) {
       const int ch = e / (CK - C), r = C + e % (CK - C);
       sBKt[ch * LDT + r] = from_f32<T>(0.f);
       sBVt[ch * LDT + r] = from_f32<T>(0.f);
+      sKeT[ch * LDT + r] = from_f32<T>(0.f);
     }
   }
   // diagonal 16 x 16 blocks: lane j of wave b computes column j of T_bb
@@ -389,15 +412,24 @@ __global__ __launch_bounds__(256) void intra_chunk_kernel(
   // For token block rb the T fragment (row 16 rb + lr, K-slot 8 lg..) is the
   // A operand of U = T (Diag(beta) V) and the B operand of
   // W^T = (Diag(beta) Kt)^T T^T.
+  T *ke_tile = ket_out + tile * (D * CK);
+  for (int b = wv; b < Cfg::NEB; b += NW) {  // Ke^T blocks, as Qt in phase 2
+    const int cb = b / KC, ks = b % KC;
+    copy_run<T>(ke_tile + b * 512 + lane * 8, sKeT + (16 * cb + lr) * LDT + 32 * ks + 4 * lg);
+  }
   T *w_tile = w_out + tile * (C * D);
   T *ut_tile = ut_out + tile * (D * C);
-  for (int rb = wv; rb < NRB; rb += 4) {
+  {
+    constexpr int CPW = Cfg::CPW;
+    const int rb = wv % NRB, cb0 = (wv / NRB) * CPW;
     F tf[KC];
 #pragma unroll
     for (int ks = 0; ks < KC; ++ks)
       tf[ks] = frag_from_f32<T>(sA + (16 * rb + lr) * LDA + 32 * ks + 8 * lg);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int j = 0; j < CPW; ++j) {
+      const int cb = cb0 + j;
+      if (CPW * Cfg::WPR != NCB && cb >= NCB) break;  // uniform
       f32x4 accW = zero4(), accU = zero4();
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) {  // all K-steps: T is zero above its diagonal
@@ -419,9 +451,9 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
   static const hipError_t attr = hipFuncSetAttribute(
       (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  const dim3 grid((unsigned)a.grid_chunks, (unsigned)a.num_heads);
+  const dim3 grid((unsigned)a.grid_chunks * (unsigned)a.num_heads);
   char *ws = a.ws;
-  hipLaunchKernelGGL(kern, grid, dim3(256), Cfg::LDS_BYTES, a.stream,
+  hipLaunchKernelGGL(kern, grid, dim3(Cfg::NT), Cfg::LDS_BYTES, a.stream,
                      reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
                      reinterpret_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.num_seqs,
                      a.num_heads, a.seq_len, reinterpret_cast<int *>(ws + a.lay.seq_first),

@@ -34,6 +34,10 @@
  *     always fp32.
  *   - Supported head sizes: d_k == d_v in {32, 64, 128} for bf16 and
  *     {32, 64} for fp32; other shapes return KDA_ERROR_NOT_SUPPORTED.
+ *   - Size limits (KDA_ERROR_NOT_SUPPORTED beyond them): total_tokens <=
+ *     2^30, num_seqs * num_heads <= 2^26, num_heads <= 65535 and at most
+ *     2^22 (chunk, head) tiles, where a call has at most
+ *     (total_tokens + num_seqs * (chunk_size - 1)) / chunk_size chunks.
  *   - No C++ exception crosses this interface.
  */
 #ifndef KDA_H_

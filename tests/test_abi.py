@@ -90,6 +90,8 @@ def test_fwd_rejects_bad_arguments_on_host(lib):
     assert _fwd(lib, dk=128, dv=64) == 2
     assert _fwd(lib, C=128) == 2
     assert _fwd(lib, dt=0) == 2                      # fp32 with d = 128
+    assert _fwd(lib, n=1, T=1 << 24, H=1024) == 2    # 2^28 (chunk, head) tiles
+    assert _fwd(lib, n=1, T=1 << 22, H=64, wsb=16) == 1  # 2^22 tiles pass, workspace fails
 
 
 def test_stage_rejects_bad_stage_and_arguments(lib):
