@@ -22,11 +22,19 @@ Also reported on the same JSON line:
                 decode, the decode kernel's achieved HBM GB/s.
 Inputs come from gated_delta_rule_chunked_amd.inputs (seeded, synthetic).
 Only one GPU is supported: --gpus above 1 exits with an error.
+
+`roofline.traffic` is the dominant kernel's HBM bytes per launch as read by
+the FETCH_SIZE and WRITE_SIZE counters (profiles/hbm_traffic_counters.md,
+scaled by what the same counters read for a plain device copy of known
+size, `--only copy`).  It is null when that file holds no reading for the
+kernel or when the kernel's sources have changed since the reading.
 """
 import argparse
 import concurrent.futures
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,6 +77,41 @@ def prefill_flops_per_token_head(d, C):
 
 def state_bytes(d):
     return 4 * d * d
+
+
+# ---------------------------------------------------------------- counters
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+CSRC = os.path.join(ROOT, "gated_delta_rule_chunked_amd", "csrc")
+KERNEL_SOURCES = {"intra": "kda_intra.hip", "inter": "kda_inter.hip",
+                  "decode_kernel": "kda_decode.hip"}
+
+
+def kernel_source_sha(kernel):
+    """sha256 over a kernel's source file and the headers it includes."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "kda_common.hpp", "kda_internal.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter readings, or None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if m is None:
+        return None
+    data = json.loads(m.group(1))
+    rec = data["kernels"].get(f"{workload}/{kernel}")
+    if rec is None or rec["sources_sha256"] != kernel_source_sha(kernel):
+        return None
+    return (rec["fetch_kib"] * 1024 * data["fetch_scale"] +
+            rec["write_kib"] * 1024 * data["write_scale"])
 
 
 def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0):
@@ -170,7 +213,7 @@ def prefill_report(w, res, d, E, C):
     return out
 
 
-def dominant_roofline(w, res, d, E, C):
+def dominant_roofline(wname, w, res, d, E, C):
     ku = res["kernel_us"]
     name = max(ku, key=ku.get)
     th = w.total_tokens * w.num_heads
@@ -178,7 +221,7 @@ def dominant_roofline(w, res, d, E, C):
                      w.initial_state is not None)
     ach = b / (ku[name] * 1e-6) / 1e9
     return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=ach / HBM_PEAK_GBS, traffic=None, kernel=name,
+                frac=ach / HBM_PEAK_GBS, traffic=measured_traffic(wname, name), kernel=name,
                 bytes_per_launch=b, avg_launch_us=ku[name])
 
 
@@ -243,7 +286,8 @@ def time_decode(torch, kda, cfg, n_steps, warmup):
                 tokens_per_s=B * n_steps / (ms * 1e-3), us_per_step=step_us,
                 roofline_steps_per_s=1e6 / roof_us, roofline_frac=roof_us / step_us,
                 roofline=dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=ach / HBM_PEAK_GBS, traffic=None,
+                              frac=ach / HBM_PEAK_GBS,
+                              traffic=measured_traffic("decode", "decode_kernel"),
                               kernel="decode_kernel", bytes_per_launch=byts,
                               avg_launch_us=step_us))
 
@@ -287,6 +331,36 @@ def cpu_baseline_decode(cfg, seconds):
                        f"fp64, {spent:.1f} s (input generation excluded)")
 
 
+# ---------------------------------------------------------------- copy
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch, steps, warmup):
+    """A plain device copy of COPY_BYTES (read once, written once, negated): what the
+    memory-traffic counters read for it scales their readings on the
+    kernels."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    # an elementwise kernel (a same-type copy_ may go to a DMA engine)
+    for _ in range(warmup):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"copy {COPY_BYTES} B: {ms * 1e3:.1f} us, {2 * COPY_BYTES / ms / 1e6:.0f} GB/s "
+        f"(read + write)")
+    print(json.dumps({"metric": "device copy (read + write) GB/s, counter calibration",
+                      "value": 2 * COPY_BYTES / ms / 1e6, "unit": "GB/s", "n_gpus": 1,
+                      "steps": steps, "warmup": warmup, "ms_per_step": ms,
+                      "higher_is_better": True, "copy_bytes": COPY_BYTES}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -299,8 +373,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["prefill", "long", "varlen", "decode"],
-                    help="run one workload only (profiling runs); its throughput is `value`")
+    ap.add_argument("--only", choices=["prefill", "long", "varlen", "decode", "copy"],
+                    help="run one workload only (profiling runs); its throughput is `value`. "
+                         "'copy' times a plain 1 GiB device copy, the reference for the "
+                         "memory-traffic counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -318,6 +394,9 @@ def main():
         print("bench.py: no ROCm GPU visible", file=sys.stderr)
         sys.exit(1)
     kda.library()  # fail loudly if the HIP library is missing
+    if args.only == "copy":
+        copy_calibration(torch, args.steps, args.warmup)
+        return
 
     # headline: chunked prefill B=2, H=8, T=2048
     cfg1 = kin.WORKLOADS[1]
@@ -329,7 +408,7 @@ def main():
         log(f"prefill B=2 H=8 T=2048: {args.warmup} warmup + {args.steps} timed steps")
         r1 = time_prefill(torch, kda, w1, args.steps, args.warmup)
         workloads["prefill"] = prefill_report(w1, r1, d, E, C)
-        roof = dominant_roofline(w1, r1, d, E, C)
+        roof = dominant_roofline("prefill", w1, r1, d, E, C)
         log(f"  {workloads['prefill']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
             f"{workloads['prefill']['ms_per_step'] * 1e3:.1f} us/step, kernels(us) "
             f"{json.dumps({k: round(v, 2) for k, v in r1['kernel_us'].items()})}")
@@ -338,7 +417,7 @@ def main():
         w2 = kin.workload(2)
         r2 = time_prefill(torch, kda, w2, min(args.steps, 20), min(args.warmup, 3))
         workloads["long"] = prefill_report(w2, r2, d, E, C)
-        workloads["long"]["roofline"] = dominant_roofline(w2, r2, d, E, C)
+        workloads["long"]["roofline"] = dominant_roofline("long", w2, r2, d, E, C)
         log(f"  {workloads['long']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
             f"frac {workloads['long']['roofline_frac']:.3f}, kernels(us) "
             f"{json.dumps({k: round(v, 2) for k, v in r2['kernel_us'].items()})}")
@@ -348,7 +427,7 @@ def main():
         w3 = kin.workload(3)
         r3 = time_prefill(torch, kda, w3, min(args.steps, 20), min(args.warmup, 3))
         workloads["varlen"] = prefill_report(w3, r3, d, E, C)
-        workloads["varlen"]["roofline"] = dominant_roofline(w3, r3, d, E, C)
+        workloads["varlen"]["roofline"] = dominant_roofline("varlen", w3, r3, d, E, C)
         workloads["varlen"]["total_tokens"] = w3.total_tokens
         log(f"  {workloads['varlen']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
             f"frac {workloads['varlen']['roofline_frac']:.3f}, kernels(us) "
