@@ -103,6 +103,11 @@ __device__ void locate_chunk(int c, int h, const int *cu, int N, int seq_len, in
   __syncthreads();
 }
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 template <typename T, int D, int C>
 struct IntraCfg {
   // 4 wavefronts; two workgroups fit a CU (LDS bound).  8-wavefront
@@ -215,7 +220,8 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   // whole token rows of the [T, H, d] inputs instead of one head's slice
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
-  const int t0 = s_loc[1], n = s_loc[2];
+  const int t0 = __builtin_amdgcn_readfirstlane(s_loc[1]);
+  const int n = __builtin_amdgcn_readfirstlane(s_loc[2]);
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const int tid = threadIdx.x, lane = lane_id();
@@ -227,73 +233,91 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   // ---------------- phase 1: cumulative decay and scaled rows ---------------
   // Every load of the phase is issued up front and unconditionally (rows past
   // the chunk end re-read its last row and are masked to zero afterwards), so
-  // a thread waits for one memory round trip instead of one per row.
+  // a thread waits for one memory round trip instead of one per row.  The
+  // tile's base addresses are wavefront-uniform; per-row offsets are 32-bit
+  // byte offsets (a tile spans at most 64 rows of H * d <= 2^23 elements).
   const int cg = tid % CG, rg = tid / CG;
   const int ch0 = 4 * cg, r0 = rg * RPT;
+  const char *gb = reinterpret_cast<const char *>(g + base);
+  const char *qb = reinterpret_cast<const char *>(q + base);
+  const char *kb = reinterpret_cast<const char *>(k + base);
+  const char *vb = reinterpret_cast<const char *>(v + base);
+  const char *bb = reinterpret_cast<const char *>(beta + ((int64_t)t0 * H + h));
   f32x4 Gv[RPT];
   typename Vec4<T>::type qr[RPT], kr[RPT], vr[RPT];
   float brr[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
-    const int r = min(r0 + j, n - 1);
-    const int64_t off = base + (int64_t)r * rs + ch0;
-    Gv[j] = *reinterpret_cast<const f32x4 *>(g + off);
-    qr[j] = load4<T>(q + off);
-    kr[j] = load4<T>(k + off);
-    vr[j] = load4<T>(v + off);
-    brr[j] = beta[(int64_t)(t0 + r) * H + h];
+    const unsigned r = (unsigned)min(r0 + j, n - 1);
+    const unsigned off = r * (unsigned)rs + (unsigned)ch0;
+    Gv[j] = *reinterpret_cast<const f32x4 *>(gb + off * 4u);
+    qr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(qb + off * (unsigned)sizeof(T));
+    kr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(kb + off * (unsigned)sizeof(T));
+    vr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(vb + off * (unsigned)sizeof(T));
+    brr[j] = *reinterpret_cast<const float *>(bb + r * (unsigned)H * 4u);
   }
-  {
-    f32x4 run = zero4();
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      run += (r0 + j < n) ? Gv[j] : zero4();
-      Gv[j] = run;
-    }
-    sTot[rg * CG + cg] = run;
-  }
-  __syncthreads();
-  f32x4 pre = zero4(), tot = zero4();
-#pragma unroll 4
-  for (int i = 0; i < RG; ++i) {
-    const f32x4 x = sTot[i * CG + cg];
-    if (i < rg) pre += x;
-    tot += x;
-  }
-  if (rg == 0)
-    *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) =
-        f32x4{__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
 
   // Per channel of this thread's token run: Diag(beta) Kt, Diag(beta) V and
   // Ke, staged transposed in phase 3.
   T bk[4][RPT], bv[4][RPT], ke[4][RPT];
+  // Full chunks (every tile but a sequence's last) skip the row masks.
+  auto scaled_rows = [&](auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    {
+      f32x4 run = zero4();
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) {
-    const int r = r0 + j;
-    if (r < C) {
-      const bool live = r < n;
-      const f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
-      const f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
-      const f32x4 vv = live ? to_f32x4(vr[j]) : zero4();
-      const float br = live ? brr[j] : 0.f;
-      if (cg == 0) sBeta[r] = br;
-      const f32x4 G = Gv[j] + pre;
-      f32x4 qt, kt, kh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float eg = __expf(G[e]);
-        qt[e] = qv[e] * eg;
-        kt[e] = kv[e] * eg;
-        kh[e] = kv[e] * __expf(-G[e]);
-        ke[e][j] = from_f32<T>(kv[e] * __expf(tot[e] - G[e]));
-        bk[e][j] = from_f32<T>(br * kt[e]);
-        bv[e][j] = from_f32<T>(br * vv[e]);
+      for (int j = 0; j < RPT; ++j) {
+        // row slots past the chunk (when RG * RPT > C) or past its end add nothing
+        const bool in = TAIL ? r0 + j < n : (RG * RPT == C || r0 + j < C);
+        run += in ? Gv[j] : zero4();
+        Gv[j] = run;
       }
-      store4_f32<T>(sKt + r * LDR + ch0, kt);
-      store4_f32<T>(sKh + r * LDR + ch0, kh);
-      store4_f32<T>(sQt + r * LDR + ch0, qt);
+      sTot[rg * CG + cg] = run;
     }
-  }
+    __syncthreads();
+    f32x4 pre = zero4(), tot = zero4();
+#pragma unroll 4
+    for (int i = 0; i < RG; ++i) {
+      const f32x4 x = sTot[i * CG + cg];
+      if (i < rg) pre += x;
+      tot += x;
+    }
+    const f32x4 etot = {__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
+    if (rg == 0) *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
+    // e^-G = 1 / e^G and e^(G_n - G) = e^G_n / e^G: in range for G > -80
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j;
+      if (r < C) {
+        const bool live = !TAIL || r < n;
+        const f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
+        const f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
+        const f32x4 vv = live ? to_f32x4(vr[j]) : zero4();
+        const float br = live ? brr[j] : 0.f;
+        if (cg == 0) sBeta[r] = br;
+        const f32x4 G = Gv[j] + pre;
+        f32x4 qt, kt, kh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float eg = __expf(G[e]);
+          const float ei = __builtin_amdgcn_rcpf(eg);
+          qt[e] = qv[e] * eg;
+          kt[e] = kv[e] * eg;
+          kh[e] = kv[e] * ei;
+          ke[e][j] = from_f32<T>(kv[e] * (ei * etot[e]));
+          bk[e][j] = from_f32<T>(br * kt[e]);
+          bv[e][j] = from_f32<T>(br * vv[e]);
+        }
+        store4_f32<T>(sKt + r * LDR + ch0, kt);
+        store4_f32<T>(sKh + r * LDR + ch0, kh);
+        store4_f32<T>(sQt + r * LDR + ch0, qt);
+      }
+    }
+  };
+  if (n == C)
+    scaled_rows(Flag<false>{});
+  else
+    scaled_rows(Flag<true>{});
   __syncthreads();
 
   // ---------------- phase 2: Qt out; A and P on the matrix cores ------------
