@@ -17,9 +17,11 @@ Also reported on the same JSON line:
                 cores on repeated whole copies of the headline batch
   workloads     long-context prefill (B=1, H=32, T=32768), varlen packed
                 prefill (16 seqs of U[512, 8192] tokens, H=16, initial
-                states) and recurrent decode (batch 256, H=32, 1000 steps) --
-                each with throughput, fraction of its roofline and, for
-                decode, the decode kernel's achieved HBM GB/s.
+                states), the headline prefill in raw form (input-side fusion:
+                softplus gate from bf16 z, q/k L2-normalised in the kernel,
+                beta from logits) and recurrent decode (batch 256, H=32, 1000
+                steps) -- each with throughput, fraction of its roofline and,
+                for decode, the decode kernel's achieved HBM GB/s.
 Inputs come from gated_delta_rule_chunked_amd.inputs (seeded, synthetic).
 Only one GPU is supported: --gpus above 1 exits with an error.
 
@@ -63,9 +65,10 @@ def log(msg):
 # (sequence, head) state for decode).  E = bytes per q/k/v/o element, d the
 # head size, C the chunk size.
 
-def prefill_bytes_per_token_head(d, E):
-    """q, k, v, o in the operand type, fp32 log-decay, fp32 beta."""
-    return 4 * E * d + 4 * d + 4
+def prefill_bytes_per_token_head(d, E, raw=False):
+    """q, k, v, o in the operand type, fp32 log-decay, fp32 beta; in raw form
+    the gate input z in the operand type replaces the fp32 log-decay."""
+    return 4 * E * d + (E * d if raw else 4 * d) + 4
 
 
 def prefill_flops_per_token_head(d, C):
@@ -114,12 +117,13 @@ def measured_traffic(workload, kernel):
             rec["write_kib"] * 1024 * data["write_scale"])
 
 
-def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0):
+def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0, raw=False):
     """Algorithmic HBM bytes of one launch of a prefill kernel: what it must
     read and write given the two-kernel split (workspace tensors count)."""
     CK = max(C, 32)
-    if stage == "intra":      # read q, k, v, g, beta; write Qt, W, U, Ke, P, e^G_n
-        return token_heads * (3 * E * d + 4 * d + 4 + 4 * E * d + E * CK + 4 * d / C)
+    if stage == "intra":      # read q, k, v, g (or z), beta; write Qt, W, U, Ke, P, e^G_n
+        gate = E * d if raw else 4 * d
+        return token_heads * (3 * E * d + gate + 4 + 4 * E * d + E * CK + 4 * d / C)
     if stage == "inter":      # read Qt, W, U, Ke, P, e^G_n; write o; states
         return (token_heads * (5 * E * d + E * CK + 4 * d / C) +
                 pairs * state_bytes(d) * (2 if with_s0 else 1))
@@ -156,13 +160,31 @@ def upload_prefill(torch, w):
                 initial_state=s0)
 
 
+def upload_prefill_raw(torch, w):
+    """Raw-form workload (inputs.RawPrefill) -> bind_fwd arguments."""
+    def op(a):
+        if w.dtype == kin.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    opt = w.options()
+    if opt["gate_A"] is not None:
+        opt["gate_A"] = torch.from_numpy(np.ascontiguousarray(opt["gate_A"])).cuda()
+    return dict(q=op(w.q), k=op(w.k), v=op(w.v), log_alpha=op(w.z),
+                beta=torch.from_numpy(np.ascontiguousarray(w.beta_logits)).cuda(),
+                cu_seqlens=None, num_seqs=w.num_seqs, initial_state=None, options=opt)
+
+
 def time_prefill(torch, kda, w, steps, warmup, per_kernel=True):
     """Times `steps` whole prefill calls, then each kernel separately."""
-    d_in = upload_prefill(torch, w)
+    raw = isinstance(w, kin.RawPrefill)
+    d_in = upload_prefill_raw(torch, w) if raw else upload_prefill(torch, w)
     call, stages, o, fs = kda.bind_fwd(
         d_in["q"], d_in["k"], d_in["v"], d_in["log_alpha"], d_in["beta"],
         cu_seqlens=d_in["cu_seqlens"], num_seqs=d_in["num_seqs"],
-        initial_state=d_in["initial_state"], chunk_size=w.chunk_size)
+        initial_state=d_in["initial_state"], chunk_size=w.chunk_size,
+        **d_in.get("options", {}))
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -198,7 +220,8 @@ def prefill_report(w, res, d, E, C):
     H = w.num_heads
     th = T * H
     s0 = w.initial_state is not None
-    byts = th * prefill_bytes_per_token_head(d, E) + w.num_seqs * H * state_bytes(d) * (
+    raw = isinstance(w, kin.RawPrefill)
+    byts = th * prefill_bytes_per_token_head(d, E, raw) + w.num_seqs * H * state_bytes(d) * (
         2 if s0 else 1)
     flops = th * prefill_flops_per_token_head(d, C)
     t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
@@ -218,7 +241,7 @@ def dominant_roofline(wname, w, res, d, E, C):
     name = max(ku, key=ku.get)
     th = w.total_tokens * w.num_heads
     b = kernel_bytes(name, th, w.num_seqs * w.num_heads, d, E, C,
-                     w.initial_state is not None)
+                     w.initial_state is not None, raw=isinstance(w, kin.RawPrefill))
     ach = b / (ku[name] * 1e-6) / 1e9
     return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=ach / HBM_PEAK_GBS, traffic=measured_traffic(wname, name), kernel=name,
@@ -368,12 +391,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--extra", default="long,varlen,decode",
-                    help="comma list of extra workloads (long, varlen, decode) or 'none'")
+    ap.add_argument("--extra", default="long,varlen,raw,decode",
+                    help="comma list of extra workloads (long, varlen, raw, decode) or 'none'")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["prefill", "long", "varlen", "decode", "copy"],
+    ap.add_argument("--only", choices=["prefill", "long", "varlen", "raw", "decode", "copy"],
                     help="run one workload only (profiling runs); its throughput is `value`. "
                          "'copy' times a plain 1 GiB device copy, the reference for the "
                          "memory-traffic counters")
@@ -433,6 +456,16 @@ def main():
             f"frac {workloads['varlen']['roofline_frac']:.3f}, kernels(us) "
             f"{json.dumps({k: round(v, 2) for k, v in r3['kernel_us'].items()})}")
         del w3
+    if "raw" in extra:
+        log("prefill in raw form (softplus gate, q/k L2 norm, beta logits in the kernel)")
+        w5 = kin.raw_prefill_workload()
+        r5 = time_prefill(torch, kda, w5, args.steps, args.warmup)
+        workloads["prefill_raw"] = prefill_report(w5, r5, d, E, C)
+        workloads["prefill_raw"]["roofline"] = dominant_roofline("prefill_raw", w5, r5, d, E, C)
+        log(f"  {workloads['prefill_raw']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+            f"{workloads['prefill_raw']['ms_per_step'] * 1e3:.1f} us/step, kernels(us) "
+            f"{json.dumps({k: round(v, 2) for k, v in r5['kernel_us'].items()})}")
+        del w5
     torch.cuda.empty_cache()
     if "decode" in extra:
         cfg4 = kin.WORKLOADS[4]
@@ -455,7 +488,7 @@ def main():
         head = workloads["prefill"]
         value, unit, ms = head["tokens_per_s"], "tokens/s", head["ms_per_step"]
     else:  # a single extra workload (profiling runs)
-        name = args.only
+        name = {"raw": "prefill_raw"}.get(args.only, args.only)
         head = workloads[name]
         roof = head["roofline"]
         if name == "decode":

@@ -21,6 +21,25 @@ bool head_dims_supported(int32_t d_k, int32_t d_v, kda_dtype dtype) {
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
 
+// Resolves kda_inputs (NULL = the plain call) into `out`.
+kda_status resolve_inputs(const kda_inputs *in, InputArgs *out) {
+  *out = InputArgs();
+  if (in == nullptr) return KDA_SUCCESS;
+  if (in->gate != KDA_GATE_LOG_ALPHA && in->gate != KDA_GATE_SOFTPLUS &&
+      in->gate != KDA_GATE_SIGMOID)
+    return KDA_ERROR_INVALID_VALUE;
+  if (in->gate == KDA_GATE_SOFTPLUS && (!in->gate_A || !aligned(in->gate_A, 4)))
+    return KDA_ERROR_INVALID_VALUE;
+  if (in->gate == KDA_GATE_SIGMOID && !(in->gate_min < 0.f && in->gate_min > -3.0e38f))
+    return KDA_ERROR_INVALID_VALUE;  // also rejects NaN
+  out->gate = in->gate;
+  out->gate_A = in->gate == KDA_GATE_SOFTPLUS ? in->gate_A : nullptr;
+  out->gate_min = in->gate == KDA_GATE_SIGMOID ? in->gate_min : 0.f;
+  out->l2norm_qk = in->l2norm_qk != 0;
+  out->beta_logits = in->beta_logits != 0;
+  return KDA_SUCCESS;
+}
+
 // Size checks shared by the workspace query and the prefill call.
 kda_status check_fwd_sizes(int64_t total_tokens, int32_t num_seqs, int32_t num_heads,
                            int32_t d_k, int32_t d_v, int32_t chunk_size, kda_dtype dtype) {
@@ -72,19 +91,23 @@ namespace {
 
 // Validates the prefill arguments and runs the stages selected by `mask`
 // (bit s = stage s) in order.
-kda_status fwd_run(unsigned mask, const void *q, const void *k, const void *v,
-                   const float *log_alpha, const float *beta, const int32_t *cu_seqlens,
+kda_status fwd_run(unsigned mask, const kda_inputs *inputs, const void *q, const void *k,
+                   const void *v, const void *gate, const float *beta,
+                   const int32_t *cu_seqlens,
                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
                    int32_t d_v, int32_t chunk_size, kda_dtype dtype,
                    const float *initial_state, float *final_state, void *o,
                    void *workspace, size_t workspace_bytes, void *stream) {
-  const kda_status st =
-      check_fwd_sizes(total_tokens, num_seqs, num_heads, d_k, d_v, chunk_size, dtype);
+  if (mask == 0u || mask > 3u) return KDA_ERROR_INVALID_VALUE;
+  InputArgs in;
+  kda_status st = resolve_inputs(inputs, &in);
+  if (st != KDA_SUCCESS) return st;
+  st = check_fwd_sizes(total_tokens, num_seqs, num_heads, d_k, d_v, chunk_size, dtype);
   if (st != KDA_SUCCESS) return st;
   if (total_tokens > 0) {
-    if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!q || !k || !v || !gate || !beta || !o) return KDA_ERROR_INVALID_VALUE;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(log_alpha, 16) || !aligned(beta, 4))
+        !aligned(gate, 16) || !aligned(beta, 4))
       return KDA_ERROR_INVALID_VALUE;
   }
   if (!cu_seqlens && (total_tokens % num_seqs) != 0) return KDA_ERROR_INVALID_VALUE;
@@ -101,8 +124,9 @@ kda_status fwd_run(unsigned mask, const void *q, const void *k, const void *v,
   a.q = q;
   a.k = k;
   a.v = v;
-  a.g = log_alpha;
+  a.gate = gate;
   a.beta = beta;
+  a.in = in;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
@@ -137,7 +161,7 @@ kda_status kda_fwd_chunked(const void *q, const void *k, const void *v,
                            int32_t d_v, int32_t chunk_size, kda_dtype dtype,
                            const float *initial_state, float *final_state, void *o,
                            void *workspace, size_t workspace_bytes, void *stream) {
-  return fwd_run(3u, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, total_tokens,
+  return fwd_run(3u, nullptr, q, k, v, log_alpha, beta, cu_seqlens, num_seqs, total_tokens,
                  num_heads, d_k, d_v, chunk_size, dtype, initial_state, final_state, o,
                  workspace, workspace_bytes, stream);
 }
@@ -150,24 +174,48 @@ kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void 
                                  const float *initial_state, float *final_state, void *o,
                                  void *workspace, size_t workspace_bytes, void *stream) {
   if (stage != KDA_STAGE_INTRA && stage != KDA_STAGE_INTER) return KDA_ERROR_INVALID_VALUE;
-  return fwd_run(1u << (unsigned)stage, q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
-                 total_tokens, num_heads, d_k, d_v, chunk_size, dtype, initial_state,
-                 final_state, o, workspace, workspace_bytes, stream);
+  return fwd_run(1u << (unsigned)stage, nullptr, q, k, v, log_alpha, beta, cu_seqlens,
+                 num_seqs, total_tokens, num_heads, d_k, d_v, chunk_size, dtype,
+                 initial_state, final_state, o, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_fwd_chunked_ex(const kda_inputs *inputs, uint32_t stages, const void *q,
+                              const void *k, const void *v, const void *gate,
+                              const float *beta, const int32_t *cu_seqlens,
+                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t d_k, int32_t d_v, int32_t chunk_size,
+                              kda_dtype dtype, const float *initial_state,
+                              float *final_state, void *o, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  return fwd_run(stages, inputs, q, k, v, gate, beta, cu_seqlens, num_seqs, total_tokens,
+                 num_heads, d_k, d_v, chunk_size, dtype, initial_state, final_state, o,
+                 workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const float *log_alpha, const float *beta, float *state,
                            void *o, int32_t batch, int32_t num_heads, int32_t d_k,
                            int32_t d_v, kda_dtype dtype, void *stream) {
+  return kda_decode_step_ex(nullptr, q, k, v, log_alpha, beta, state, o, batch, num_heads,
+                            d_k, d_v, dtype, stream);
+}
+
+kda_status kda_decode_step_ex(const kda_inputs *inputs, const void *q, const void *k,
+                              const void *v, const void *gate, const float *beta,
+                              float *state, void *o, int32_t batch, int32_t num_heads,
+                              int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream) {
+  InputArgs in;
+  const kda_status st = resolve_inputs(inputs, &in);
+  if (st != KDA_SUCCESS) return st;
   if (batch < 1 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;
   if (d_k != d_v || !(d_k == 32 || d_k == 64 || d_k == 128)) return KDA_ERROR_NOT_SUPPORTED;
   if ((int64_t)batch * num_heads > ((int64_t)1 << 31) - 1) return KDA_ERROR_NOT_SUPPORTED;
-  if (!q || !k || !v || !log_alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+  if (!q || !k || !v || !gate || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(log_alpha, 16) || !aligned(state, 16) || !aligned(beta, 4))
+      !aligned(gate, 16) || !aligned(state, 16) || !aligned(beta, 4))
     return KDA_ERROR_INVALID_VALUE;
-  if (launch_decode(q, k, v, log_alpha, beta, state, o, batch, num_heads, d_k, dtype,
+  if (launch_decode(q, k, v, gate, beta, in, state, o, batch, num_heads, d_k, dtype,
                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return KDA_ERROR_LAUNCH_FAILED;
   return KDA_SUCCESS;

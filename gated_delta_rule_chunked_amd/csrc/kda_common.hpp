@@ -224,6 +224,56 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Lane index helpers for the tile convention above.
+// ---- input-side fusion (kda_inputs in kda.h), fp32 ------------------------
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// Kimi Linear's gate g = -exp(A) softplus(z), softplus(z) = log(1 + e^z)
+// written as max(z, 0) + log(1 + e^-|z|) so that no exponential overflows.
+__device__ __forceinline__ float gate_softplus(float z, float eA) {
+  return -eA * (fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z))));
+}
+__device__ __forceinline__ f32x4 gate_softplus(f32x4 z, float eA) {
+  return f32x4{gate_softplus(z[0], eA), gate_softplus(z[1], eA), gate_softplus(z[2], eA),
+               gate_softplus(z[3], eA)};
+}
+
+// The bounded gate g = g_min sigmoid(z), in (g_min, 0).
+__device__ __forceinline__ float gate_sigmoid(float z, float gmin) { return gmin * sigmoid(z); }
+__device__ __forceinline__ f32x4 gate_sigmoid(f32x4 z, float gmin) {
+  return f32x4{gmin * sigmoid(z[0]), gmin * sigmoid(z[1]), gmin * sigmoid(z[2]),
+               gmin * sigmoid(z[3])};
+}
+
+// x + (x of the lane that the DPP control selects), within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 8, 16, 32 or 64),
+// every lane of a group receiving the group's sum.  Pairwise exchanges:
+// quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i
+// with 7 - i) and the row mirror (i with 15 - i), each pairing two groups
+// whose sums are already complete; beyond 16 lanes a cross-lane shuffle.
+template <int W>
+__device__ __forceinline__ float group_sum(float s) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  s = dpp_add<0xB1>(s);   // quad_perm [1,0,3,2]
+  s = dpp_add<0x4E>(s);   // quad_perm [2,3,0,1]
+  s = dpp_add<0x141>(s);  // row_half_mirror
+  if constexpr (W >= 16) s = dpp_add<0x140>(s);  // row_mirror
+  if constexpr (W >= 32) s += __shfl_xor(s, 16);
+  if constexpr (W >= 64) s += __shfl_xor(s, 32);
+  return s;
+}
+
+// 1 / sqrt(|x|^2 + 1e-6) for a vector whose d channels sit 4 per lane in W
+// consecutive lanes (W = d / 4, lane groups aligned to W).
+template <int W>
+__device__ __forceinline__ float l2_inv_norm(f32x4 x) {
+  return rsqrtf(group_sum<W>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]) + 1e-6f);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 

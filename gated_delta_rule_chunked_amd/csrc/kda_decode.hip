@@ -21,15 +21,20 @@
 // r = t / (d/4) + i * (threads / (d/4)); at every step i the block reads or
 // writes a contiguous run of rows.  Column sums are reduced over the lanes of
 // a wavefront with cross-lane shuffles and over wavefronts through LDS.
+//
+// Input-side fusion (kda_inputs): with RAW the gate input is z and the gate
+// function gives g per key channel.  With l2norm_qk, q and k enter the step
+// only through S^T (alpha k), S^T (alpha q), k . q and k u^T, so their norms
+// are reduced alongside k . q and applied as scalar factors.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, bool RAW>
 __global__ __launch_bounds__(NT) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta,
+    const void *__restrict__ gate, const float *__restrict__ beta, const InputArgs in,
     float *__restrict__ state, T *__restrict__ o) {
   constexpr int NCQ = D / 4;         // float4 column groups
   constexpr int NRG = NT / NCQ;      // row groups
@@ -39,7 +44,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 
   __shared__ f32x4 s_x[NW][NCQ];
   __shared__ f32x4 s_y[NW][NCQ];
-  __shared__ float s_kq[NW];
+  __shared__ float s_kq[NW], s_kk[NW], s_qq[NW];
 
   const int64_t p = blockIdx.x;
   const int tid = threadIdx.x;
@@ -47,23 +52,32 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   float *S = state + p * D * D;
   const T *qp = q + p * D;
   const T *kp = k + p * D;
-  const float *gp = g + p * D;
+  const float eA = (RAW && in.gate == KDA_GATE_SOFTPLUS) ? __expf(in.gate_A[p % in.heads]) : 0.f;
 
   f32x4 Sv[RPT];
   float a[RPT], kr[RPT];
   f32x4 x = zero4(), y = zero4();
-  float kq = 0.f;
+  float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + i * NRG;
     Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + r * D + 4 * cq));
-    a[i] = __expf(gp[r]);
+    float gr;
+    if constexpr (RAW) {
+      const float z = to_f32(reinterpret_cast<const T *>(gate)[p * D + r]);
+      gr = in.gate == KDA_GATE_SOFTPLUS ? gate_softplus(z, eA) : gate_sigmoid(z, in.gate_min);
+    } else {
+      gr = reinterpret_cast<const float *>(gate)[p * D + r];
+    }
+    a[i] = __expf(gr);
     kr[i] = to_f32(kp[r]);
     const float qr = to_f32(qp[r]);
     const float ka = a[i] * kr[i], qa = a[i] * qr;
     x += Sv[i] * ka;
     y += Sv[i] * qa;
     kq += kr[i] * qr;
+    kk += kr[i] * kr[i];
+    qq += qr * qr;
   }
   // reduce over the row groups of this wavefront (lanes cq + NCQ * m)
 #pragma unroll
@@ -74,6 +88,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(
       y[e] += __shfl_xor(y[e], off);
     }
     kq += __shfl_xor(kq, off);
+    kk += __shfl_xor(kk, off);
+    qq += __shfl_xor(qq, off);
   }
   const int wave = tid >> 6, lane = tid & 63;
   if (lane < NCQ) {
@@ -82,17 +98,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   }
   // kq: each row group summed its own rows and the shuffles added the row
   // groups of this wave, so any lane holds the wave's part.
-  if (lane == 0) s_kq[wave] = kq;
+  if (lane == 0) {
+    s_kq[wave] = kq;
+    s_kk[wave] = kk;
+    s_qq[wave] = qq;
+  }
   __syncthreads();
   f32x4 xs = zero4(), ys = zero4();
-  float kqs = 0.f;
+  float kqs = 0.f, kks = 0.f, qqs = 0.f;
 #pragma unroll
   for (int wv = 0; wv < NW; ++wv) {
     xs += s_x[wv][cq];
     ys += s_y[wv][cq];
     kqs += s_kq[wv];
+    kks += s_kk[wv];
+    qqs += s_qq[wv];
   }
-  const float b = beta[p];
+  float rk = 1.f;  // k <- rk k, q <- rq q
+  if (in.l2norm_qk) {
+    rk = rsqrtf(kks + 1e-6f);
+    const float rq = rsqrtf(qqs + 1e-6f);
+    xs *= rk;
+    ys *= rq;
+    kqs *= rk * rq;
+  }
+  const float b = in.beta_logits ? sigmoid(beta[p]) : beta[p];
   f32x4 vv;
   {
     const T *vp = v + p * D + 4 * cq;
@@ -106,44 +136,49 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + i * NRG;
-    __builtin_nontemporal_store(a[i] * Sv[i] + kr[i] * u, reinterpret_cast<f32x4 *>(S + r * D + 4 * cq));
+    __builtin_nontemporal_store(a[i] * Sv[i] + (rk * kr[i]) * u,
+                                reinterpret_cast<f32x4 *>(S + r * D + 4 * cq));
   }
 }
 
-template <typename T>
-static hipError_t launch_decode_t(const void *q, const void *k, const void *v,
-                                  const float *g, const float *beta, float *state,
-                                  void *o, int pairs, int d, hipStream_t s) {
+template <typename T, int D, int NT>
+static void launch_decode_k(const void *q, const void *k, const void *v, const void *gate,
+                            const float *beta, const InputArgs &in, float *state, void *o,
+                            int pairs, hipStream_t s) {
   const T *qq = reinterpret_cast<const T *>(q);
   const T *kk = reinterpret_cast<const T *>(k);
   const T *vv = reinterpret_cast<const T *>(v);
   T *oo = reinterpret_cast<T *>(o);
+  if (in.gate == KDA_GATE_LOG_ALPHA)
+    hipLaunchKernelGGL((decode_kernel<T, D, NT, false>), dim3(pairs), dim3(NT), 0, s, qq, kk,
+                       vv, gate, beta, in, state, oo);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, NT, true>), dim3(pairs), dim3(NT), 0, s, qq, kk,
+                       vv, gate, beta, in, state, oo);
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const void *q, const void *k, const void *v,
+                                  const void *gate, const float *beta, const InputArgs &in,
+                                  float *state, void *o, int pairs, int d, hipStream_t s) {
   switch (d) {
-    case 32:
-      hipLaunchKernelGGL((decode_kernel<T, 32, 64>), dim3(pairs), dim3(64), 0, s, qq, kk,
-                         vv, g, beta, state, oo);
-      break;
-    case 64:
-      hipLaunchKernelGGL((decode_kernel<T, 64, 256>), dim3(pairs), dim3(256), 0, s, qq,
-                         kk, vv, g, beta, state, oo);
-      break;
-    case 128:
-      hipLaunchKernelGGL((decode_kernel<T, 128, 256>), dim3(pairs), dim3(256), 0, s, qq,
-                         kk, vv, g, beta, state, oo);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: launch_decode_k<T, 32, 64>(q, k, v, gate, beta, in, state, o, pairs, s); break;
+    case 64: launch_decode_k<T, 64, 256>(q, k, v, gate, beta, in, state, o, pairs, s); break;
+    case 128: launch_decode_k<T, 128, 256>(q, k, v, gate, beta, in, state, o, pairs, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, float *state, void *o, int batch, int heads,
-                         int d, kda_dtype dt, hipStream_t stream) {
+hipError_t launch_decode(const void *q, const void *k, const void *v, const void *gate,
+                         const float *beta, const InputArgs &in, float *state, void *o,
+                         int batch, int heads, int d, kda_dtype dt, hipStream_t stream) {
   const int pairs = batch * heads;
+  InputArgs ia = in;
+  ia.heads = heads;
   if (dt == KDA_DTYPE_BF16)
-    return launch_decode_t<bf16>(q, k, v, g, beta, state, o, pairs, d, stream);
-  return launch_decode_t<float>(q, k, v, g, beta, state, o, pairs, d, stream);
+    return launch_decode_t<bf16>(q, k, v, gate, beta, ia, state, o, pairs, d, stream);
+  return launch_decode_t<float>(q, k, v, gate, beta, ia, state, o, pairs, d, stream);
 }
 
 }  // namespace kda

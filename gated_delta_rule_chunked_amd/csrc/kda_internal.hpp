@@ -60,10 +60,24 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
   return L;
 }
 
+// Input-side fusion, resolved on the host (kda_inputs in kda.h): the gate
+// function (0 = g given, 1 = softplus gate, 2 = sigmoid gate), A per head
+// (softplus gate), g_min (sigmoid gate), and the q/k normalisation and
+// beta-logit flags.
+struct InputArgs {
+  int gate = KDA_GATE_LOG_ALPHA;
+  const float *gate_A = nullptr;
+  float gate_min = 0.f;
+  int l2norm_qk = 0, beta_logits = 0;
+  int heads = 0;  // decode: heads per sequence, to find A of state p
+};
+
 // Arguments common to the two prefill launches.
 struct FwdArgs {
   const void *q, *k, *v;
-  const float *g, *beta;
+  const void *gate;        // g (fp32) or the gate input z (operand type)
+  const float *beta;
+  InputArgs in;
   const int *cu_seqlens;  // device, or nullptr for equal lengths
   int num_seqs, num_heads, d, chunk;
   int64_t total_tokens;
@@ -80,8 +94,8 @@ struct FwdArgs {
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
 hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
 hipError_t launch_decode(const void *q, const void *k, const void *v,
-                         const float *g, const float *beta, float *state,
-                         void *o, int batch, int heads, int d, kda_dtype dt,
-                         hipStream_t stream);
+                         const void *gate, const float *beta, const InputArgs &in,
+                         float *state, void *o, int batch, int heads, int d,
+                         kda_dtype dt, hipStream_t stream);
 
 }  // namespace kda

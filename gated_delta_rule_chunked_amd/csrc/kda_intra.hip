@@ -189,10 +189,12 @@ __device__ __forceinline__ void store_elems(T *p, const T *x) {
   }
 }
 
-template <typename T, int D, int C>
+// RAW: the gate input is z in the operand type and in.gate selects the gate
+// function; otherwise it is g itself in fp32.
+template <typename T, int D, int C, bool RAW>
 __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta,
+    const void *__restrict__ gate, const float *__restrict__ beta, const InputArgs in,
     const int *__restrict__ cu, int N, int H, int seq_len, int *__restrict__ seq_first,
     T *__restrict__ qt_out, T *__restrict__ w_out, T *__restrict__ ut_out,
     T *__restrict__ ket_out, T *__restrict__ p_out, float *__restrict__ gam_out) {
@@ -238,23 +240,38 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   // byte offsets (a tile spans at most 64 rows of H * d <= 2^23 elements).
   const int cg = tid % CG, rg = tid / CG;
   const int ch0 = 4 * cg, r0 = rg * RPT;
-  const char *gb = reinterpret_cast<const char *>(g + base);
+  constexpr unsigned GSZ = RAW ? (unsigned)sizeof(T) : 4u;  // bytes per gate element
+  const char *gb = reinterpret_cast<const char *>(gate) + base * GSZ;
   const char *qb = reinterpret_cast<const char *>(q + base);
   const char *kb = reinterpret_cast<const char *>(k + base);
   const char *vb = reinterpret_cast<const char *>(v + base);
   const char *bb = reinterpret_cast<const char *>(beta + ((int64_t)t0 * H + h));
   f32x4 Gv[RPT];
-  typename Vec4<T>::type qr[RPT], kr[RPT], vr[RPT];
+  typename Vec4<T>::type qr[RPT], kr[RPT], vr[RPT], zr[RAW ? RPT : 1];
   float brr[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const unsigned r = (unsigned)min(r0 + j, n - 1);
     const unsigned off = r * (unsigned)rs + (unsigned)ch0;
-    Gv[j] = *reinterpret_cast<const f32x4 *>(gb + off * 4u);
+    if constexpr (RAW)
+      zr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(gb + off * GSZ);
+    else
+      Gv[j] = *reinterpret_cast<const f32x4 *>(gb + off * GSZ);
     qr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(qb + off * (unsigned)sizeof(T));
     kr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(kb + off * (unsigned)sizeof(T));
     vr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(vb + off * (unsigned)sizeof(T));
     brr[j] = *reinterpret_cast<const float *>(bb + r * (unsigned)H * 4u);
+  }
+
+  if constexpr (RAW) {  // the gate function, in fp32
+    if (in.gate == KDA_GATE_SOFTPLUS) {
+      const float eA = __expf(in.gate_A[h]);
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) Gv[j] = gate_softplus(to_f32x4(zr[j]), eA);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) Gv[j] = gate_sigmoid(to_f32x4(zr[j]), in.gate_min);
+    }
   }
 
   // Per channel of this thread's token run: Diag(beta) Kt, Diag(beta) V and
@@ -290,10 +307,14 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       const int r = r0 + j;
       if (r < C) {
         const bool live = !TAIL || r < n;
-        const f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
-        const f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
+        f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
+        f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
         const f32x4 vv = live ? to_f32x4(vr[j]) : zero4();
-        const float br = live ? brr[j] : 0.f;
+        if (in.l2norm_qk) {  // the CG lanes of this row hold its d channels
+          qv *= l2_inv_norm<CG>(qv);
+          kv *= l2_inv_norm<CG>(kv);
+        }
+        const float br = live ? (in.beta_logits ? sigmoid(brr[j]) : brr[j]) : 0.f;
         if (cg == 0) sBeta[r] = br;
         const f32x4 G = Gv[j] + pre;
         f32x4 qt, kt, kh;
@@ -468,10 +489,10 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   }
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool RAW>
 static hipError_t launch_intra_t(const FwdArgs &a) {
   using Cfg = IntraCfg<T, D, C>;
-  auto kern = intra_chunk_kernel<T, D, C>;
+  auto kern = intra_chunk_kernel<T, D, C, RAW>;
   static const hipError_t attr = hipFuncSetAttribute(
       (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
   if (attr != hipSuccess) return attr;
@@ -479,7 +500,7 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
   char *ws = a.ws;
   hipLaunchKernelGGL(kern, grid, dim3(Cfg::NT), Cfg::LDS_BYTES, a.stream,
                      reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
-                     reinterpret_cast<const T *>(a.v), a.g, a.beta, a.cu_seqlens, a.num_seqs,
+                     reinterpret_cast<const T *>(a.v), a.gate, a.beta, a.in, a.cu_seqlens, a.num_seqs,
                      a.num_heads, a.seq_len, reinterpret_cast<int *>(ws + a.lay.seq_first),
                      reinterpret_cast<T *>(ws + a.lay.qt), reinterpret_cast<T *>(ws + a.lay.w),
                      reinterpret_cast<T *>(ws + a.lay.ut), reinterpret_cast<T *>(ws + a.lay.ket),
@@ -487,12 +508,18 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int C>
+static hipError_t launch_intra_c(const FwdArgs &a) {
+  return a.in.gate == KDA_GATE_LOG_ALPHA ? launch_intra_t<T, D, C, false>(a)
+                                         : launch_intra_t<T, D, C, true>(a);
+}
+
 template <typename T, int D>
 static hipError_t launch_intra_d(const FwdArgs &a) {
   switch (a.chunk) {
-    case 16: return launch_intra_t<T, D, 16>(a);
-    case 32: return launch_intra_t<T, D, 32>(a);
-    case 64: return launch_intra_t<T, D, 64>(a);
+    case 16: return launch_intra_c<T, D, 16>(a);
+    case 32: return launch_intra_c<T, D, 32>(a);
+    case 64: return launch_intra_c<T, D, 64>(a);
   }
   return hipErrorInvalidValue;
 }

@@ -218,3 +218,124 @@ def decode_step(step: int, batch: int = 256, H: int = 32, d: int = 128,
     return DecodeStep(q=_round_operand(q, dtype), k=_round_operand(k, dtype),
                       v=_round_operand(v, dtype), g=g.astype(np.float32),
                       beta=beta.astype(np.float32), dtype=dtype)
+
+
+# ---- raw inputs for the input-side fusion (kda_inputs) ----------------------
+# Recipe (numpy PCG64, seed given, fp64 draws in this order):
+#   1. q, k ~ N(0, 1) [T, H, d], not normalised (norms about sqrt(d));
+#   2. v ~ N(0, 1);
+#   3. beta logits ~ N(0, 1) [T, H];
+#   4. gate input z ~ N(z_mu, 1) [T, H, d];
+#   5. softplus gate: A[h] = log(u), u ~ U(0.05, 0.3) [H]; sigmoid gate:
+#      g_min = -5 (Kimi K3's bound).
+# q, k, v and z are rounded to the operand dtype; A and the beta logits are
+# fp32.  With z_mu = 0 (softplus) the decays are -exp(A) softplus(z), about
+# -0.03 .. -0.25 per token, and with z_mu = -3 (sigmoid) about -0.25: chunk
+# sums of 64 tokens stay far above -80.
+
+GATE_Z_MU = {"softplus": 0.0, "sigmoid": -3.0}
+
+
+@dataclasses.dataclass
+class RawPrefill:
+    """A prefill workload in the form the layers before the operator
+    produce it (raw q/k, gate input z, beta logits)."""
+    q: np.ndarray          # [T, H, d] operand dtype, not normalised
+    k: np.ndarray
+    v: np.ndarray
+    z: np.ndarray          # [T, H, d] operand dtype, gate input
+    beta_logits: np.ndarray  # [T, H] float32
+    gate: str              # "softplus" or "sigmoid"
+    gate_A: Optional[np.ndarray]  # [H] float32 (softplus)
+    gate_min: float
+    cu_seqlens: Optional[np.ndarray]
+    num_seqs: int
+    initial_state: Optional[np.ndarray]
+    dtype: str
+    chunk_size: int
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    def options(self) -> dict:
+        """The fusion options, as keyword arguments of the binding's calls
+        and of the oracle's prepare_inputs (gate_A as a host array)."""
+        return dict(gate=self.gate, gate_A=self.gate_A, gate_min=self.gate_min,
+                    l2norm_qk=True, beta_logits=True)
+
+    def f64(self):
+        """(q, k, v, z, beta_logits, initial_state), exact float64."""
+        s0 = None if self.initial_state is None else self.initial_state.astype(np.float64)
+        return (as_f64(self.q, self.dtype), as_f64(self.k, self.dtype),
+                as_f64(self.v, self.dtype), as_f64(self.z, self.dtype),
+                self.beta_logits.astype(np.float64), s0)
+
+
+def make_prefill_raw(seed, *, H: int, d: int, dtype: str, chunk_size: int, gate: str,
+                     B: int = 1, T: int = 0, lengths=None,
+                     s0_std: Optional[float] = None) -> RawPrefill:
+    """Draw one raw-input prefill workload (recipe above)."""
+    rng = np.random.default_rng(seed)
+    if lengths is not None:
+        lengths = [int(x) for x in lengths]
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        n, total = len(lengths), int(cu[-1])
+    else:
+        cu, n, total = None, B, B * T
+    q = rng.standard_normal((total, H, d))
+    k = rng.standard_normal((total, H, d))
+    v = rng.standard_normal((total, H, d))
+    bl = rng.standard_normal((total, H))
+    z = rng.normal(GATE_Z_MU[gate], 1.0, size=(total, H, d))
+    A = None
+    if gate == "softplus":
+        A = np.log(rng.uniform(0.05, 0.3, size=H)).astype(np.float32)
+    s0 = None
+    if s0_std is not None:
+        s0 = rng.normal(0.0, s0_std, size=(n, H, d, d)).astype(np.float32)
+    return RawPrefill(q=_round_operand(q, dtype), k=_round_operand(k, dtype),
+                      v=_round_operand(v, dtype), z=_round_operand(z, dtype),
+                      beta_logits=bl.astype(np.float32), gate=gate, gate_A=A,
+                      gate_min=-5.0, cu_seqlens=cu, num_seqs=n, initial_state=s0,
+                      dtype=dtype, chunk_size=chunk_size)
+
+
+# Raw-input form of the headline prefill (Kimi Linear's softplus gate), the
+# input-side fusion benchmark workload; seed 5.
+RAW_PREFILL = dict(name="prefill_raw", B=2, H=8, T=2048, d=128, chunk_size=64,
+                   dtype=BF16, gate="softplus")
+
+
+def raw_prefill_workload() -> RawPrefill:
+    w = dict(RAW_PREFILL)
+    w.pop("name")
+    return make_prefill_raw(5, **w)
+
+
+def decode_step_raw(step: int, batch: int, H: int, d: int, dtype: str, gate: str,
+                    seed_base: int = 6) -> RawPrefill:
+    """Raw inputs of decode step `step` ([batch, H, d], one token per
+    state): q, k, v, beta logits and z from default_rng([seed_base, step]) in
+    the order of the recipe above; the per-head A (a parameter, the same at
+    every step) from default_rng(seed_base)."""
+    rng = np.random.default_rng([seed_base, step])
+    q = rng.standard_normal((batch, H, d))
+    k = rng.standard_normal((batch, H, d))
+    v = rng.standard_normal((batch, H, d))
+    bl = rng.standard_normal((batch, H))
+    z = rng.normal(GATE_Z_MU[gate], 1.0, size=(batch, H, d))
+    A = None
+    if gate == "softplus":
+        A = np.log(np.random.default_rng(seed_base).uniform(0.05, 0.3, size=H))
+        A = A.astype(np.float32)
+    return RawPrefill(q=_round_operand(q, dtype), k=_round_operand(k, dtype),
+                      v=_round_operand(v, dtype), z=_round_operand(z, dtype),
+                      beta_logits=bl.astype(np.float32), gate=gate, gate_A=A,
+                      gate_min=-5.0, cu_seqlens=None, num_seqs=batch, initial_state=None,
+                      dtype=dtype, chunk_size=0)

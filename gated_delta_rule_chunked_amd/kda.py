@@ -21,6 +21,15 @@ KDA_DTYPE_BF16 = 1
 
 _lib = None
 
+GATES = {"log_alpha": 0, "softplus": 1, "sigmoid": 2}
+
+
+class KdaInputs(ctypes.Structure):
+    """kda_inputs (include/kda.h): input-side fusion options."""
+    _fields_ = [("gate", ctypes.c_int), ("gate_A", ctypes.c_void_p),
+                ("gate_min", ctypes.c_float), ("l2norm_qk", ctypes.c_int32),
+                ("beta_logits", ctypes.c_int32)]
+
 
 class KdaError(RuntimeError):
     """A KDA call returned a non-success status, or the library is missing."""
@@ -50,6 +59,11 @@ def library():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
+    pin = ctypes.POINTER(KdaInputs)
+    lib.kda_fwd_chunked_ex.restype = ctypes.c_int
+    lib.kda_fwd_chunked_ex.argtypes = [pin, ctypes.c_uint32] + lib.kda_fwd_chunked.argtypes
+    lib.kda_decode_step_ex.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [pin] + lib.kda_decode_step.argtypes
     _lib = lib
     return lib
 
@@ -98,15 +112,40 @@ def workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: i
 STAGES = {"intra": 0, "inter": 1}
 
 
+def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, dev):
+    """kda_inputs for the options, or None for the plain call, and the
+    tensors it points to."""
+    if gate not in GATES:
+        raise KdaError(f"unknown gate {gate!r}; one of {sorted(GATES)}")
+    if gate == "log_alpha" and not l2norm_qk and not beta_logits:
+        return None, ()
+    keep = ()
+    a_ptr = None
+    if gate == "softplus":
+        if gate_A is None:
+            raise KdaError("gate='softplus' needs gate_A, fp32 [H]")
+        _need(gate_A, "gate_A", torch.float32, (H,))
+        a_ptr, keep = gate_A.data_ptr(), (gate_A,)
+    return ctypes.pointer(KdaInputs(GATES[gate], a_ptr, float(gate_min), int(bool(l2norm_qk)),
+                                    int(bool(beta_logits)))), keep
+
+
+def _need_gate(g, gate, dtype, shape):
+    _need(g, "gate" if gate != "log_alpha" else "log_alpha",
+          torch.float32 if gate == "log_alpha" else dtype, shape)
+
+
 def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chunk_size,
-              output_final_state, out, final_state, workspace, allow_alloc_ws=True):
+              output_final_state, out, final_state, workspace, allow_alloc_ws=True,
+              gate="log_alpha"):
     """Checks the tensors of a prefill call, allocates missing outputs and
-    returns (ctypes argument tuple, o, final_state, workspace)."""
+    returns (ctypes argument tuple, o, final_state, workspace).  With a gate
+    other than "log_alpha", `log_alpha` is the gate input z (q's dtype)."""
     T, H, d = q.shape
     dt = _dtype_code(q.dtype)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype, (T, H, d))
-    _need(log_alpha, "log_alpha", torch.float32, (T, H, d))
+    _need_gate(log_alpha, gate, q.dtype, (T, H, d))
     _need(beta, "beta", torch.float32, (T, H))
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -147,8 +186,12 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 final_state: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None,
                 stage: Optional[str] = None,
+                gate: str = "log_alpha", gate_A: Optional[torch.Tensor] = None,
+                gate_min: float = -5.0, l2norm_qk: bool = False,
+                beta_logits: bool = False,
                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked KDA prefill (kda_fwd_chunked).
+    """Chunked KDA prefill (kda_fwd_chunked, or kda_fwd_chunked_ex with
+    input-side fusion).
 
     q, k: [T, H, d] and v: [T, H, d] (bf16 or fp32, same dtype);
     log_alpha: [T, H, d] fp32; beta: [T, H] fp32;
@@ -159,13 +202,23 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     update states in place.  `stage` ("intra" or "inter") runs only
     that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
     and `final_state` of a preceding call with the same arguments.
+
+    Input-side fusion (kda_inputs): gate="softplus" (g = -exp(gate_A[h])
+    softplus(z)) or "sigmoid" (g = gate_min sigmoid(z)) makes `log_alpha`
+    the gate input z, in q's dtype; l2norm_qk normalises q and k per token
+    and head; beta_logits passes beta through a sigmoid.
     """
     if stage is not None and stage not in STAGES:
         raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
     args, o, fs, _ = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
                                initial_state, chunk_size, output_final_state, out,
-                               final_state, workspace, allow_alloc_ws=stage is None)
-    if stage is None:
+                               final_state, workspace, allow_alloc_ws=stage is None,
+                               gate=gate)
+    opt, _keep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1], q.device)
+    if opt is not None:
+        mask = 3 if stage is None else 1 << STAGES[stage]
+        _check(library().kda_fwd_chunked_ex(opt, mask, *args), "kda_fwd_chunked_ex")
+    elif stage is None:
         _check(library().kda_fwd_chunked(*args), "kda_fwd_chunked")
     else:
         _check(library().kda_fwd_chunked_stage(STAGES[stage], *args),
@@ -193,60 +246,70 @@ class BoundCall:
 
 def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
              initial_state=None, chunk_size=64, output_final_state=True,
-             out=None, final_state=None, workspace=None):
+             out=None, final_state=None, workspace=None, gate="log_alpha", gate_A=None,
+             gate_min=-5.0, l2norm_qk=False, beta_logits=False):
     """Validate and marshal a kda_fwd_chunked call once, for repeated calls.
 
     Nothing is launched here.  Returns (call, stage_calls, o, final_state):
     `call()` runs the whole prefill and `stage_calls[name]()` one of its
     kernels ("intra", "inter"; kda_fwd_chunked_stage) on the same workspace.
+    The input-side fusion options are those of fwd_chunked.
     """
     args, o, fs, ws = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
                                 initial_state, chunk_size, output_final_state, out,
-                                final_state, workspace)
-    keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws)
+                                final_state, workspace, gate=gate)
+    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1], q.device)
+    keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws, opt) + akeep
     lib = library()
-    call = BoundCall(lib.kda_fwd_chunked, args, "kda_fwd_chunked", keep)
-    stages = {name: BoundCall(lib.kda_fwd_chunked_stage, (sid,) + args,
-                              f"kda_fwd_chunked_stage({name})", keep)
-              for name, sid in STAGES.items()}
+    if opt is None:
+        call = BoundCall(lib.kda_fwd_chunked, args, "kda_fwd_chunked", keep)
+        stages = {name: BoundCall(lib.kda_fwd_chunked_stage, (sid,) + args,
+                                  f"kda_fwd_chunked_stage({name})", keep)
+                  for name, sid in STAGES.items()}
+    else:
+        call = BoundCall(lib.kda_fwd_chunked_ex, (opt, 3) + args, "kda_fwd_chunked_ex", keep)
+        stages = {name: BoundCall(lib.kda_fwd_chunked_ex, (opt, 1 << sid) + args,
+                                  f"kda_fwd_chunked_ex({name})", keep)
+                  for name, sid in STAGES.items()}
     return call, stages, o, fs
 
 
-def bind_decode(q, k, v, log_alpha, beta, state, out=None):
+def bind_decode(q, k, v, log_alpha, beta, state, out=None, gate="log_alpha", gate_A=None,
+                gate_min=-5.0, l2norm_qk=False, beta_logits=False):
     """Validate and marshal a kda_decode_step call once.  Returns (call, o);
-    each `call()` advances `state` by one step in place."""
+    each `call()` advances `state` by one step in place.  The input-side
+    fusion options are those of decode_step."""
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype, (B, H, d))
-    _need(log_alpha, "log_alpha", torch.float32, (B, H, d))
+    _need_gate(log_alpha, gate, q.dtype, (B, H, d))
     _need(beta, "beta", torch.float32, (B, H))
     _need(state, "state", torch.float32, (B, H, d, d))
     o = out if out is not None else torch.empty((B, H, d), dtype=v.dtype, device=q.device)
     _need(o, "out", v.dtype, (B, H, d))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
             B, H, d, d, _dtype_code(q.dtype), _stream(q.device))
-    return BoundCall(library().kda_decode_step, args, "kda_decode_step",
-                     (q, k, v, log_alpha, beta, state, o)), o
+    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, q.device)
+    keep = (q, k, v, log_alpha, beta, state, o, opt) + akeep
+    if opt is None:
+        return BoundCall(library().kda_decode_step, args, "kda_decode_step", keep), o
+    return BoundCall(library().kda_decode_step_ex, (opt,) + args, "kda_decode_step_ex",
+                     keep), o
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 log_alpha: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One recurrent KDA step (kda_decode_step); `state` is updated in place.
+                out: Optional[torch.Tensor] = None, gate: str = "log_alpha",
+                gate_A: Optional[torch.Tensor] = None, gate_min: float = -5.0,
+                l2norm_qk: bool = False, beta_logits: bool = False) -> torch.Tensor:
+    """One recurrent KDA step (kda_decode_step, or kda_decode_step_ex with
+    input-side fusion); `state` is updated in place.
 
-    q, k, v: [B, H, d] (bf16 or fp32); log_alpha: [B, H, d] fp32;
-    beta: [B, H] fp32; state: [B, H, d, d] fp32.  Returns o [B, H, d].
+    q, k, v: [B, H, d] (bf16 or fp32); log_alpha: [B, H, d] fp32 (or the gate
+    input z in q's dtype, see fwd_chunked); beta: [B, H] fp32;
+    state: [B, H, d, d] fp32.  Returns o [B, H, d].
     """
-    B, H, d = q.shape
-    dt = _dtype_code(q.dtype)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _need(t, name, q.dtype, (B, H, d))
-    _need(log_alpha, "log_alpha", torch.float32, (B, H, d))
-    _need(beta, "beta", torch.float32, (B, H))
-    _need(state, "state", torch.float32, (B, H, d, d))
-    o = out if out is not None else torch.empty((B, H, d), dtype=v.dtype, device=q.device)
-    _need(o, "out", v.dtype, (B, H, d))
-    _check(library().kda_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o), B, H,
-        d, d, dt, _stream(q.device)), "kda_decode_step")
+    call, o = bind_decode(q, k, v, log_alpha, beta, state, out=out, gate=gate, gate_A=gate_A,
+                          gate_min=gate_min, l2norm_qk=l2norm_qk, beta_logits=beta_logits)
+    call()
     return o

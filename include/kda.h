@@ -158,6 +158,61 @@ kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void 
                                  void *stream);
 
 /*
+ * ---- Input-side fusion ----------------------------------------------------
+ * Steps that the layers feeding the operator would otherwise run as separate
+ * passes over q, k, the gate and beta, done by the kernels as they read them
+ * (docsaid.org "Kimi Linear", section "Les autres pieces": q and k are
+ * L2-normalised, beta is a sigmoid, the decay comes from a gate function;
+ * fr.news.hada.io, section "Configuration du modele Kimi Linear";
+ * mkdocs.reaper.mx "Attention lineaire et recurrence", section "Le piege
+ * numerique de la decroissance cumulee": Kimi Linear's
+ * g = -exp(A) softplus(z), and the scaled sigmoid bounded below by g_min).
+ * All of it is evaluated in fp32 from the stored inputs.
+ */
+typedef enum {
+  KDA_GATE_LOG_ALPHA = 0, /* gate holds g = log(alpha) itself, fp32           */
+  KDA_GATE_SOFTPLUS = 1,  /* gate holds z in dtype: g = -exp(A[h]) softplus(z),
+                             softplus(z) = log(1 + exp(z))                     */
+  KDA_GATE_SIGMOID = 2    /* gate holds z in dtype: g = gate_min sigmoid(z),
+                             so g lies in (gate_min, 0)                        */
+} kda_gate;
+
+typedef struct {
+  kda_gate gate;
+  const float *gate_A;  /* KDA_GATE_SOFTPLUS: [num_heads] fp32 device array  */
+  float gate_min;       /* KDA_GATE_SIGMOID: finite and < 0 (-5 in Kimi K3)  */
+  int32_t l2norm_qk;    /* nonzero: q <- q / sqrt(|q|^2 + 1e-6) per token and
+                           head, and the same for k, before any other use   */
+  int32_t beta_logits;  /* nonzero: beta holds logits b; beta = sigmoid(b)   */
+} kda_inputs;
+
+/*
+ * kda_fwd_chunked with input-side fusion and a stage mask.
+ *
+ *   inputs   how to read gate and beta, and whether to normalise q and k;
+ *            NULL means {KDA_GATE_LOG_ALPHA, NULL, 0, 0, 0}, i.e. exactly
+ *            kda_fwd_chunked.
+ *   stages   bit 0 runs the intra-chunk kernel, bit 1 the inter-chunk
+ *            kernel (3 = the whole call; see kda_fwd_chunked_stage for the
+ *            ordering rules of single stages).  Other values are invalid.
+ *   gate     [total_tokens, H, d_k]: fp32 g for KDA_GATE_LOG_ALPHA, else z
+ *            in dtype (half the bytes of g for bf16).  16-byte aligned.
+ *   beta     [total_tokens, H] fp32: beta, or its logits.
+ * Every other argument is as for kda_fwd_chunked, and so is the decay
+ * precondition, which now applies to the g the gate function produces.
+ * KDA_GATE_SIGMOID with gate_min >= -5 meets it for any z when
+ * chunk_size = 16 (16 x 5 = 80, the tile bound of the section cited above).
+ */
+kda_status kda_fwd_chunked_ex(const kda_inputs *inputs, uint32_t stages, const void *q,
+                              const void *k, const void *v, const void *gate,
+                              const float *beta, const int32_t *cu_seqlens,
+                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t d_k, int32_t d_v, int32_t chunk_size,
+                              kda_dtype dtype, const float *initial_state,
+                              float *final_state, void *o, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for a batch of states, updated in place.
  * For each (b, h): S' = Diag(alpha) S; u = beta (v - S'^T k);
  * o = S'^T q + (k . q) u; S <- S' + k u^T -- the same update and read-out as
@@ -180,6 +235,15 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            float *state, void *o, int32_t batch,
                            int32_t num_heads, int32_t d_k, int32_t d_v,
                            kda_dtype dtype, void *stream);
+
+/*
+ * kda_decode_step with input-side fusion: `inputs` and `gate` as for
+ * kda_fwd_chunked_ex (gate [batch, H, d_k]; NULL inputs = kda_decode_step).
+ */
+kda_status kda_decode_step_ex(const kda_inputs *inputs, const void *q, const void *k,
+                              const void *v, const void *gate, const float *beta,
+                              float *state, void *o, int32_t batch, int32_t num_heads,
+                              int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -158,3 +158,62 @@ def ut_inverse(A):
     _check(lib.kda_oracle_ut_inverse(ap, n, out.ctypes.data_as(_dp)),
            "kda_oracle_ut_inverse")
     return out
+
+
+# ---- input-side transforms (numpy, fp64) ------------------------------------
+# The steps that produce the operator's inputs from the layers before it
+# (docsaid.org "Kimi Linear", section "Les autres pieces"; fr.news.hada.io,
+# section "Configuration du modele Kimi Linear"; mkdocs.reaper.mx "Attention
+# lineaire et recurrence", section "Le piege numerique de la decroissance
+# cumulee"), written from their definitions.  A fused call of the library is
+# checked against `recurrent` / `decode` applied to what these return.
+
+def softplus(z):
+    """log(1 + e^z), computed as max(z, 0) + log1p(e^-|z|)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def gate_softplus(z, A):
+    """Kimi Linear's decay gate: g = -exp(A) softplus(z), one A per head.
+    z: [..., H, d_k]; A: [H]."""
+    A = np.asarray(A, dtype=np.float64)
+    return -np.exp(A)[:, None] * softplus(z)
+
+
+def gate_sigmoid(z, g_min):
+    """The bounded gate g = g_min sigmoid(z), which lies in (g_min, 0)."""
+    return float(g_min) * sigmoid(z)
+
+
+def l2_normalize(x, eps=1e-6):
+    """x / sqrt(|x|^2 + eps) over the last axis (per token and head)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def prepare_inputs(q, k, gate_in, beta_in, gate="log_alpha", gate_A=None, gate_min=-5.0,
+                   l2norm_qk=False, beta_logits=False):
+    """(q, k, g, beta) as the recurrence takes them, from the inputs of a
+    fused call: gate "log_alpha" (gate_in is g), "softplus" or "sigmoid"
+    (gate_in is z); q and k L2-normalised if asked; beta from logits if
+    asked."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if gate == "log_alpha":
+        g = np.asarray(gate_in, dtype=np.float64)
+    elif gate == "softplus":
+        g = gate_softplus(gate_in, gate_A)
+    elif gate == "sigmoid":
+        g = gate_sigmoid(gate_in, gate_min)
+    else:
+        raise ValueError(f"unknown gate {gate!r}")
+    if l2norm_qk:
+        q, k = l2_normalize(q), l2_normalize(k)
+    b = sigmoid(beta_in) if beta_logits else np.asarray(beta_in, dtype=np.float64)
+    return q, k, g, b

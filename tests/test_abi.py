@@ -134,3 +134,51 @@ def test_binding_fails_loudly_without_device():
         kda.fwd_chunked(x, x, x, x, torch.zeros((4, 1)))
     with pytest.raises(kda.KdaError):
         kda.decode_step(x, x, x, x, torch.zeros((4, 1)), torch.zeros((4, 1, 32, 32)))
+
+
+def _opts(gate=0, A=None, gmin=0.0, norm=0, blog=0):
+    from gated_delta_rule_chunked_amd import kda
+    return ctypes.pointer(kda.KdaInputs(gate, A, gmin, norm, blog))
+
+
+def _fwd_ex(lib, opt, stages=3, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=None, n=2, T=256, H=2, dk=128,
+             dv=128, C=64, dt=1, s0=None, sf=None, o=FAKE, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(over)
+    return lib.kda_fwd_chunked_ex(opt, stages, a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                  a["cu"], a["n"], a["T"], a["H"], a["dk"], a["dv"], a["C"],
+                                  a["dt"], a["s0"], a["sf"], a["o"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+def test_fwd_ex_rejects_bad_options_on_host(lib):
+    """Input-side fusion options are validated before anything is enqueued
+    (every case below fails validation; none launches)."""
+    assert _fwd_ex(lib, None, stages=0) == 1
+    assert _fwd_ex(lib, None, stages=4) == 1
+    assert _fwd_ex(lib, _opts(gate=7)) == 1
+    assert _fwd_ex(lib, _opts(gate=1, A=None)) == 1              # softplus needs A
+    assert _fwd_ex(lib, _opts(gate=2, gmin=0.0)) == 1            # g_min must be < 0
+    assert _fwd_ex(lib, _opts(gate=2, gmin=float("nan"))) == 1
+    assert _fwd_ex(lib, _opts(gate=2, gmin=float("-inf"))) == 1
+    assert _fwd_ex(lib, _opts(gate=1, A=(1 << 20) + 2)) == 1     # misaligned A
+    # valid options still meet the size and workspace checks
+    assert _fwd_ex(lib, _opts(gate=2, gmin=-5.0, norm=1, blog=1), wsb=16) == 1
+    assert _fwd_ex(lib, _opts(gate=1, A=1 << 20), dk=96, dv=96) == 2
+    assert _fwd_ex(lib, _opts(gate=2, gmin=-5.0), g=ctypes.c_void_p((1 << 20) + 8)) == 1
+
+
+def test_decode_ex_rejects_bad_options_on_host(lib):
+    def dec_ex(opt, **over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, st=FAKE, o=FAKE, B=4, H=2,
+                 dk=128, dv=128, dt=1, stream=None)
+        a.update(over)
+        return lib.kda_decode_step_ex(opt, a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                      a["st"], a["o"], a["B"], a["H"], a["dk"], a["dv"],
+                                      a["dt"], a["stream"])
+    assert dec_ex(_opts(gate=3)) == 1
+    assert dec_ex(_opts(gate=1)) == 1
+    assert dec_ex(_opts(gate=2, gmin=1.0)) == 1
+    assert dec_ex(_opts(gate=2, gmin=-5.0), st=None) == 1
+    assert dec_ex(_opts(gate=1, A=1 << 20), dk=48, dv=48) == 2
