@@ -37,6 +37,11 @@ kda_status resolve_inputs(const kda_inputs *in, InputArgs *out) {
   out->gate_min = in->gate == KDA_GATE_SIGMOID ? in->gate_min : 0.f;
   out->l2norm_qk = in->l2norm_qk != 0;
   out->beta_logits = in->beta_logits != 0;
+  if (in->state_slots) {
+    if (!aligned(in->state_slots, 4) || in->num_slots < 1) return KDA_ERROR_INVALID_VALUE;
+    out->slots = in->state_slots;
+    out->num_slots = in->num_slots;
+  }
   return KDA_SUCCESS;
 }
 

@@ -49,7 +49,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   const int64_t p = blockIdx.x;
   const int tid = threadIdx.x;
   const int cq = tid % NCQ, rg = tid / NCQ;
-  float *S = state + p * D * D;
+  int64_t sp = p;  // state of (sequence, head) p: row p, or its slot of the pool
+  if (in.slots) {
+    const int64_t b = p / in.heads;
+    const int sl = in.slots[b];
+    if (sl < 0 || sl >= in.num_slots) {  // padding: o = 0, no state touched
+      if (rg == 0) store4_f32<T>(o + p * D + 4 * cq, zero4());
+      return;
+    }
+    sp = (int64_t)sl * in.heads + (p - b * in.heads);
+  }
+  float *S = state + sp * D * D;
   const T *qp = q + p * D;
   const T *kp = k + p * D;
   const float eA = (RAW && in.gate == KDA_GATE_SOFTPLUS) ? __expf(in.gate_A[p % in.heads]) : 0.f;

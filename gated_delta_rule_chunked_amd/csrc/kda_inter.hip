@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const float *__restrict__ gam, const int *__restrict__ cu,
     const int *__restrict__ seq_first, int N, int H, int seq_len,
     const float *__restrict__ s0, float *__restrict__ s_final,
-    T *__restrict__ o) {
+    const int *__restrict__ slots, int num_slots, T *__restrict__ o) {
   using Ops = InterOps<T, D, C>;
   using F = typename Ops::F;
   using V4 = typename Ops::V4;
@@ -108,16 +108,24 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   }
   const int nch = (len + C - 1) / C;
   const int64_t rs = (int64_t)H * D;
+  // state of this (sequence, head): row `pair`, or its slot of the pools
+  int64_t spair = pair;
+  bool has_state = true;
+  if (slots) {
+    const int sl = slots[seq];
+    has_state = sl >= 0 && sl < num_slots;  // padding: zero start, no final write
+    spair = has_state ? (int64_t)sl * H + h : 0;
+  }
 
   // the wave's state rows: S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
   f32x4 S[CBW];
-  const int64_t sbase = (int64_t)pair * D * D + col0 + lr;
+  const int64_t sbase = spair * D * D + col0 + lr;
 #pragma unroll
   for (int j = 0; j < CBW; ++j) {
     const int cb = wv * CBW + j;
     f32x4 x = zero4();
     if (cb < NCB) {
-      if (s0) {
+      if (s0 && has_state) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = s0[sbase + (int64_t)(16 * cb + 4 * lg + i) * D];
       }
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     if (ci + 2 < nch) step(B2, ci + 2);
   }
 
-  if (s_final) {
+  if (s_final && has_state) {
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
@@ -277,7 +285,8 @@ static hipError_t launch_inter_c(const FwdArgs &a) {
                      reinterpret_cast<const T *>(ws + a.lay.p),
                      reinterpret_cast<const float *>(ws + a.lay.gam), a.cu_seqlens,
                      reinterpret_cast<const int *>(ws + a.lay.seq_first), a.num_seqs,
-                     a.num_heads, a.seq_len, a.s0, a.s_final, reinterpret_cast<T *>(a.o));
+                     a.num_heads, a.seq_len, a.s0, a.s_final, a.in.slots, a.in.num_slots,
+                     reinterpret_cast<T *>(a.o));
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ struct InputArgs {
   const float *gate_A = nullptr;
   float gate_min = 0.f;
   int l2norm_qk = 0, beta_logits = 0;
+  const int *slots = nullptr;  // state slot per sequence, or nullptr
+  int num_slots = 0;
   int heads = 0;  // decode: heads per sequence, to find A of state p
 };
 

@@ -28,7 +28,8 @@ class KdaInputs(ctypes.Structure):
     """kda_inputs (include/kda.h): input-side fusion options."""
     _fields_ = [("gate", ctypes.c_int), ("gate_A", ctypes.c_void_p),
                 ("gate_min", ctypes.c_float), ("l2norm_qk", ctypes.c_int32),
-                ("beta_logits", ctypes.c_int32)]
+                ("beta_logits", ctypes.c_int32), ("state_slots", ctypes.c_void_p),
+                ("num_slots", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -112,12 +113,13 @@ def workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: i
 STAGES = {"intra": 0, "inter": 1}
 
 
-def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, dev):
+def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
+            num_slots=0, n=None):
     """kda_inputs for the options, or None for the plain call, and the
     tensors it points to."""
     if gate not in GATES:
         raise KdaError(f"unknown gate {gate!r}; one of {sorted(GATES)}")
-    if gate == "log_alpha" and not l2norm_qk and not beta_logits:
+    if gate == "log_alpha" and not l2norm_qk and not beta_logits and state_slots is None:
         return None, ()
     keep = ()
     a_ptr = None
@@ -126,8 +128,12 @@ def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, dev):
             raise KdaError("gate='softplus' needs gate_A, fp32 [H]")
         _need(gate_A, "gate_A", torch.float32, (H,))
         a_ptr, keep = gate_A.data_ptr(), (gate_A,)
+    s_ptr = None
+    if state_slots is not None:
+        _need(state_slots, "state_slots", torch.int32, (n,))
+        s_ptr, keep = state_slots.data_ptr(), keep + (state_slots,)
     return ctypes.pointer(KdaInputs(GATES[gate], a_ptr, float(gate_min), int(bool(l2norm_qk)),
-                                    int(bool(beta_logits)))), keep
+                                    int(bool(beta_logits)), s_ptr, int(num_slots))), keep
 
 
 def _need_gate(g, gate, dtype, shape):
@@ -137,10 +143,12 @@ def _need_gate(g, gate, dtype, shape):
 
 def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chunk_size,
               output_final_state, out, final_state, workspace, allow_alloc_ws=True,
-              gate="log_alpha"):
+              gate="log_alpha", state_slots=None):
     """Checks the tensors of a prefill call, allocates missing outputs and
-    returns (ctypes argument tuple, o, final_state, workspace).  With a gate
-    other than "log_alpha", `log_alpha` is the gate input z (q's dtype)."""
+    returns (ctypes argument tuple, o, final_state, workspace, num_slots).
+    With a gate other than "log_alpha", `log_alpha` is the gate input z
+    (q's dtype).  With state_slots the states are pools [num_slots, H, d, d]
+    and the final states go to `final_state`, by default `initial_state`."""
     T, H, d = q.shape
     dt = _dtype_code(q.dtype)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -152,16 +160,25 @@ def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chu
         n = cu_seqlens.numel() - 1
     else:
         n = 1 if num_seqs is None else int(num_seqs)
-    if initial_state is not None:
-        _need(initial_state, "initial_state", torch.float32, (n, H, d, d))
     dev = q.device
+    num_slots = 0
+    if state_slots is not None:
+        pool = initial_state if initial_state is not None else final_state
+        if pool is None:
+            raise KdaError("state_slots needs an initial_state or final_state pool")
+        num_slots = pool.shape[0]
+        if output_final_state and final_state is None:
+            final_state = initial_state
+    ns = n if state_slots is None else num_slots
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (ns, H, d, d))
     o = out if out is not None else torch.empty((T, H, d), dtype=v.dtype, device=dev)
     _need(o, "out", v.dtype, (T, H, d))
     fs = None
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty(
             (n, H, d, d), dtype=torch.float32, device=dev)
-        _need(fs, "final_state", torch.float32, (n, H, d, d))
+        _need(fs, "final_state", torch.float32, (ns, H, d, d))
     need = workspace_size(T, n, H, d, chunk_size, q.dtype)
     if need == 0:
         raise KdaError(f"unsupported sizes T={T} N={n} H={H} d={d} chunk={chunk_size} "
@@ -173,7 +190,7 @@ def _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs, initial_state, chu
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), n,
             T, H, d, d, chunk_size, dt, _ptr(initial_state), _ptr(fs), _ptr(o),
             _ptr(workspace), workspace.numel(), _stream(dev))
-    return args, o, fs, workspace
+    return args, o, fs, workspace, num_slots
 
 
 def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -188,7 +205,7 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 stage: Optional[str] = None,
                 gate: str = "log_alpha", gate_A: Optional[torch.Tensor] = None,
                 gate_min: float = -5.0, l2norm_qk: bool = False,
-                beta_logits: bool = False,
+                beta_logits: bool = False, state_slots: Optional[torch.Tensor] = None,
                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill (kda_fwd_chunked, or kda_fwd_chunked_ex with
     input-side fusion).
@@ -206,15 +223,18 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     Input-side fusion (kda_inputs): gate="softplus" (g = -exp(gate_A[h])
     softplus(z)) or "sigmoid" (g = gate_min sigmoid(z)) makes `log_alpha`
     the gate input z, in q's dtype; l2norm_qk normalises q and k per token
-    and head; beta_logits passes beta through a sigmoid.
+    and head; beta_logits passes beta through a sigmoid.  state_slots (int32
+    [N] device tensor) makes initial_state / final_state pools of states
+    indexed by slot (final_state defaults to initial_state then).
     """
     if stage is not None and stage not in STAGES:
         raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
-    args, o, fs, _ = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
-                               initial_state, chunk_size, output_final_state, out,
-                               final_state, workspace, allow_alloc_ws=stage is None,
-                               gate=gate)
-    opt, _keep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1], q.device)
+    args, o, fs, _, nsl = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
+                                    initial_state, chunk_size, output_final_state, out,
+                                    final_state, workspace, allow_alloc_ws=stage is None,
+                                    gate=gate, state_slots=state_slots)
+    opt, _keep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
+                         state_slots, nsl, args[6])
     if opt is not None:
         mask = 3 if stage is None else 1 << STAGES[stage]
         _check(library().kda_fwd_chunked_ex(opt, mask, *args), "kda_fwd_chunked_ex")
@@ -247,7 +267,7 @@ class BoundCall:
 def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
              initial_state=None, chunk_size=64, output_final_state=True,
              out=None, final_state=None, workspace=None, gate="log_alpha", gate_A=None,
-             gate_min=-5.0, l2norm_qk=False, beta_logits=False):
+             gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None):
     """Validate and marshal a kda_fwd_chunked call once, for repeated calls.
 
     Nothing is launched here.  Returns (call, stage_calls, o, final_state):
@@ -255,10 +275,11 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
     kernels ("intra", "inter"; kda_fwd_chunked_stage) on the same workspace.
     The input-side fusion options are those of fwd_chunked.
     """
-    args, o, fs, ws = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
-                                initial_state, chunk_size, output_final_state, out,
-                                final_state, workspace, gate=gate)
-    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1], q.device)
+    args, o, fs, ws, nsl = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
+                                     initial_state, chunk_size, output_final_state, out,
+                                     final_state, workspace, gate=gate, state_slots=state_slots)
+    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
+                         state_slots, nsl, args[6])
     keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws, opt) + akeep
     lib = library()
     if opt is None:
@@ -275,21 +296,22 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
 
 
 def bind_decode(q, k, v, log_alpha, beta, state, out=None, gate="log_alpha", gate_A=None,
-                gate_min=-5.0, l2norm_qk=False, beta_logits=False):
+                gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None):
     """Validate and marshal a kda_decode_step call once.  Returns (call, o);
     each `call()` advances `state` by one step in place.  The input-side
-    fusion options are those of decode_step."""
+    fusion and state-slot options are those of decode_step."""
     B, H, d = q.shape
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype, (B, H, d))
     _need_gate(log_alpha, gate, q.dtype, (B, H, d))
     _need(beta, "beta", torch.float32, (B, H))
-    _need(state, "state", torch.float32, (B, H, d, d))
+    nsl = state.shape[0] if state_slots is not None else 0
+    _need(state, "state", torch.float32, (nsl if state_slots is not None else B, H, d, d))
     o = out if out is not None else torch.empty((B, H, d), dtype=v.dtype, device=q.device)
     _need(o, "out", v.dtype, (B, H, d))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
             B, H, d, d, _dtype_code(q.dtype), _stream(q.device))
-    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, q.device)
+    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots, nsl, B)
     keep = (q, k, v, log_alpha, beta, state, o, opt) + akeep
     if opt is None:
         return BoundCall(library().kda_decode_step, args, "kda_decode_step", keep), o
@@ -301,15 +323,20 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 log_alpha: torch.Tensor, beta: torch.Tensor, state: torch.Tensor,
                 out: Optional[torch.Tensor] = None, gate: str = "log_alpha",
                 gate_A: Optional[torch.Tensor] = None, gate_min: float = -5.0,
-                l2norm_qk: bool = False, beta_logits: bool = False) -> torch.Tensor:
+                l2norm_qk: bool = False, beta_logits: bool = False,
+                state_slots: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One recurrent KDA step (kda_decode_step, or kda_decode_step_ex with
     input-side fusion); `state` is updated in place.
 
     q, k, v: [B, H, d] (bf16 or fp32); log_alpha: [B, H, d] fp32 (or the gate
     input z in q's dtype, see fwd_chunked); beta: [B, H] fp32;
-    state: [B, H, d, d] fp32.  Returns o [B, H, d].
+    state: [B, H, d, d] fp32, or with state_slots (int32 [B] device tensor)
+    a pool [num_slots, H, d, d] in which sequence b uses slot state_slots[b]
+    (a slot outside the pool marks padding: o = 0, no state touched).
+    Returns o [B, H, d].
     """
     call, o = bind_decode(q, k, v, log_alpha, beta, state, out=out, gate=gate, gate_A=gate_A,
-                          gate_min=gate_min, l2norm_qk=l2norm_qk, beta_logits=beta_logits)
+                          gate_min=gate_min, l2norm_qk=l2norm_qk, beta_logits=beta_logits,
+                          state_slots=state_slots)
     call()
     return o

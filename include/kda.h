@@ -184,6 +184,17 @@ typedef struct {
   int32_t l2norm_qk;    /* nonzero: q <- q / sqrt(|q|^2 + 1e-6) per token and
                            head, and the same for k, before any other use   */
   int32_t beta_logits;  /* nonzero: beta holds logits b; beta = sigmoid(b)   */
+  /* Serving: state slots (a drop-in cache for continuous batching; the
+     state per request has a fixed size, docsaid.org "Calculer le cache a la
+     main").  NULL = state i belongs to sequence i.  Otherwise the state
+     tensors (decode: state; prefill: initial_state and final_state) are
+     pools of num_slots states [num_slots, H, d_k, d_v], and sequence i uses
+     slot state_slots[i] (int32 device array, one entry per sequence).  A
+     slot outside [0, num_slots) marks padding: decode writes o = 0 for it
+     and leaves every state untouched; prefill starts it from a zero state
+     and writes no final state.  Slots of different sequences must differ.  */
+  const int32_t *state_slots;
+  int32_t num_slots;
 } kda_inputs;
 
 /*

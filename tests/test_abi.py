@@ -167,6 +167,11 @@ def test_fwd_ex_rejects_bad_options_on_host(lib):
     assert _fwd_ex(lib, _opts(gate=2, gmin=-5.0, norm=1, blog=1), wsb=16) == 1
     assert _fwd_ex(lib, _opts(gate=1, A=1 << 20), dk=96, dv=96) == 2
     assert _fwd_ex(lib, _opts(gate=2, gmin=-5.0), g=ctypes.c_void_p((1 << 20) + 8)) == 1
+    from gated_delta_rule_chunked_amd import kda
+    bad_slots = ctypes.pointer(kda.KdaInputs(0, None, 0.0, 0, 0, (1 << 20) + 2, 4))
+    assert _fwd_ex(lib, bad_slots) == 1                          # misaligned slots
+    no_pool = ctypes.pointer(kda.KdaInputs(0, None, 0.0, 0, 0, 1 << 20, 0))
+    assert _fwd_ex(lib, no_pool) == 1                            # num_slots < 1
 
 
 def test_decode_ex_rejects_bad_options_on_host(lib):
