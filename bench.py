@@ -17,9 +17,10 @@ Also reported on the same JSON line:
                 cores on repeated whole copies of the headline batch
   workloads     long-context prefill (B=1, H=32, T=32768), varlen packed
                 prefill (16 seqs of U[512, 8192] tokens, H=16, initial
-                states), the headline prefill in raw form (input-side fusion:
-                softplus gate from bf16 z, q/k L2-normalised in the kernel,
-                beta from logits) and recurrent decode (batch 256, H=32, 1000
+                states), the headline prefill in model-boundary form (input-side
+                fusion: softplus gate from bf16 z, q/k L2-normalised, beta
+                from logits; output epilogue: per-head RMSNorm and sigmoid
+                output gate) and recurrent decode (batch 256, H=32, 1000
                 steps) -- each with throughput, fraction of its roofline and,
                 for decode, the decode kernel's achieved HBM GB/s.
 Inputs come from gated_delta_rule_chunked_amd.inputs (seeded, synthetic).
@@ -65,10 +66,11 @@ def log(msg):
 # (sequence, head) state for decode).  E = bytes per q/k/v/o element, d the
 # head size, C the chunk size.
 
-def prefill_bytes_per_token_head(d, E, raw=False):
+def prefill_bytes_per_token_head(d, E, raw=False, epilogue=False):
     """q, k, v, o in the operand type, fp32 log-decay, fp32 beta; in raw form
-    the gate input z in the operand type replaces the fp32 log-decay."""
-    return 4 * E * d + (E * d if raw else 4 * d) + 4
+    the gate input z in the operand type replaces the fp32 log-decay; the
+    output epilogue adds the output-gate input."""
+    return 4 * E * d + (E * d if raw else 4 * d) + 4 + (E * d if epilogue else 0)
 
 
 def prefill_flops_per_token_head(d, C):
@@ -117,7 +119,7 @@ def measured_traffic(workload, kernel):
             rec["write_kib"] * 1024 * data["write_scale"])
 
 
-def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0, raw=False):
+def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0, raw=False, epilogue=False):
     """Algorithmic HBM bytes of one launch of a prefill kernel: what it must
     read and write given the two-kernel split (workspace tensors count)."""
     CK = max(C, 32)
@@ -125,7 +127,8 @@ def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0, raw=False):
         gate = E * d if raw else 4 * d
         return token_heads * (3 * E * d + gate + 4 + 4 * E * d + E * CK + 4 * d / C)
     if stage == "inter":      # read Qt, W, U, Ke, P, e^G_n; write o; states
-        return (token_heads * (5 * E * d + E * CK + 4 * d / C) +
+        epi = 3 * E * d if epilogue else 0  # epilogue pass: read o, z_o; write o
+        return (token_heads * (5 * E * d + E * CK + 4 * d / C + epi) +
                 pairs * state_bytes(d) * (2 if with_s0 else 1))
     raise ValueError(stage)
 
@@ -171,6 +174,9 @@ def upload_prefill_raw(torch, w):
     opt = w.options()
     if opt["gate_A"] is not None:
         opt["gate_A"] = torch.from_numpy(np.ascontiguousarray(opt["gate_A"])).cuda()
+    if w.out_norm_weight is not None:
+        opt["out_norm_weight"] = torch.from_numpy(w.out_norm_weight).cuda()
+        opt["out_gate"] = op(w.out_gate)
     return dict(q=op(w.q), k=op(w.k), v=op(w.v), log_alpha=op(w.z),
                 beta=torch.from_numpy(np.ascontiguousarray(w.beta_logits)).cuda(),
                 cu_seqlens=None, num_seqs=w.num_seqs, initial_state=None, options=opt)
@@ -221,8 +227,9 @@ def prefill_report(w, res, d, E, C):
     th = T * H
     s0 = w.initial_state is not None
     raw = isinstance(w, kin.RawPrefill)
-    byts = th * prefill_bytes_per_token_head(d, E, raw) + w.num_seqs * H * state_bytes(d) * (
-        2 if s0 else 1)
+    epi = raw and w.out_norm_weight is not None
+    byts = th * prefill_bytes_per_token_head(d, E, raw, epi) + w.num_seqs * H * state_bytes(
+        d) * (2 if s0 else 1)
     flops = th * prefill_flops_per_token_head(d, C)
     t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
     sec = res["ms_per_step"] * 1e-3
@@ -240,8 +247,10 @@ def dominant_roofline(wname, w, res, d, E, C):
     ku = res["kernel_us"]
     name = max(ku, key=ku.get)
     th = w.total_tokens * w.num_heads
+    raw = isinstance(w, kin.RawPrefill)
     b = kernel_bytes(name, th, w.num_seqs * w.num_heads, d, E, C,
-                     w.initial_state is not None, raw=isinstance(w, kin.RawPrefill))
+                     w.initial_state is not None, raw=raw,
+                     epilogue=raw and w.out_norm_weight is not None)
     ach = b / (ku[name] * 1e-6) / 1e9
     return dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=ach / HBM_PEAK_GBS, traffic=measured_traffic(wname, name), kernel=name,
@@ -457,13 +466,15 @@ def main():
             f"{json.dumps({k: round(v, 2) for k, v in r3['kernel_us'].items()})}")
         del w3
     if "raw" in extra:
-        log("prefill in raw form (softplus gate, q/k L2 norm, beta logits in the kernel)")
+        log("prefill in model-boundary form (softplus gate, q/k L2 norm, beta logits, "
+            "RMSNorm + output gate, all in the kernels)")
         w5 = kin.raw_prefill_workload()
         r5 = time_prefill(torch, kda, w5, args.steps, args.warmup)
-        workloads["prefill_raw"] = prefill_report(w5, r5, d, E, C)
-        workloads["prefill_raw"]["roofline"] = dominant_roofline("prefill_raw", w5, r5, d, E, C)
-        log(f"  {workloads['prefill_raw']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
-            f"{workloads['prefill_raw']['ms_per_step'] * 1e3:.1f} us/step, kernels(us) "
+        workloads["prefill_fused"] = prefill_report(w5, r5, d, E, C)
+        workloads["prefill_fused"]["roofline"] = dominant_roofline("prefill_fused", w5, r5, d,
+                                                                   E, C)
+        log(f"  {workloads['prefill_fused']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+            f"{workloads['prefill_fused']['ms_per_step'] * 1e3:.1f} us/step, kernels(us) "
             f"{json.dumps({k: round(v, 2) for k, v in r5['kernel_us'].items()})}")
         del w5
     torch.cuda.empty_cache()
@@ -488,7 +499,7 @@ def main():
         head = workloads["prefill"]
         value, unit, ms = head["tokens_per_s"], "tokens/s", head["ms_per_step"]
     else:  # a single extra workload (profiling runs)
-        name = {"raw": "prefill_raw"}.get(args.only, args.only)
+        name = {"raw": "prefill_fused"}.get(args.only, args.only)
         head = workloads[name]
         roof = head["roofline"]
         if name == "decode":

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "kda")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_decode.hip",
+           "kda_epilogue.hip"]
 ARCH = "gfx950"
 
 

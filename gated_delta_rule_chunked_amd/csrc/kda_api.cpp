@@ -21,9 +21,9 @@ bool head_dims_supported(int32_t d_k, int32_t d_v, kda_dtype dtype) {
 
 size_t elem_size(kda_dtype dt) { return dt == KDA_DTYPE_BF16 ? 2 : 4; }
 
-// Resolves kda_inputs (NULL = the plain call) into `out`.
-kda_status resolve_inputs(const kda_inputs *in, InputArgs *out) {
-  *out = InputArgs();
+// Resolves kda_options (NULL = the plain call) into `out`.
+kda_status resolve_options(const kda_options *in, OptArgs *out) {
+  *out = OptArgs();
   if (in == nullptr) return KDA_SUCCESS;
   if (in->gate != KDA_GATE_LOG_ALPHA && in->gate != KDA_GATE_SOFTPLUS &&
       in->gate != KDA_GATE_SIGMOID)
@@ -41,6 +41,16 @@ kda_status resolve_inputs(const kda_inputs *in, InputArgs *out) {
     if (!aligned(in->state_slots, 4) || in->num_slots < 1) return KDA_ERROR_INVALID_VALUE;
     out->slots = in->state_slots;
     out->num_slots = in->num_slots;
+  }
+  if (in->out_gate && !in->out_norm_weight) return KDA_ERROR_INVALID_VALUE;
+  if (in->out_norm_weight) {
+    if (!aligned(in->out_norm_weight, 16) || (in->out_gate && !aligned(in->out_gate, 16)))
+      return KDA_ERROR_INVALID_VALUE;
+    if (!(in->out_norm_eps > 0.f && in->out_norm_eps < 3.0e38f))  // also rejects NaN
+      return KDA_ERROR_INVALID_VALUE;
+    out->norm_w = in->out_norm_weight;
+    out->out_gate = in->out_gate;
+    out->norm_eps = in->out_norm_eps;
   }
   return KDA_SUCCESS;
 }
@@ -96,7 +106,7 @@ namespace {
 
 // Validates the prefill arguments and runs the stages selected by `mask`
 // (bit s = stage s) in order.
-kda_status fwd_run(unsigned mask, const kda_inputs *inputs, const void *q, const void *k,
+kda_status fwd_run(unsigned mask, const kda_options *options, const void *q, const void *k,
                    const void *v, const void *gate, const float *beta,
                    const int32_t *cu_seqlens,
                    int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
@@ -104,8 +114,8 @@ kda_status fwd_run(unsigned mask, const kda_inputs *inputs, const void *q, const
                    const float *initial_state, float *final_state, void *o,
                    void *workspace, size_t workspace_bytes, void *stream) {
   if (mask == 0u || mask > 3u) return KDA_ERROR_INVALID_VALUE;
-  InputArgs in;
-  kda_status st = resolve_inputs(inputs, &in);
+  OptArgs in;
+  kda_status st = resolve_options(options, &in);
   if (st != KDA_SUCCESS) return st;
   st = check_fwd_sizes(total_tokens, num_seqs, num_heads, d_k, d_v, chunk_size, dtype);
   if (st != KDA_SUCCESS) return st;
@@ -152,6 +162,9 @@ kda_status fwd_run(unsigned mask, const kda_inputs *inputs, const void *q, const
 
   if ((mask & 1u) && launch_intra(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 2u) && launch_inter(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
+  if ((mask & 2u) && in.norm_w && total_tokens > 0 &&
+      launch_out_epilogue(o, in, total_tokens * num_heads, d_v, dtype, a.stream) != hipSuccess)
+    return KDA_ERROR_LAUNCH_FAILED;
   return KDA_SUCCESS;
 }
 
@@ -184,7 +197,7 @@ kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void 
                  initial_state, final_state, o, workspace, workspace_bytes, stream);
 }
 
-kda_status kda_fwd_chunked_ex(const kda_inputs *inputs, uint32_t stages, const void *q,
+kda_status kda_fwd_chunked_ex(const kda_options *options, uint32_t stages, const void *q,
                               const void *k, const void *v, const void *gate,
                               const float *beta, const int32_t *cu_seqlens,
                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
@@ -192,7 +205,7 @@ kda_status kda_fwd_chunked_ex(const kda_inputs *inputs, uint32_t stages, const v
                               kda_dtype dtype, const float *initial_state,
                               float *final_state, void *o, void *workspace,
                               size_t workspace_bytes, void *stream) {
-  return fwd_run(stages, inputs, q, k, v, gate, beta, cu_seqlens, num_seqs, total_tokens,
+  return fwd_run(stages, options, q, k, v, gate, beta, cu_seqlens, num_seqs, total_tokens,
                  num_heads, d_k, d_v, chunk_size, dtype, initial_state, final_state, o,
                  workspace, workspace_bytes, stream);
 }
@@ -205,12 +218,12 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                             d_k, d_v, dtype, stream);
 }
 
-kda_status kda_decode_step_ex(const kda_inputs *inputs, const void *q, const void *k,
+kda_status kda_decode_step_ex(const kda_options *options, const void *q, const void *k,
                               const void *v, const void *gate, const float *beta,
                               float *state, void *o, int32_t batch, int32_t num_heads,
                               int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream) {
-  InputArgs in;
-  const kda_status st = resolve_inputs(inputs, &in);
+  OptArgs in;
+  const kda_status st = resolve_options(options, &in);
   if (st != KDA_SUCCESS) return st;
   if (batch < 1 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERROR_INVALID_VALUE;
   if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERROR_INVALID_VALUE;

@@ -177,6 +177,12 @@ __device__ __forceinline__ typename Frag<T>::type pack_quads(f32x4 a, f32x4 b) {
   return r;
 }
 
+// 8 consecutive elements from two fp32 quads (16 bytes for bf16).
+template <typename T>
+__device__ __forceinline__ void store8_f32(T *p, f32x4 a, f32x4 b) {
+  *reinterpret_cast<typename Frag<T>::type *>(p) = pack_quads<T>(a, b);
+}
+
 // ---- fragment-major workspace storage -------------------------------------
 // An operand that one kernel writes and another feeds to the matrix cores is
 // stored in the order its fragments are loaded, so that each wavefront load
@@ -224,7 +230,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Lane index helpers for the tile convention above.
-// ---- input-side fusion (kda_inputs in kda.h), fp32 ------------------------
+// ---- input-side fusion (kda_options in kda.h), fp32 ------------------------
 __device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
 
 // Kimi Linear's gate g = -exp(A) softplus(z), softplus(z) = log(1 + e^z)
@@ -250,17 +256,17 @@ __device__ __forceinline__ float dpp_add(float x) {
   return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of W consecutive lanes (W = 8, 16, 32 or 64),
+// Sum over aligned groups of W consecutive lanes (W = 4, 8, 16, 32 or 64),
 // every lane of a group receiving the group's sum.  Pairwise exchanges:
 // quad permutes [1,0,3,2] and [2,3,0,1], then the half-row mirror (lane i
 // with 7 - i) and the row mirror (i with 15 - i), each pairing two groups
 // whose sums are already complete; beyond 16 lanes a cross-lane shuffle.
 template <int W>
 __device__ __forceinline__ float group_sum(float s) {
-  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  static_assert(W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
   s = dpp_add<0xB1>(s);   // quad_perm [1,0,3,2]
   s = dpp_add<0x4E>(s);   // quad_perm [2,3,0,1]
-  s = dpp_add<0x141>(s);  // row_half_mirror
+  if constexpr (W >= 8) s = dpp_add<0x141>(s);  // row_half_mirror
   if constexpr (W >= 16) s = dpp_add<0x140>(s);  // row_mirror
   if constexpr (W >= 32) s += __shfl_xor(s, 16);
   if constexpr (W >= 64) s += __shfl_xor(s, 32);

@@ -22,10 +22,12 @@
 // writes a contiguous run of rows.  Column sums are reduced over the lanes of
 // a wavefront with cross-lane shuffles and over wavefronts through LDS.
 //
-// Input-side fusion (kda_inputs): with RAW the gate input is z and the gate
+// Input-side fusion (kda_options): with RAW the gate input is z and the gate
 // function gives g per key channel.  With l2norm_qk, q and k enter the step
 // only through S^T (alpha k), S^T (alpha q), k . q and k u^T, so their norms
-// are reduced alongside k . q and applied as scalar factors.
+// are reduced alongside k . q and applied as scalar factors.  The output
+// epilogue (RMSNorm over the row, output gate) runs on the fp32 row held by
+// the first d/4 lanes before it is rounded and stored.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -34,7 +36,7 @@ namespace kda {
 template <typename T, int D, int NT, bool RAW>
 __global__ __launch_bounds__(NT) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const void *__restrict__ gate, const float *__restrict__ beta, const InputArgs in,
+    const void *__restrict__ gate, const float *__restrict__ beta, const OptArgs in,
     float *__restrict__ state, T *__restrict__ o) {
   constexpr int NCQ = D / 4;         // float4 column groups
   constexpr int NRG = NT / NCQ;      // row groups
@@ -139,8 +141,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(
     vv = f32x4{to_f32(vp[0]), to_f32(vp[1]), to_f32(vp[2]), to_f32(vp[3])};
   }
   const f32x4 u = b * (vv - xs);
-  if (rg == 0) {
-    const f32x4 ov = ys + kqs * u;
+  if (rg == 0) {  // lanes 0 .. NCQ-1 of wave 0 hold the output row
+    f32x4 ov = ys + kqs * u;
+    if (in.norm_w) {  // output epilogue on the fp32 row: RMSNorm, gate
+      const float ss = group_sum<NCQ>(ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] +
+                                      ov[3] * ov[3]);
+      ov *= rsqrtf(ss * (1.f / D) + in.norm_eps);
+      ov *= *reinterpret_cast<const f32x4 *>(in.norm_w + 4 * cq);
+      if (in.out_gate) {
+        const f32x4 zo = to_f32x4(load4<T>(reinterpret_cast<const T *>(in.out_gate) +
+                                           p * D + 4 * cq));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] *= sigmoid(zo[e]);
+      }
+    }
     store4_f32<T>(o + p * D + 4 * cq, ov);
   }
 #pragma unroll
@@ -153,7 +167,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
 
 template <typename T, int D, int NT>
 static void launch_decode_k(const void *q, const void *k, const void *v, const void *gate,
-                            const float *beta, const InputArgs &in, float *state, void *o,
+                            const float *beta, const OptArgs &in, float *state, void *o,
                             int pairs, hipStream_t s) {
   const T *qq = reinterpret_cast<const T *>(q);
   const T *kk = reinterpret_cast<const T *>(k);
@@ -169,7 +183,7 @@ static void launch_decode_k(const void *q, const void *k, const void *v, const v
 
 template <typename T>
 static hipError_t launch_decode_t(const void *q, const void *k, const void *v,
-                                  const void *gate, const float *beta, const InputArgs &in,
+                                  const void *gate, const float *beta, const OptArgs &in,
                                   float *state, void *o, int pairs, int d, hipStream_t s) {
   switch (d) {
     case 32: launch_decode_k<T, 32, 64>(q, k, v, gate, beta, in, state, o, pairs, s); break;
@@ -181,10 +195,10 @@ static hipError_t launch_decode_t(const void *q, const void *k, const void *v,
 }
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const void *gate,
-                         const float *beta, const InputArgs &in, float *state, void *o,
+                         const float *beta, const OptArgs &in, float *state, void *o,
                          int batch, int heads, int d, kda_dtype dt, hipStream_t stream) {
   const int pairs = batch * heads;
-  InputArgs ia = in;
+  OptArgs ia = in;
   ia.heads = heads;
   if (dt == KDA_DTYPE_BF16)
     return launch_decode_t<bf16>(q, k, v, gate, beta, ia, state, o, pairs, d, stream);

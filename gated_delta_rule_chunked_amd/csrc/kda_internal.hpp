@@ -60,17 +60,21 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
   return L;
 }
 
-// Input-side fusion, resolved on the host (kda_inputs in kda.h): the gate
+// kda_options (kda.h) resolved on the host.  Input-side fusion: the gate
 // function (0 = g given, 1 = softplus gate, 2 = sigmoid gate), A per head
-// (softplus gate), g_min (sigmoid gate), and the q/k normalisation and
-// beta-logit flags.
-struct InputArgs {
+// (softplus gate), g_min (sigmoid gate), the q/k normalisation and
+// beta-logit flags.  Serving: state slots.  Output epilogue: RMSNorm weight
+// (nullptr = off), output gate input and epsilon.
+struct OptArgs {
   int gate = KDA_GATE_LOG_ALPHA;
   const float *gate_A = nullptr;
   float gate_min = 0.f;
   int l2norm_qk = 0, beta_logits = 0;
   const int *slots = nullptr;  // state slot per sequence, or nullptr
   int num_slots = 0;
+  const float *norm_w = nullptr;
+  const void *out_gate = nullptr;
+  float norm_eps = 0.f;
   int heads = 0;  // decode: heads per sequence, to find A of state p
 };
 
@@ -79,7 +83,7 @@ struct FwdArgs {
   const void *q, *k, *v;
   const void *gate;        // g (fp32) or the gate input z (operand type)
   const float *beta;
-  InputArgs in;
+  OptArgs in;
   const int *cu_seqlens;  // device, or nullptr for equal lengths
   int num_seqs, num_heads, d, chunk;
   int64_t total_tokens;
@@ -95,8 +99,11 @@ struct FwdArgs {
 
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
 hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
+// In place on o [rows, d]: o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(z).
+hipError_t launch_out_epilogue(void *o, const OptArgs &in, int64_t rows, int d,
+                               kda_dtype dt, hipStream_t stream);
 hipError_t launch_decode(const void *q, const void *k, const void *v,
-                         const void *gate, const float *beta, const InputArgs &in,
+                         const void *gate, const float *beta, const OptArgs &in,
                          float *state, void *o, int batch, int heads, int d,
                          kda_dtype dt, hipStream_t stream);
 

@@ -146,12 +146,6 @@ struct IntraCfg {
   static_assert(NW % NRB == 0, "phase-4 wave split");
 };
 
-// 8 consecutive elements from two fp32 quads (16 bytes for bf16).
-template <typename T>
-__device__ __forceinline__ void store8_f32(T *p, f32x4 a, f32x4 b) {
-  *reinterpret_cast<typename Frag<T>::type *>(p) = pack_quads<T>(a, b);
-}
-
 // One lane's run of a fragment-major block: the 8 kperm positions 8 g .. 8 g + 7
 // of a 32-group hold indices 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, so
 // the run is two quads of a row-major LDS row, written as 8 consecutive
@@ -194,7 +188,7 @@ __device__ __forceinline__ void store_elems(T *p, const T *x) {
 template <typename T, int D, int C, bool RAW>
 __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const void *__restrict__ gate, const float *__restrict__ beta, const InputArgs in,
+    const void *__restrict__ gate, const float *__restrict__ beta, const OptArgs in,
     const int *__restrict__ cu, int N, int H, int seq_len, int *__restrict__ seq_first,
     T *__restrict__ qt_out, T *__restrict__ w_out, T *__restrict__ ut_out,
     T *__restrict__ ket_out, T *__restrict__ p_out, float *__restrict__ gam_out) {

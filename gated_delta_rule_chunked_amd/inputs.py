@@ -220,7 +220,7 @@ def decode_step(step: int, batch: int = 256, H: int = 32, d: int = 128,
                       beta=beta.astype(np.float32), dtype=dtype)
 
 
-# ---- raw inputs for the input-side fusion (kda_inputs) ----------------------
+# ---- raw inputs for the input-side fusion (kda_options) ----------------------
 # Recipe (numpy PCG64, seed given, fp64 draws in this order):
 #   1. q, k ~ N(0, 1) [T, H, d], not normalised (norms about sqrt(d));
 #   2. v ~ N(0, 1);
@@ -253,6 +253,8 @@ class RawPrefill:
     initial_state: Optional[np.ndarray]
     dtype: str
     chunk_size: int
+    out_norm_weight: Optional[np.ndarray] = None  # [d] float32: output epilogue
+    out_gate: Optional[np.ndarray] = None         # [T, H, d] operand dtype
 
     @property
     def total_tokens(self) -> int:
@@ -306,16 +308,21 @@ def make_prefill_raw(seed, *, H: int, d: int, dtype: str, chunk_size: int, gate:
                       dtype=dtype, chunk_size=chunk_size)
 
 
-# Raw-input form of the headline prefill (Kimi Linear's softplus gate), the
-# input-side fusion benchmark workload; seed 5.
-RAW_PREFILL = dict(name="prefill_raw", B=2, H=8, T=2048, d=128, chunk_size=64,
+# Model-boundary form of the headline prefill, the fusion benchmark workload:
+# raw inputs (Kimi Linear's softplus gate, seed 5) and the output epilogue
+# (RMSNorm weight and output-gate logits from epilogue_inputs, seed 55).
+RAW_PREFILL = dict(name="prefill_fused", B=2, H=8, T=2048, d=128, chunk_size=64,
                    dtype=BF16, gate="softplus")
 
 
-def raw_prefill_workload() -> RawPrefill:
+def raw_prefill_workload(with_epilogue: bool = True) -> RawPrefill:
     w = dict(RAW_PREFILL)
     w.pop("name")
-    return make_prefill_raw(5, **w)
+    r = make_prefill_raw(5, **w)
+    if with_epilogue:
+        r.out_norm_weight, r.out_gate = epilogue_inputs(55, (r.total_tokens, r.num_heads),
+                                                        w["d"], w["dtype"])
+    return r
 
 
 def decode_step_raw(step: int, batch: int, H: int, d: int, dtype: str, gate: str,
@@ -339,3 +346,13 @@ def decode_step_raw(step: int, batch: int, H: int, d: int, dtype: str, gate: str
                       beta_logits=bl.astype(np.float32), gate=gate, gate_A=A,
                       gate_min=-5.0, cu_seqlens=None, num_seqs=batch, initial_state=None,
                       dtype=dtype, chunk_size=0)
+
+
+def epilogue_inputs(seed, rows_shape, d: int, dtype: str):
+    """Output-epilogue inputs from default_rng(seed), in this order: RMSNorm
+    weight 1 + 0.2 N(0, 1) [d] (fp32), then output-gate logits N(0, 1)
+    [*rows_shape, d] rounded to the operand dtype."""
+    rng = np.random.default_rng(seed)
+    w = (1.0 + 0.2 * rng.standard_normal(d)).astype(np.float32)
+    z = rng.standard_normal(tuple(rows_shape) + (d,))
+    return w, _round_operand(z, dtype)

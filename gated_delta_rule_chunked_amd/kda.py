@@ -24,12 +24,14 @@ _lib = None
 GATES = {"log_alpha": 0, "softplus": 1, "sigmoid": 2}
 
 
-class KdaInputs(ctypes.Structure):
-    """kda_inputs (include/kda.h): input-side fusion options."""
+class KdaOptions(ctypes.Structure):
+    """kda_options (include/kda.h): input-side fusion, state slots, output
+    epilogue."""
     _fields_ = [("gate", ctypes.c_int), ("gate_A", ctypes.c_void_p),
                 ("gate_min", ctypes.c_float), ("l2norm_qk", ctypes.c_int32),
                 ("beta_logits", ctypes.c_int32), ("state_slots", ctypes.c_void_p),
-                ("num_slots", ctypes.c_int32)]
+                ("num_slots", ctypes.c_int32), ("out_norm_weight", ctypes.c_void_p),
+                ("out_gate", ctypes.c_void_p), ("out_norm_eps", ctypes.c_float)]
 
 
 class KdaError(RuntimeError):
@@ -60,7 +62,7 @@ def library():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
-    pin = ctypes.POINTER(KdaInputs)
+    pin = ctypes.POINTER(KdaOptions)
     lib.kda_fwd_chunked_ex.restype = ctypes.c_int
     lib.kda_fwd_chunked_ex.argtypes = [pin, ctypes.c_uint32] + lib.kda_fwd_chunked.argtypes
     lib.kda_decode_step_ex.restype = ctypes.c_int
@@ -114,12 +116,15 @@ STAGES = {"intra": 0, "inter": 1}
 
 
 def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
-            num_slots=0, n=None):
-    """kda_inputs for the options, or None for the plain call, and the
-    tensors it points to."""
+            num_slots=0, n=None, epilogue=None):
+    """kda_options for the options, or None for the plain call, and the
+    tensors it points to.  `epilogue` = (out_norm_weight, out_gate,
+    out_norm_eps, d, out_gate_shape, dtype) or None."""
     if gate not in GATES:
         raise KdaError(f"unknown gate {gate!r}; one of {sorted(GATES)}")
-    if gate == "log_alpha" and not l2norm_qk and not beta_logits and state_slots is None:
+    no_epi = epilogue is None or (epilogue[0] is None and epilogue[1] is None)
+    if (gate == "log_alpha" and not l2norm_qk and not beta_logits and state_slots is None
+            and no_epi):
         return None, ()
     keep = ()
     a_ptr = None
@@ -132,8 +137,20 @@ def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
     if state_slots is not None:
         _need(state_slots, "state_slots", torch.int32, (n,))
         s_ptr, keep = state_slots.data_ptr(), keep + (state_slots,)
-    return ctypes.pointer(KdaInputs(GATES[gate], a_ptr, float(gate_min), int(bool(l2norm_qk)),
-                                    int(bool(beta_logits)), s_ptr, int(num_slots))), keep
+    w_ptr = z_ptr = None
+    eps = 0.0
+    if not no_epi:
+        w, z, eps, d, zshape, dtype = epilogue
+        if w is None:
+            raise KdaError("out_gate needs out_norm_weight (the epilogue is RMSNorm, then gate)")
+        _need(w, "out_norm_weight", torch.float32, (d,))
+        w_ptr, keep = w.data_ptr(), keep + (w,)
+        if z is not None:
+            _need(z, "out_gate", dtype, zshape)
+            z_ptr, keep = z.data_ptr(), keep + (z,)
+    return ctypes.pointer(KdaOptions(GATES[gate], a_ptr, float(gate_min), int(bool(l2norm_qk)),
+                                     int(bool(beta_logits)), s_ptr, int(num_slots), w_ptr,
+                                     z_ptr, float(eps))), keep
 
 
 def _need_gate(g, gate, dtype, shape):
@@ -206,6 +223,8 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 gate: str = "log_alpha", gate_A: Optional[torch.Tensor] = None,
                 gate_min: float = -5.0, l2norm_qk: bool = False,
                 beta_logits: bool = False, state_slots: Optional[torch.Tensor] = None,
+                out_norm_weight: Optional[torch.Tensor] = None,
+                out_gate: Optional[torch.Tensor] = None, out_norm_eps: float = 1e-6,
                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill (kda_fwd_chunked, or kda_fwd_chunked_ex with
     input-side fusion).
@@ -220,12 +239,15 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     that kernel (kda_fwd_chunked_stage); it then needs the `workspace`, `out`
     and `final_state` of a preceding call with the same arguments.
 
-    Input-side fusion (kda_inputs): gate="softplus" (g = -exp(gate_A[h])
+    Input-side fusion (kda_options): gate="softplus" (g = -exp(gate_A[h])
     softplus(z)) or "sigmoid" (g = gate_min sigmoid(z)) makes `log_alpha`
     the gate input z, in q's dtype; l2norm_qk normalises q and k per token
     and head; beta_logits passes beta through a sigmoid.  state_slots (int32
     [N] device tensor) makes initial_state / final_state pools of states
     indexed by slot (final_state defaults to initial_state then).
+    out_norm_weight (fp32 [d]) turns on the output epilogue: every output
+    row becomes o / sqrt(mean(o^2) + out_norm_eps) * out_norm_weight *
+    sigmoid(out_gate) (out_gate [T, H, d] in v's dtype, or None).
     """
     if stage is not None and stage not in STAGES:
         raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
@@ -234,7 +256,9 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                     final_state, workspace, allow_alloc_ws=stage is None,
                                     gate=gate, state_slots=state_slots)
     opt, _keep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
-                         state_slots, nsl, args[6])
+                         state_slots, nsl, args[6],
+                         (out_norm_weight, out_gate, out_norm_eps, q.shape[2], tuple(o.shape),
+                          v.dtype))
     if opt is not None:
         mask = 3 if stage is None else 1 << STAGES[stage]
         _check(library().kda_fwd_chunked_ex(opt, mask, *args), "kda_fwd_chunked_ex")
@@ -267,7 +291,8 @@ class BoundCall:
 def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
              initial_state=None, chunk_size=64, output_final_state=True,
              out=None, final_state=None, workspace=None, gate="log_alpha", gate_A=None,
-             gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None):
+             gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None,
+             out_norm_weight=None, out_gate=None, out_norm_eps=1e-6):
     """Validate and marshal a kda_fwd_chunked call once, for repeated calls.
 
     Nothing is launched here.  Returns (call, stage_calls, o, final_state):
@@ -279,7 +304,9 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
                                      initial_state, chunk_size, output_final_state, out,
                                      final_state, workspace, gate=gate, state_slots=state_slots)
     opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
-                         state_slots, nsl, args[6])
+                         state_slots, nsl, args[6],
+                         (out_norm_weight, out_gate, out_norm_eps, q.shape[2], tuple(o.shape),
+                          v.dtype))
     keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws, opt) + akeep
     lib = library()
     if opt is None:
@@ -296,7 +323,8 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
 
 
 def bind_decode(q, k, v, log_alpha, beta, state, out=None, gate="log_alpha", gate_A=None,
-                gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None):
+                gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None,
+                out_norm_weight=None, out_gate=None, out_norm_eps=1e-6):
     """Validate and marshal a kda_decode_step call once.  Returns (call, o);
     each `call()` advances `state` by one step in place.  The input-side
     fusion and state-slot options are those of decode_step."""
@@ -311,7 +339,8 @@ def bind_decode(q, k, v, log_alpha, beta, state, out=None, gate="log_alpha", gat
     _need(o, "out", v.dtype, (B, H, d))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(state), _ptr(o),
             B, H, d, d, _dtype_code(q.dtype), _stream(q.device))
-    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots, nsl, B)
+    opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots, nsl, B,
+                         (out_norm_weight, out_gate, out_norm_eps, d, (B, H, d), v.dtype))
     keep = (q, k, v, log_alpha, beta, state, o, opt) + akeep
     if opt is None:
         return BoundCall(library().kda_decode_step, args, "kda_decode_step", keep), o
@@ -324,7 +353,10 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 out: Optional[torch.Tensor] = None, gate: str = "log_alpha",
                 gate_A: Optional[torch.Tensor] = None, gate_min: float = -5.0,
                 l2norm_qk: bool = False, beta_logits: bool = False,
-                state_slots: Optional[torch.Tensor] = None) -> torch.Tensor:
+                state_slots: Optional[torch.Tensor] = None,
+                out_norm_weight: Optional[torch.Tensor] = None,
+                out_gate: Optional[torch.Tensor] = None,
+                out_norm_eps: float = 1e-6) -> torch.Tensor:
     """One recurrent KDA step (kda_decode_step, or kda_decode_step_ex with
     input-side fusion); `state` is updated in place.
 
@@ -333,10 +365,12 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     state: [B, H, d, d] fp32, or with state_slots (int32 [B] device tensor)
     a pool [num_slots, H, d, d] in which sequence b uses slot state_slots[b]
     (a slot outside the pool marks padding: o = 0, no state touched).
-    Returns o [B, H, d].
+    The output epilogue options are those of fwd_chunked (out_gate
+    [B, H, d]).  Returns o [B, H, d].
     """
     call, o = bind_decode(q, k, v, log_alpha, beta, state, out=out, gate=gate, gate_A=gate_A,
                           gate_min=gate_min, l2norm_qk=l2norm_qk, beta_logits=beta_logits,
-                          state_slots=state_slots)
+                          state_slots=state_slots, out_norm_weight=out_norm_weight,
+                          out_gate=out_gate, out_norm_eps=out_norm_eps)
     call()
     return o

@@ -158,16 +158,19 @@ kda_status kda_fwd_chunked_stage(kda_fwd_stage stage, const void *q, const void 
                                  void *stream);
 
 /*
- * ---- Input-side fusion ----------------------------------------------------
- * Steps that the layers feeding the operator would otherwise run as separate
- * passes over q, k, the gate and beta, done by the kernels as they read them
- * (docsaid.org "Kimi Linear", section "Les autres pieces": q and k are
- * L2-normalised, beta is a sigmoid, the decay comes from a gate function;
- * fr.news.hada.io, section "Configuration du modele Kimi Linear";
- * mkdocs.reaper.mx "Attention lineaire et recurrence", section "Le piege
- * numerique de la decroissance cumulee": Kimi Linear's
+ * ---- Options of the _ex calls ---------------------------------------------
+ * Input-side fusion: steps that the layers feeding the operator would
+ * otherwise run as separate passes over q, k, the gate and beta, done by the
+ * kernels as they read them (docsaid.org "Kimi Linear", section "Les autres
+ * pieces": q and k are L2-normalised, beta is a sigmoid, the decay comes from
+ * a gate function; fr.news.hada.io, section "Configuration du modele Kimi
+ * Linear"; mkdocs.reaper.mx "Attention lineaire et recurrence", section "Le
+ * piege numerique de la decroissance cumulee": Kimi Linear's
  * g = -exp(A) softplus(z), and the scaled sigmoid bounded below by g_min).
- * All of it is evaluated in fp32 from the stored inputs.
+ * Output epilogue: the per-head RMSNorm and the data-dependent sigmoid
+ * output gate that follow the operator (same docsaid.org section;
+ * fr.news.hada.io, section "Configuration du modele Kimi Linear").
+ * All of it is evaluated in fp32.
  */
 typedef enum {
   KDA_GATE_LOG_ALPHA = 0, /* gate holds g = log(alpha) itself, fp32           */
@@ -178,13 +181,14 @@ typedef enum {
 } kda_gate;
 
 typedef struct {
+  /* -- input-side fusion -- */
   kda_gate gate;
   const float *gate_A;  /* KDA_GATE_SOFTPLUS: [num_heads] fp32 device array  */
   float gate_min;       /* KDA_GATE_SIGMOID: finite and < 0 (-5 in Kimi K3)  */
   int32_t l2norm_qk;    /* nonzero: q <- q / sqrt(|q|^2 + 1e-6) per token and
                            head, and the same for k, before any other use   */
   int32_t beta_logits;  /* nonzero: beta holds logits b; beta = sigmoid(b)   */
-  /* Serving: state slots (a drop-in cache for continuous batching; the
+  /* -- serving: state slots (a drop-in cache for continuous batching; the
      state per request has a fixed size, docsaid.org "Calculer le cache a la
      main").  NULL = state i belongs to sequence i.  Otherwise the state
      tensors (decode: state; prefill: initial_state and final_state) are
@@ -192,17 +196,28 @@ typedef struct {
      slot state_slots[i] (int32 device array, one entry per sequence).  A
      slot outside [0, num_slots) marks padding: decode writes o = 0 for it
      and leaves every state untouched; prefill starts it from a zero state
-     and writes no final state.  Slots of different sequences must differ.  */
+     and writes no final state.  Slots of different sequences must differ. */
   const int32_t *state_slots;
   int32_t num_slots;
-} kda_inputs;
+  /* -- output epilogue: when out_norm_weight is set, every output row
+     o[t, h, :] (d_v values) becomes
+         o / sqrt(mean(o^2) + out_norm_eps) * out_norm_weight * sigmoid(z_o)
+     with z_o = out_gate[t, h, :] (the sigmoid factor is 1 when out_gate is
+     NULL).  Decode applies it to the fp32 output before rounding; prefill
+     runs it as a pass over o after the inter-chunk kernel (its d_v columns
+     are computed by different workgroups), within the inter stage.        */
+  const float *out_norm_weight; /* [d_v] fp32, shared by the heads, or NULL */
+  const void *out_gate;         /* [tokens or batch, H, d_v] in dtype, or NULL */
+  float out_norm_eps;           /* > 0, finite                              */
+} kda_options;
 
 /*
- * kda_fwd_chunked with input-side fusion and a stage mask.
+ * kda_fwd_chunked with options (input-side fusion, state slots, output
+ * epilogue) and a stage mask.
  *
- *   inputs   how to read gate and beta, and whether to normalise q and k;
- *            NULL means {KDA_GATE_LOG_ALPHA, NULL, 0, 0, 0}, i.e. exactly
- *            kda_fwd_chunked.
+ *   options  kda_options above; NULL (or all fields zero) is exactly
+ *            kda_fwd_chunked.  out_gate is [total_tokens, H, d_v] in dtype,
+ *            16-byte aligned.
  *   stages   bit 0 runs the intra-chunk kernel, bit 1 the inter-chunk
  *            kernel (3 = the whole call; see kda_fwd_chunked_stage for the
  *            ordering rules of single stages).  Other values are invalid.
@@ -214,7 +229,7 @@ typedef struct {
  * KDA_GATE_SIGMOID with gate_min >= -5 meets it for any z when
  * chunk_size = 16 (16 x 5 = 80, the tile bound of the section cited above).
  */
-kda_status kda_fwd_chunked_ex(const kda_inputs *inputs, uint32_t stages, const void *q,
+kda_status kda_fwd_chunked_ex(const kda_options *options, uint32_t stages, const void *q,
                               const void *k, const void *v, const void *gate,
                               const float *beta, const int32_t *cu_seqlens,
                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
@@ -248,10 +263,11 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            kda_dtype dtype, void *stream);
 
 /*
- * kda_decode_step with input-side fusion: `inputs` and `gate` as for
- * kda_fwd_chunked_ex (gate [batch, H, d_k]; NULL inputs = kda_decode_step).
+ * kda_decode_step with options: `options` and `gate` as for
+ * kda_fwd_chunked_ex (gate [batch, H, d_k], out_gate [batch, H, d_v];
+ * NULL options = kda_decode_step).  With state_slots, `state` is the pool.
  */
-kda_status kda_decode_step_ex(const kda_inputs *inputs, const void *q, const void *k,
+kda_status kda_decode_step_ex(const kda_options *options, const void *q, const void *k,
                               const void *v, const void *gate, const float *beta,
                               float *state, void *o, int32_t batch, int32_t num_heads,
                               int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream);

@@ -217,3 +217,24 @@ def prepare_inputs(q, k, gate_in, beta_in, gate="log_alpha", gate_A=None, gate_m
         q, k = l2_normalize(q), l2_normalize(k)
     b = sigmoid(beta_in) if beta_logits else np.asarray(beta_in, dtype=np.float64)
     return q, k, g, b
+
+
+# ---- output epilogue (numpy, fp64) ------------------------------------------
+# docsaid.org "Kimi Linear", section "Les autres pieces" and fr.news.hada.io,
+# section "Configuration du modele Kimi Linear": the output goes through an
+# RMSNorm per head, then is multiplied by a data-dependent sigmoid gate.
+
+def rms_norm(o, weight, eps):
+    """o / sqrt(mean(o^2) + eps) * weight over the last axis (per token and
+    head); weight [d_v] is shared by the heads."""
+    o = np.asarray(o, dtype=np.float64)
+    return o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps) * np.asarray(
+        weight, dtype=np.float64)
+
+
+def output_epilogue(o, weight, eps, out_gate=None):
+    """RMSNorm per head, then the sigmoid output gate (factor 1 without one)."""
+    y = rms_norm(o, weight, eps)
+    if out_gate is not None:
+        y = y * sigmoid(out_gate)
+    return y

@@ -138,7 +138,7 @@ def test_binding_fails_loudly_without_device():
 
 def _opts(gate=0, A=None, gmin=0.0, norm=0, blog=0):
     from gated_delta_rule_chunked_amd import kda
-    return ctypes.pointer(kda.KdaInputs(gate, A, gmin, norm, blog))
+    return ctypes.pointer(kda.KdaOptions(gate, A, gmin, norm, blog))
 
 
 def _fwd_ex(lib, opt, stages=3, **over):
@@ -168,10 +168,18 @@ def test_fwd_ex_rejects_bad_options_on_host(lib):
     assert _fwd_ex(lib, _opts(gate=1, A=1 << 20), dk=96, dv=96) == 2
     assert _fwd_ex(lib, _opts(gate=2, gmin=-5.0), g=ctypes.c_void_p((1 << 20) + 8)) == 1
     from gated_delta_rule_chunked_amd import kda
-    bad_slots = ctypes.pointer(kda.KdaInputs(0, None, 0.0, 0, 0, (1 << 20) + 2, 4))
+    bad_slots = ctypes.pointer(kda.KdaOptions(0, None, 0.0, 0, 0, (1 << 20) + 2, 4))
     assert _fwd_ex(lib, bad_slots) == 1                          # misaligned slots
-    no_pool = ctypes.pointer(kda.KdaInputs(0, None, 0.0, 0, 0, 1 << 20, 0))
+    no_pool = ctypes.pointer(kda.KdaOptions(0, None, 0.0, 0, 0, 1 << 20, 0))
     assert _fwd_ex(lib, no_pool) == 1                            # num_slots < 1
+    def epi(w, z, eps):
+        return ctypes.pointer(kda.KdaOptions(0, None, 0.0, 0, 0, None, 0, w, z, eps))
+    assert _fwd_ex(lib, epi(None, 1 << 20, 1e-6)) == 1           # gate without norm
+    assert _fwd_ex(lib, epi(1 << 20, None, 0.0)) == 1            # eps must be > 0
+    assert _fwd_ex(lib, epi(1 << 20, None, float("nan"))) == 1
+    assert _fwd_ex(lib, epi((1 << 20) + 4, None, 1e-6)) == 1     # weight 16-byte aligned
+    assert _fwd_ex(lib, epi(1 << 20, (1 << 20) + 8, 1e-6)) == 1  # out_gate 16-byte aligned
+    assert _fwd_ex(lib, epi(1 << 20, 1 << 20, 1e-6), wsb=16) == 1
 
 
 def test_decode_ex_rejects_bad_options_on_host(lib):

@@ -1,4 +1,4 @@
-"""Input-side fusion (kda_inputs; kda_fwd_chunked_ex, kda_decode_step_ex):
+"""Input-side fusion (kda_options; kda_fwd_chunked_ex, kda_decode_step_ex):
 parity of the fused calls with the fp64 oracle applied to the transformed
 inputs (oracle.prepare_inputs: gate function, q/k L2 normalisation, beta
 from logits), at the tolerances of the plain calls.
@@ -98,7 +98,7 @@ def test_fused_headline_raw_workload():
     """The B=2, H=8, T=2048 prefill in raw form (softplus gate), every output
     and final state, run stage by stage through kda_fwd_chunked_ex."""
     print("[fused] prefill_raw B=2 H=8 T=2048", flush=True)
-    w = kin.raw_prefill_workload()
+    w = kin.raw_prefill_workload(with_epilogue=False)
     o, s = _run_raw(w, stage_split=True)
     _check(w, o, s)
 
@@ -117,7 +117,7 @@ def test_ex_entry_without_options_is_the_plain_call():
     o1, s1 = kda.fwd_chunked(q, k, v, g, b, cu_seqlens=cu, chunk_size=32)
     call, _, o2, s2 = kda.bind_fwd(q, k, v, g, b, cu_seqlens=cu, chunk_size=32)
     args = call._args
-    opt = ctypes.pointer(kda.kda.KdaInputs(0, None, 0.0, 0, 0))
+    opt = ctypes.pointer(kda.kda.KdaOptions(0, None, 0.0, 0, 0))
     st = lib.kda_fwd_chunked_ex(opt, 3, *args)
     assert st == 0
     torch.cuda.synchronize()

@@ -111,3 +111,34 @@ def test_prepare_inputs_defaults_are_identity_and_normalised_keys_erase():
     _, S = oracle.recurrent(qn, kn, v, gn, bn, initial_state=S0)
     for h in range(H):
         np.testing.assert_allclose(S[0, h].T @ kn[-1, h], v[-1, h], rtol=0, atol=1e-6)
+
+
+def test_rms_norm_unit_rms_and_scale_invariance():
+    """[DS] "Les autres pieces": RMSNorm per head.  With unit weight the
+    normalised row has root-mean-square 1 (up to eps); it does not depend on
+    a positive scale of the row; the weight multiplies channel by channel;
+    (3, 4) has RMS sqrt(12.5)."""
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((5, 3, 32)) * 4
+    y = oracle.rms_norm(o, np.ones(32), 1e-12)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-10)
+    np.testing.assert_allclose(oracle.rms_norm(o * 7.5, np.ones(32), 0.0),
+                               oracle.rms_norm(o, np.ones(32), 0.0), rtol=1e-13)
+    w = rng.random(32)
+    np.testing.assert_allclose(oracle.rms_norm(o, w, 1e-6),
+                               oracle.rms_norm(o, np.ones(32), 1e-6) * w, rtol=1e-14)
+    np.testing.assert_allclose(oracle.rms_norm(np.array([3.0, 4.0]), np.ones(2), 0.0),
+                               np.array([3.0, 4.0]) / math.sqrt(12.5), rtol=1e-15)
+
+
+def test_output_gate_halves_at_zero_and_passes_at_large_logits():
+    """[DS]: the normalised output is multiplied by a sigmoid gate: a logit of
+    0 halves it, a large logit passes it, no gate leaves it unchanged."""
+    o = np.random.default_rng(7).standard_normal((4, 2, 16))
+    w = np.ones(16)
+    base = oracle.output_epilogue(o, w, 1e-6)
+    np.testing.assert_array_equal(base, oracle.rms_norm(o, w, 1e-6))
+    np.testing.assert_allclose(oracle.output_epilogue(o, w, 1e-6, np.zeros_like(o)),
+                               0.5 * base, rtol=1e-15)
+    np.testing.assert_allclose(oracle.output_epilogue(o, w, 1e-6, np.full_like(o, 60.0)),
+                               base, rtol=1e-15)
