@@ -88,14 +88,15 @@ def state_bytes(d):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "gated_delta_rule_chunked_amd", "csrc")
-KERNEL_SOURCES = {"intra": "kda_intra.hip", "inter": "kda_inter.hip",
-                  "decode_kernel": "kda_decode.hip"}
+KERNEL_SOURCES = {"intra": ("kda_intra.hip",), "inter": ("kda_inter.hip", "kda_epilogue.hip"),
+                  "decode_kernel": ("kda_decode.hip",)}
 
 
 def kernel_source_sha(kernel):
-    """sha256 over a kernel's source file and the headers it includes."""
+    """sha256 over the sources of a stage's kernels and the headers they
+    include (the inter stage runs the output epilogue pass when asked)."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "kda_common.hpp", "kda_internal.hpp"):
+    for f in KERNEL_SOURCES[kernel] + ("kda_common.hpp", "kda_internal.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
