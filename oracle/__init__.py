@@ -238,3 +238,60 @@ def output_epilogue(o, weight, eps, out_gate=None):
     if out_gate is not None:
         y = y * sigmoid(out_gate)
     return y
+
+
+# ---- backward (torch CPU, fp64) ---------------------------------------------
+# The gradient of the recurrence for training (fr.news.hada.io, section
+# "Algorithme parallele par chunks": the UT transform is there to use the
+# matrix units in training).  The forward is the definition written out token
+# by token in torch fp64 on the CPU (S' = Diag(alpha) S; u = beta (v - S'^T k);
+# S = S' + k u^T; o = S^T q), and torch's reverse-mode autograd takes its
+# gradient.  tests/test_oracle_backward.py pins it to central finite
+# differences and to closed forms.
+
+def _torch_recurrent(q, k, v, g, beta, bounds, s0):
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    outs = []
+    finals = []
+    for n, (a, b) in enumerate(bounds):
+        S = s0[n] if s0 is not None else torch.zeros((H, dk, dv), dtype=torch.float64)
+        for t in range(a, b):
+            Sp = torch.exp(g[t])[:, :, None] * S                          # [H, dk, dv]
+            u = beta[t][:, None] * (v[t] - torch.einsum("hkv,hk->hv", Sp, k[t]))
+            S = Sp + k[t][:, :, None] * u[:, None, :]
+            outs.append(torch.einsum("hkv,hk->hv", S, q[t]))
+        finals.append(S)
+    o = torch.stack(outs) if outs else torch.zeros((0, H, dv), dtype=torch.float64)
+    return o, torch.stack(finals)
+
+
+def recurrent_backward(q, k, v, g, beta, d_o, d_final_state=None, cu_seqlens=None,
+                       num_seqs=None, initial_state=None):
+    """Gradients of L = sum(o * d_o) + sum(S_final * d_final_state) with
+    respect to q, k, v, g, beta and the initial state.  Returns a dict with
+    keys dq, dk, dv, dg, dbeta, ds0 (ds0 is zero-filled when there is no
+    initial state, the gradient a zero initial state would get)."""
+    import torch
+    q = np.asarray(q, dtype=np.float64)
+    T, H, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    if cu_seqlens is not None:
+        c = [int(x) for x in cu_seqlens]
+        bounds = list(zip(c[:-1], c[1:]))
+    else:
+        n = 1 if num_seqs is None else int(num_seqs)
+        L = T // n
+        bounds = [(i * L, (i + 1) * L) for i in range(n)]
+    n = len(bounds)
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    tq, tk, tv, tg, tb = t(q), t(k), t(v), t(g), t(beta)
+    s0 = t(initial_state if initial_state is not None else np.zeros((n, H, dk, dv)))
+    o, sf = _torch_recurrent(tq, tk, tv, tg, tb, bounds, s0)
+    loss = (o * torch.tensor(np.asarray(d_o, dtype=np.float64))).sum()
+    if d_final_state is not None:
+        loss = loss + (sf * torch.tensor(np.asarray(d_final_state, dtype=np.float64))).sum()
+    loss.backward()
+    g_ = lambda x: x.grad.detach().numpy().copy() if x.grad is not None else np.zeros(x.shape)
+    return dict(dq=g_(tq), dk=g_(tk), dv=g_(tv), dg=g_(tg), dbeta=g_(tb), ds0=g_(s0))
