@@ -20,9 +20,10 @@ Also reported on the same JSON line:
                 states), the headline prefill in model-boundary form (input-side
                 fusion: softplus gate from bf16 z, q/k L2-normalised, beta
                 from logits; output epilogue: per-head RMSNorm and sigmoid
-                output gate) and recurrent decode (batch 256, H=32, 1000
-                steps) -- each with throughput, fraction of its roofline and,
-                for decode, the decode kernel's achieved HBM GB/s.
+                output gate), the backward of the headline prefill (training:
+                dq, dk, dv, dg, dbeta from d_o) and recurrent decode (batch 256,
+                H=32, 1000 steps) -- each with throughput, fraction of its
+                roofline and, for decode, the decode kernel's achieved HBM GB/s.
 Inputs come from gated_delta_rule_chunked_amd.inputs (seeded, synthetic).
 Only one GPU is supported: --gpus above 1 exits with an error.
 
@@ -82,6 +83,12 @@ def prefill_flops_per_token_head(d, C):
 
 def state_bytes(d):
     return 4 * d * d
+
+
+def backward_bytes_per_token_head(d, E):
+    """Read q, k, v, d_o (operand type), log-decay (fp32), beta; write dq, dk,
+    dv (operand type), dg (fp32), dbeta."""
+    return 4 * E * d + 4 * d + 4 + 3 * E * d + 4 * d + 4
 
 
 # ---------------------------------------------------------------- counters
@@ -258,6 +265,35 @@ def dominant_roofline(wname, w, res, d, E, C):
                 bytes_per_launch=b, avg_launch_us=ku[name])
 
 
+def time_backward(torch, kda, w, steps, warmup, d, E):
+    """Times `steps` kda_bwd_chunked calls on workload w with d_o ~ N(0, 1)."""
+    d_in = upload_prefill(torch, w)
+    do, _ = kin.backward_inputs(7, w.total_tokens, w.num_heads, d, w.num_seqs, w.dtype)
+    d_o = torch.from_numpy(np.ascontiguousarray(do).view(np.int16)).view(torch.bfloat16).cuda()
+    call, _ = kda.bind_bwd(d_in["q"], d_in["k"], d_in["v"], d_in["log_alpha"], d_in["beta"],
+                           d_o, cu_seqlens=d_in["cu_seqlens"], num_seqs=d_in["num_seqs"],
+                           initial_state=d_in["initial_state"], chunk_size=w.chunk_size)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    th = w.total_tokens * w.num_heads
+    byts = th * backward_bytes_per_token_head(d, E) + w.num_seqs * w.num_heads * state_bytes(d)
+    ach = byts / (ms * 1e-3) / 1e9
+    return dict(tokens_per_s=w.total_tokens / (ms * 1e-3), ms_per_step=ms,
+                algorithmic_bytes=byts, roofline_frac=ach / HBM_PEAK_GBS,
+                roofline=dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=ach / HBM_PEAK_GBS, traffic=None,
+                              kernel="kda_bwd_chunked (4 kernels)", bytes_per_launch=byts,
+                              avg_launch_us=ms * 1e3))
+
+
 # ---------------------------------------------------------------- decode
 
 def build_decode_inputs(torch, cfg, n_steps):
@@ -401,12 +437,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--extra", default="long,varlen,raw,decode",
-                    help="comma list of extra workloads (long, varlen, raw, decode) or 'none'")
+    ap.add_argument("--extra", default="long,varlen,raw,bwd,decode",
+                    help="comma list of extra workloads (long, varlen, raw, bwd, decode) or "
+                         "'none'")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["prefill", "long", "varlen", "raw", "decode", "copy"],
+    ap.add_argument("--only", choices=["prefill", "long", "varlen", "raw", "bwd", "decode",
+                                       "copy"],
                     help="run one workload only (profiling runs); its throughput is `value`. "
                          "'copy' times a plain 1 GiB device copy, the reference for the "
                          "memory-traffic counters")
@@ -478,6 +516,12 @@ def main():
             f"{workloads['prefill_fused']['ms_per_step'] * 1e3:.1f} us/step, kernels(us) "
             f"{json.dumps({k: round(v, 2) for k, v in r5['kernel_us'].items()})}")
         del w5
+    if "bwd" in extra:
+        log("backward of the headline prefill (B=2 H=8 T=2048)")
+        workloads["backward"] = time_backward(torch, kda, w1, min(args.steps, 20),
+                                              min(args.warmup, 3), d, E)
+        log(f"  {workloads['backward']['tokens_per_s'] / 1e6:.2f} M tokens/s, "
+            f"{workloads['backward']['ms_per_step'] * 1e3:.1f} us/step")
     torch.cuda.empty_cache()
     if "decode" in extra:
         cfg4 = kin.WORKLOADS[4]
@@ -500,11 +544,13 @@ def main():
         head = workloads["prefill"]
         value, unit, ms = head["tokens_per_s"], "tokens/s", head["ms_per_step"]
     else:  # a single extra workload (profiling runs)
-        name = {"raw": "prefill_fused"}.get(args.only, args.only)
+        name = {"raw": "prefill_fused", "bwd": "backward"}.get(args.only, args.only)
         head = workloads[name]
         roof = head["roofline"]
         if name == "decode":
             value, unit, ms = head["steps_per_s"], "steps/s", head["us_per_step"] * 1e-3
+        elif name == "backward":
+            value, unit, ms = head["tokens_per_s"], "tokens/s", head["ms_per_step"]
         else:
             value, unit, ms = head["tokens_per_s"], "tokens/s", head["ms_per_step"]
     line = {

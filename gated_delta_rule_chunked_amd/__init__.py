@@ -9,7 +9,8 @@ Submodules are loaded on first use so that ``gated_delta_rule_chunked_amd.inputs
 (the seeded input generators) can be imported without torch or the library.
 """
 _BINDING_NAMES = ("fwd_chunked", "decode_step", "workspace_size", "library",
-                  "KdaError", "library_path", "bind_fwd", "bind_decode")
+                  "KdaError", "library_path", "bind_fwd", "bind_decode", "bwd_chunked",
+                  "bind_bwd", "bwd_workspace_size")
 
 __all__ = list(_BINDING_NAMES)
 

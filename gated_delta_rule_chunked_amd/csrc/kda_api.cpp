@@ -210,6 +210,75 @@ kda_status kda_fwd_chunked_ex(const kda_options *options, uint32_t stages, const
                  workspace, workspace_bytes, stream);
 }
 
+size_t kda_bwd_chunked_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t d_k, int32_t d_v,
+                                      int32_t chunk_size, kda_dtype dtype) {
+  if (check_fwd_sizes(total_tokens, num_seqs, num_heads, d_k, d_v, chunk_size, dtype) !=
+      KDA_SUCCESS)
+    return 0;
+  return bwd_layout(total_tokens, num_seqs, num_heads, d_k, chunk_size).total;
+}
+
+kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const int32_t *cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                           int32_t d_v, int32_t chunk_size, kda_dtype dtype,
+                           const float *initial_state, const void *d_o,
+                           const float *d_final_state, void *dq, void *dk, void *dv,
+                           float *dlog_alpha, float *dbeta, float *d_initial_state,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  const kda_status st =
+      check_fwd_sizes(total_tokens, num_seqs, num_heads, d_k, d_v, chunk_size, dtype);
+  if (st != KDA_SUCCESS) return st;
+  if (total_tokens > 0) {
+    if (!q || !k || !v || !log_alpha || !beta || !d_o || !dq || !dk || !dv || !dlog_alpha ||
+        !dbeta)
+      return KDA_ERROR_INVALID_VALUE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(log_alpha, 16) ||
+        !aligned(dlog_alpha, 16) || !aligned(beta, 4) || !aligned(dbeta, 4))
+      return KDA_ERROR_INVALID_VALUE;
+  }
+  if (!cu_seqlens && (total_tokens % num_seqs) != 0) return KDA_ERROR_INVALID_VALUE;
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERROR_INVALID_VALUE;
+  if ((initial_state && !aligned(initial_state, 16)) ||
+      (d_final_state && !aligned(d_final_state, 16)) ||
+      (d_initial_state && !aligned(d_initial_state, 16)))
+    return KDA_ERROR_INVALID_VALUE;
+  const BwdLayout lay = bwd_layout(total_tokens, num_seqs, num_heads, d_k, chunk_size);
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total)
+    return KDA_ERROR_INVALID_VALUE;
+  BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.d_o = d_o;
+  a.g = log_alpha;
+  a.beta = beta;
+  a.s0 = initial_state;
+  a.dsf = d_final_state;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.d = d_k;
+  a.chunk = chunk_size;
+  a.seq_len = cu_seqlens ? 0 : (int)(total_tokens / num_seqs);
+  a.grid_chunks = cu_seqlens ? (total_tokens + (int64_t)num_seqs * (chunk_size - 1)) / chunk_size
+                             : (int64_t)num_seqs * ((a.seq_len + chunk_size - 1) / chunk_size);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dlog_alpha;
+  a.dbeta = dbeta;
+  a.ds0 = d_initial_state;
+  a.ws = reinterpret_cast<char *>(workspace);
+  a.lay = lay;
+  a.stream = reinterpret_cast<hipStream_t>(stream);
+  if (launch_bwd(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
+  return KDA_SUCCESS;
+}
+
 kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const float *log_alpha, const float *beta, float *state,
                            void *o, int32_t batch, int32_t num_heads, int32_t d_k,

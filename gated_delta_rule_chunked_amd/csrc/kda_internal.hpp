@@ -97,7 +97,67 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
+// Backward workspace (kda_bwd_chunked), fp32 throughout, per (chunk, head)
+// tile: the recomputed chunk factors (row-major [C][D] or [C][C]), the chunk
+// start state and the gradient of the state after the chunk ([D][D]), the
+// gradient of U - W S ([C][D]) and the per-tile scratch of the gradient
+// kernel; seq_first [num_seqs] as in the forward.
+struct BwdLayout {
+  int64_t tiles = 0;
+  int64_t scratch_per_tile = 0;  // floats
+  size_t seq_first = 0, kt = 0, kh = 0, qt = 0, ke = 0, w = 0, u = 0, vr = 0, gc = 0,
+         tm = 0, pm = 0, mm = 0, gam = 0, bt = 0, sc = 0, dse = 0, dun = 0, scratch = 0,
+         total = 0;
+};
+
+inline BwdLayout bwd_layout(int64_t T, int64_t N, int64_t H, int64_t D, int64_t C) {
+  BwdLayout L;
+  L.tiles = ((T + N * (C - 1)) / C) * H;
+  L.scratch_per_tile = 9 * C * D + 4 * C * C + D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  const size_t f = sizeof(float), t = (size_t)L.tiles;
+  L.seq_first = take(sizeof(int) * (size_t)N);
+  L.kt = take(f * t * C * D);
+  L.kh = take(f * t * C * D);
+  L.qt = take(f * t * C * D);
+  L.ke = take(f * t * C * D);
+  L.w = take(f * t * C * D);
+  L.u = take(f * t * C * D);
+  L.vr = take(f * t * C * D);
+  L.gc = take(f * t * C * D);
+  L.tm = take(f * t * C * C);
+  L.pm = take(f * t * C * C);
+  L.mm = take(f * t * C * C);
+  L.gam = take(f * t * D);
+  L.bt = take(f * t * C);
+  L.sc = take(f * t * D * D);
+  L.dse = take(f * t * D * D);
+  L.dun = take(f * t * C * D);
+  L.scratch = take(f * t * (size_t)L.scratch_per_tile);
+  L.total = off;
+  return L;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *d_o;
+  const float *g, *beta, *s0, *dsf;
+  const int *cu_seqlens;
+  int num_seqs, num_heads, d, chunk, seq_len;
+  int64_t grid_chunks;
+  void *dq, *dk, *dv;
+  float *dg, *dbeta, *ds0;
+  char *ws;
+  BwdLayout lay;
+  hipStream_t stream;
+};
+
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
+hipError_t launch_bwd(const BwdArgs &a, kda_dtype dt);
 hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
 // In place on o [rows, d]: o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(z).
 hipError_t launch_out_epilogue(void *o, const OptArgs &in, int64_t rows, int d,

@@ -47,62 +47,6 @@
 
 namespace kda {
 
-// Locates chunk id `c` among the sequences: s_loc = (sequence, first token,
-// rows), rows = 0 when c lies past the last chunk.  The workgroup of head 0
-// that owns the first chunk of a sequence records it in seq_first.
-__device__ void locate_chunk(int c, int h, const int *cu, int N, int seq_len, int C,
-                             int *s_loc, int *s_scan, int *seq_first) {
-  const int tid = threadIdx.x;
-  if (cu == nullptr) {
-    if (tid == 0) {
-      const int per = (seq_len + C - 1) / C;
-      const int s = c / per, i = c % per;
-      s_loc[0] = s;
-      s_loc[1] = s * seq_len + i * C;
-      s_loc[2] = (s < N) ? min(C, seq_len - i * C) : 0;
-      if (h == 0 && i == 0 && s < N) seq_first[s] = c;
-    }
-    __syncthreads();
-    return;
-  }
-  if (tid == 0) { s_loc[0] = 0; s_loc[1] = 0; s_loc[2] = 0; s_loc[3] = 0; }
-  int base = 0;
-  for (int s0 = 0; s0 < N; s0 += blockDim.x) {
-    const int s = s0 + tid;
-    int len = 0, start = 0;
-    if (s < N) {
-      start = cu[s];
-      len = cu[s + 1] - start;
-    }
-    const int nc = (len + C - 1) / C;
-    __syncthreads();
-    s_scan[tid] = nc;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-      const int add = (tid >= off) ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
-    }
-    const int incl = base + s_scan[tid];
-    const int excl = incl - nc;
-    if (s < N && nc > 0) {
-      if (c >= excl && c < incl) {
-        const int i = c - excl;
-        s_loc[0] = s;
-        s_loc[1] = start + i * C;
-        s_loc[2] = min(C, len - i * C);
-        s_loc[3] = 1;
-      }
-      if (h == 0 && c == excl) seq_first[s] = c;
-    }
-    base += s_scan[blockDim.x - 1];
-    __syncthreads();
-    if (s_loc[3]) break;
-  }
-  __syncthreads();
-}
-
 template <bool B>
 struct Flag {
   static constexpr bool value = B;

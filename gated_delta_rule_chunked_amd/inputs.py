@@ -356,3 +356,13 @@ def epilogue_inputs(seed, rows_shape, d: int, dtype: str):
     w = (1.0 + 0.2 * rng.standard_normal(d)).astype(np.float32)
     z = rng.standard_normal(tuple(rows_shape) + (d,))
     return w, _round_operand(z, dtype)
+
+
+def backward_inputs(seed, T: int, H: int, d: int, n: int, dtype: str):
+    """Gradients fed to the backward, from default_rng(seed) in this order:
+    d_o ~ N(0, 1) [T, H, d] rounded to the operand dtype, then the final-state
+    gradient ~ N(0, 0.1) [n, H, d, d] (fp32)."""
+    rng = np.random.default_rng(seed)
+    do = _round_operand(rng.standard_normal((T, H, d)), dtype)
+    dsf = rng.normal(0.0, 0.1, size=(n, H, d, d)).astype(np.float32)
+    return do, dsf

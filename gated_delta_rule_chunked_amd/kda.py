@@ -62,6 +62,12 @@ def library():
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                     ctypes.c_int, vp]
+    lib.kda_bwd_chunked_workspace_size.restype = sz
+    lib.kda_bwd_chunked_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
+    lib.kda_bwd_chunked.restype = ctypes.c_int
+    lib.kda_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
+                                    ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    sz, vp]
     pin = ctypes.POINTER(KdaOptions)
     lib.kda_fwd_chunked_ex.restype = ctypes.c_int
     lib.kda_fwd_chunked_ex.argtypes = [pin, ctypes.c_uint32] + lib.kda_fwd_chunked.argtypes
@@ -374,3 +380,63 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                           out_gate=out_gate, out_norm_eps=out_norm_eps)
     call()
     return o
+
+
+def bwd_workspace_size(total_tokens: int, num_seqs: int, num_heads: int, head_dim: int,
+                       chunk_size: int, dtype: torch.dtype) -> int:
+    """Bytes of workspace bwd_chunked needs (0 = unsupported sizes)."""
+    return int(library().kda_bwd_chunked_workspace_size(
+        total_tokens, num_seqs, num_heads, head_dim, head_dim, chunk_size,
+        _dtype_code(dtype)))
+
+
+def bind_bwd(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, num_seqs=None,
+             initial_state=None, d_final_state=None, chunk_size=64, want_d_initial=True,
+             workspace=None):
+    """Validate and marshal a kda_bwd_chunked call once.  Returns (call,
+    grads) with grads a dict of the output tensors dq, dk, dv (q's dtype),
+    dg, dbeta and ds0 (fp32; ds0 None unless want_d_initial)."""
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _need(t, name, q.dtype, (T, H, d))
+    _need(log_alpha, "log_alpha", torch.float32, (T, H, d))
+    _need(beta, "beta", torch.float32, (T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n = cu_seqlens.numel() - 1
+    else:
+        n = 1 if num_seqs is None else int(num_seqs)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _need(t, name, torch.float32, (n, H, d, d))
+    dev = q.device
+    grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                 dg=torch.empty_like(log_alpha), dbeta=torch.empty_like(beta),
+                 ds0=torch.empty((n, H, d, d), dtype=torch.float32, device=dev)
+                 if want_d_initial else None)
+    need = bwd_workspace_size(T, n, H, d, chunk_size, q.dtype)
+    if need == 0:
+        raise KdaError(f"unsupported sizes T={T} N={n} H={H} d={d} chunk={chunk_size}")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), n, T,
+            H, d, d, chunk_size, _dtype_code(q.dtype), _ptr(initial_state), _ptr(d_o),
+            _ptr(d_final_state), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]),
+            _ptr(grads["dg"]), _ptr(grads["dbeta"]), _ptr(grads["ds0"]), _ptr(workspace),
+            workspace.numel(), _stream(dev))
+    keep = (q, k, v, log_alpha, beta, d_o, cu_seqlens, initial_state, d_final_state,
+            workspace) + tuple(grads.values())
+    return BoundCall(library().kda_bwd_chunked, args, "kda_bwd_chunked", keep), grads
+
+
+def bwd_chunked(q, k, v, log_alpha, beta, d_o, cu_seqlens=None, num_seqs=None,
+                initial_state=None, d_final_state=None, chunk_size=64, want_d_initial=True):
+    """Gradients of the chunked prefill (kda_bwd_chunked) for the loss
+    sum(o * d_o) + sum(final_state * d_final_state).  Arguments as for
+    fwd_chunked; returns a dict dq, dk, dv, dg, dbeta, ds0."""
+    call, grads = bind_bwd(q, k, v, log_alpha, beta, d_o, cu_seqlens=cu_seqlens,
+                           num_seqs=num_seqs, initial_state=initial_state,
+                           d_final_state=d_final_state, chunk_size=chunk_size,
+                           want_d_initial=want_d_initial)
+    call()
+    return grads

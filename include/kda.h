@@ -272,6 +272,45 @@ kda_status kda_decode_step_ex(const kda_options *options, const void *q, const v
                               float *state, void *o, int32_t batch, int32_t num_heads,
                               int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream);
 
+/*
+ * ---- Backward (training) ----------------------------------------------------
+ * Gradients of the chunked prefill (fr.news.hada.io Kimi Linear summary,
+ * section "Algorithme parallele par chunks": the chunk form with the UT
+ * transform is what training runs), for the loss
+ *     L = sum(o * d_o) + sum(final_state * d_final_state).
+ * The chunk factors and the chunk start states are recomputed from the
+ * inputs; everything is evaluated in fp32.
+ *
+ *   q, k, v, log_alpha, beta, cu_seqlens, num_seqs, ..., initial_state:
+ *                 as for kda_fwd_chunked (same values as the forward call).
+ *   d_o           [total_tokens, H, d_v] dtype, the gradient of o.
+ *   d_final_state [num_seqs, H, d_k, d_v] fp32, or NULL for zero.
+ *   dq, dk        [total_tokens, H, d_k] dtype (outputs).
+ *   dv            [total_tokens, H, d_v] dtype (output).
+ *   dlog_alpha    [total_tokens, H, d_k] fp32 (output).
+ *   dbeta         [total_tokens, H] fp32 (output).
+ *   d_initial_state [num_seqs, H, d_k, d_v] fp32 (output), or NULL to skip.
+ *   workspace     at least kda_bwd_chunked_workspace_size() bytes, 256-byte
+ *                 aligned, clobbered (about 0.7 MiB per (chunk, head) tile
+ *                 for d = 128, C = 64).
+ * Alignment rules are those of kda_fwd_chunked (d_o, dq, dk, dv 16-byte;
+ * dlog_alpha 16-byte; dbeta 4-byte).  The decay precondition is the
+ * forward's.
+ */
+size_t kda_bwd_chunked_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                      int32_t num_heads, int32_t d_k, int32_t d_v,
+                                      int32_t chunk_size, kda_dtype dtype);
+
+kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const int32_t *cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                           int32_t d_v, int32_t chunk_size, kda_dtype dtype,
+                           const float *initial_state, const void *d_o,
+                           const float *d_final_state, void *dq, void *dk, void *dv,
+                           float *dlog_alpha, float *dbeta, float *d_initial_state,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

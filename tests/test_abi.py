@@ -195,3 +195,27 @@ def test_decode_ex_rejects_bad_options_on_host(lib):
     assert dec_ex(_opts(gate=2, gmin=1.0)) == 1
     assert dec_ex(_opts(gate=2, gmin=-5.0), st=None) == 1
     assert dec_ex(_opts(gate=1, A=1 << 20), dk=48, dv=48) == 2
+
+
+def test_bwd_rejects_bad_arguments_on_host(lib):
+    """kda_bwd_chunked validates before anything is enqueued (every case below
+    fails validation)."""
+    def bwd(**over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=None, n=2, T=256, H=2, dk=64,
+                 dv=64, C=64, dt=1, s0=None, do=FAKE, dsf=None, dq=FAKE, dk_=FAKE, dv_=FAKE,
+                 dg=FAKE, db=FAKE, ds0=None, ws=FAKE, wsb=16, stream=None)
+        a.update(over)
+        return lib.kda_bwd_chunked(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["n"],
+                                   a["T"], a["H"], a["dk"], a["dv"], a["C"], a["dt"], a["s0"],
+                                   a["do"], a["dsf"], a["dq"], a["dk_"], a["dv_"], a["dg"],
+                                   a["db"], a["ds0"], a["ws"], a["wsb"], a["stream"])
+    assert bwd() == 1                                   # workspace too small
+    assert bwd(do=None) == 1
+    assert bwd(dq=None) == 1
+    assert bwd(db=ctypes.c_void_p((1 << 20) + 2)) == 1
+    assert bwd(dsf=ctypes.c_void_p((1 << 20) + 4)) == 1
+    assert bwd(dk=96, dv=96) == 2
+    assert bwd(C=128) == 2
+    assert bwd(T=255) == 1
+    assert lib.kda_bwd_chunked_workspace_size(4096, 2, 8, 128, 128, 64, 1) > 0
+    assert lib.kda_bwd_chunked_workspace_size(4096, 2, 8, 96, 96, 64, 1) == 0

@@ -1,0 +1,73 @@
+"""Backward (kda_bwd_chunked) against the fp64 autograd oracle
+(oracle.recurrent_backward), every gradient normwise at the operator's
+tolerances.
+
+fr.news.hada.io Kimi Linear summary, section "Algorithme parallele par
+chunks" (the chunk form is what training runs).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+import oracle  # noqa: E402
+from gated_delta_rule_chunked_amd import inputs as kin  # noqa: E402
+from kda_testutil import TOL, from_device, relerr, to_device, f32_device, upload_prefill  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _kda():
+    import gated_delta_rule_chunked_amd as kda
+    return kda
+
+
+def _run(w, do, dsf, chunk):
+    kda = _kda()
+    dd = upload_prefill(w)
+    gr = kda.bwd_chunked(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
+                         to_device(do, w.dtype), cu_seqlens=dd["cu_seqlens"],
+                         num_seqs=dd["num_seqs"], initial_state=dd["initial_state"],
+                         d_final_state=None if dsf is None else f32_device(dsf),
+                         chunk_size=chunk)
+    torch.cuda.synchronize()
+    return {k: from_device(v) for k, v in gr.items()}
+
+
+def _check(w, do, dsf, got):
+    q, k, v, g, b, s0 = w.f64()
+    cu = None if w.cu_seqlens is None else w.cu_seqlens.astype(np.int64)
+    ref = oracle.recurrent_backward(q, k, v, g, b, kin.as_f64(do, w.dtype), dsf,
+                                    cu_seqlens=cu, num_seqs=w.num_seqs, initial_state=s0)
+    tol = TOL[w.dtype]
+    errs = {key: relerr(got[key], ref[key]) for key in ("dq", "dk", "dv", "dg", "dbeta", "ds0")}
+    print("  relerr " + " ".join(f"{k}={e:.2e}" for k, e in errs.items()), flush=True)
+    for key, e in errs.items():
+        assert e <= tol, f"{key} error {e:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [(kin.BF16, 128, 64), (kin.BF16, 64, 32),
+                                           (kin.BF16, 32, 16), (kin.F32, 32, 16),
+                                           (kin.F32, 64, 64)])
+def test_backward_ragged(dtype, d, chunk):
+    """Packed sequences with tails, an empty and a one-token sequence,
+    initial states and a final-state gradient."""
+    print(f"[backward] dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill(500 + d + chunk, H=2, d=d, dtype=dtype, chunk_size=chunk,
+                         lengths=[70, 0, 1, 33], s0_std=0.05)
+    do, dsf = kin.backward_inputs(501 + d, w.total_tokens, 2, d, w.num_seqs, dtype)
+    _check(w, do, dsf, _run(w, do, dsf, chunk))
+
+
+def test_backward_equal_lengths_no_final_gradient():
+    """B=2 sequences of 256 tokens, H=2, d=128, C=64, zero initial state and no
+    final-state gradient (the default loss sum(o * d_o))."""
+    print("[backward] B=2 T=256 d=128", flush=True)
+    w = kin.make_prefill(77, B=2, T=256, H=2, d=128, dtype=kin.BF16, chunk_size=64)
+    do, _ = kin.backward_inputs(78, w.total_tokens, 2, 128, 2, kin.BF16)
+    _check(w, do, None, _run(w, do, None, 64))
