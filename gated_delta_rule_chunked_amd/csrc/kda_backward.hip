@@ -32,8 +32,10 @@
 //   bwd_grad_kernel   per (chunk, head): dq, dk, dv, dg, dbeta
 // The state columns never mix (in the forward and in dS), which is what makes
 // the column slices of the two chains exact.  Rows past a chunk's end are
-// zero (beta = 0, q = k = v = 0, dO = 0) and contribute nothing.  Products are
-// plain fp32 loops over L2-resident tiles.
+// zero (beta = 0, q = k = v = 0, dO = 0) and contribute nothing.  Products run
+// through block_mm: K slices of both operands are staged in LDS with
+// coalesced loads and every thread accumulates a register block of the
+// output in fp32.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -41,21 +43,76 @@ namespace kda {
 
 namespace {
 
-// out[i][j] (+)= alpha * sum_k A(i, k) B(k, j) for i < M, j < N, with
-// A(i, k) = TA ? A[k][i] : A[i][k] and B(k, j) = TB ? B[j][k] : B[k][j]
-// (row-major, leading dimensions given).  Every thread of the block takes
-// output elements in turn; callers separate dependent products with
-// __syncthreads().
+constexpr int KS = 16;  // contraction slice staged in LDS
+
+// out[i][j] = alpha * sum_k A(i, k) B(k, j) (+ out[i][j] when acc) for
+// i < M, j < N, with A(i, k) = TA ? A[k][i] : A[i][k] and
+// B(k, j) = TB ? B[j][k] : B[k][j] (row-major, leading dimensions given).
+// M, N, K are multiples of 16 and M, N <= 128; out may be global memory or
+// LDS and must not alias A or B.  256 threads: thread (ty, tx) = (tid / 16,
+// tid % 16) owns rows ty + 16 a and columns tx + 16 b.  `lds` holds
+// 2 * KS * 128 floats.  Ends with a barrier, so the block may use `out` right
+// after.
 template <bool TA, bool TB>
-__device__ void bgemm(float *out, int ldo, const float *A, int lda, const float *B, int ldb,
-                      int M, int N, int K, float alpha, bool acc) {
-  for (int e = threadIdx.x; e < M * N; e += blockDim.x) {
-    const int i = e / N, j = e % N;
-    float s = 0.f;
-    for (int kk = 0; kk < K; ++kk)
-      s += (TA ? A[kk * lda + i] : A[i * lda + kk]) * (TB ? B[j * ldb + kk] : B[kk * ldb + j]);
-    out[i * ldo + j] = alpha * s + (acc ? out[i * ldo + j] : 0.f);
+__device__ void block_mm(float *out, int ldo, const float *A, int lda, const float *B, int ldb,
+                         int M, int N, int K, float alpha, bool acc, float *lds) {
+  float *sa = lds, *sb = lds + KS * 128;  // sa[kk][i], sb[kk][j]
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int ma = M / 16, nb = N / 16;
+  float c[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) c[a][b] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += KS) {
+    for (int e = tid; e < M * KS; e += 256) {
+      int i, kk;
+      if (TA) { kk = e / M; i = e % M; } else { i = e / KS; kk = e % KS; }
+      sa[kk * M + i] = TA ? A[(k0 + kk) * lda + i] : A[i * lda + k0 + kk];
+    }
+    for (int e = tid; e < N * KS; e += 256) {
+      int j, kk;
+      if (TB) { j = e / KS; kk = e % KS; } else { kk = e / N; j = e % N; }
+      sb[kk * N + j] = TB ? B[j * ldb + k0 + kk] : B[(k0 + kk) * ldb + j];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < KS; ++kk) {
+      float av[8], bv[8];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) av[a] = a < ma ? sa[kk * M + ty + 16 * a] : 0.f;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) bv[b] = b < nb ? sb[kk * N + tx + 16 * b] : 0.f;
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) c[a][b] += av[a] * bv[b];
+    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      if (a < ma && b < nb) {
+        float *o = out + (ty + 16 * a) * ldo + tx + 16 * b;
+        *o = alpha * c[a][b] + (acc ? *o : 0.f);
+      }
+  __syncthreads();
+}
+
+// out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
+// length L (leading dimension ld), one wavefront per row.
+__device__ void row_dots(float *out, const float *X, const float *Y, int ld, int R, int L,
+                         bool acc) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int r = wv; r < R; r += 4) {
+    float s = 0.f;
+    for (int j = lane; j < L; j += 64) s += X[r * ld + j] * Y[r * ld + j];
+    s = group_sum<64>(s);
+    if (lane == 0) out[r] = s + (acc ? out[r] : 0.f);
+  }
+  __syncthreads();
 }
 
 struct TilePtr {
@@ -107,6 +164,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     int N, int H, int seq_len, int C, int D, BwdLayout L, char *ws) {
   __shared__ int s_loc[4];
   __shared__ int s_scan[256];
+  __shared__ float s_mm[2 * KS * 128];
+  __shared__ float s_a[64 * 65];  // A = strict_lower(beta M), for the substitution
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -114,6 +173,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+  float *bkt = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
+  float *bvv = bkt + (int64_t)C * D;  // Diag(beta) Kt and Diag(beta) V (scratch)
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
   // cumulative log-decay per channel (rows past the end add nothing)
@@ -139,55 +200,75 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     p.qt[e] = qv * __expf(G);
     p.ke[e] = kv * __expf(Gn - G);
     p.vr[e] = vv;
+    bkt[e] = p.bt[r] * kv * __expf(G);
+    bvv[e] = p.bt[r] * vv;
   }
   __syncthreads();
-  bgemm<false, true>(p.mm, C, p.kt, D, p.kh, D, C, C, D, 1.f, false);  // M = Kt Kh^T
-  bgemm<false, true>(p.pm, C, p.qt, D, p.kh, D, C, C, D, 1.f, false);  // Qt Kh^T
-  __syncthreads();
+  block_mm<false, true>(p.mm, C, p.kt, D, p.kh, D, C, C, D, 1.f, false, s_mm);  // M = Kt Kh^T
+  block_mm<false, true>(p.pm, C, p.qt, D, p.kh, D, C, C, D, 1.f, false, s_mm);  // Qt Kh^T
   for (int e = tid; e < C * C; e += blockDim.x) {
     const int r = e / C, s = e % C;
     if (s > r) p.pm[e] = 0.f;  // P = lower incl. diagonal
+    s_a[r * 65 + s] = s < r ? p.bt[r] * p.mm[e] : 0.f;
   }
-  // T = (I + A)^-1, A = strict_lower(beta_r M_rs): column j by thread j,
-  // forward substitution row by row
+  __syncthreads();
+  // T = (I + A)^-1: column j by thread j, forward substitution row by row
   for (int j = tid; j < C; j += blockDim.x) {
+    float tcol[64];
+#pragma unroll
+    for (int r = 0; r < 64; ++r) tcol[r] = 0.f;
     for (int r = 0; r < C; ++r) {
-      float t;
-      if (r < j) {
-        t = 0.f;
-      } else if (r == j) {
-        t = 1.f;
-      } else {
+      float t = r == j ? 1.f : 0.f;
+      if (r > j) {
         float s = 0.f;
-        for (int m = j; m < r; ++m) s += p.bt[r] * p.mm[r * C + m] * p.tm[m * C + j];
+        for (int m = j; m < r; ++m) s += s_a[r * 65 + m] * tcol[m];
         t = -s;
       }
+      tcol[r] = t;
       p.tm[r * C + j] = t;
     }
   }
   __syncthreads();
-  // W = T Diag(beta) Kt, U = T Diag(beta) V
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, i = e % D;
-    float sw = 0.f, su = 0.f;
-    for (int m = 0; m <= r; ++m) {
-      const float tb = p.tm[r * C + m] * p.bt[m];
-      sw += tb * p.kt[m * D + i];
-      su += tb * p.vr[m * D + i];
-    }
-    p.w[e] = sw;
-    p.u[e] = su;
+  block_mm<false, false>(p.w, D, p.tm, C, bkt, D, C, D, C, 1.f, false, s_mm);  // W = T (beta Kt)
+  block_mm<false, false>(p.u, D, p.tm, C, bvv, D, C, D, C, 1.f, false, s_mm);  // U = T (beta V)
+}
+
+// ---- chain helpers ----------------------------------------------------------
+// A chunk's [rows][cols] fp32 matrix, cols % 4 == 0, moved as float4 through
+// registers (rows * cols / 1024 float4 per thread; at most 8 here) into LDS
+// rows of stride cols + 4.
+struct Stage8 {
+  f32x4 r[8];
+};
+
+__device__ void stage_load(Stage8 &st, const float *src, int rows, int cols) {
+  const int n4 = rows * cols / 4;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int e = threadIdx.x + 256 * m;
+    if (e < n4) st.r[m] = reinterpret_cast<const f32x4 *>(src)[e];
+  }
+}
+
+__device__ void stage_store(const Stage8 &st, float *dst, int rows, int cols) {
+  const int n4 = rows * cols / 4, c4 = cols / 4;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int e = threadIdx.x + 256 * m;
+    if (e < n4) *reinterpret_cast<f32x4 *>(dst + (e / c4) * (cols + 4) + 4 * (e % c4)) = st.r[m];
   }
 }
 
 // ---- 2. chunk start states ------------------------------------------------
-// One block per (sequence, head, 16-column slice); the slice of S lives in LDS.
+// One block per (sequence, head, 16-column slice); the slice of S lives in LDS
+// and each chunk's W and Ke are staged whole in LDS, the next chunk's being
+// loaded into registers while this one is computed.
 __global__ __launch_bounds__(256) void bwd_state_kernel(
     const int *__restrict__ cu, int N, int H, int seq_len, int C, int D,
     const float *__restrict__ s0, BwdLayout L, char *ws) {
-  __shared__ float sS[128 * 16];
-  __shared__ float sU[64 * 16];
-  const int NS = D / 16;
+  extern __shared__ __align__(16) float sm[];
+  const int NS = D / 16, LD = D + 4;
+  float *sW = sm, *sK = sW + C * LD, *sS = sK + C * LD, *sU = sS + D * 16, *sG = sU + C * 16;
   const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
   const int seq = pair / H, h = pair % H;
   if (seq >= N) return;
@@ -199,29 +280,41 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(
     const int i = e / 16, j = e % 16;
     sS[e] = s0 ? s0[((int64_t)pair * D + i) * D + col0 + j] : 0.f;
   }
-  __syncthreads();
+  Stage8 rw, rk;
+  if (nch > 0) {
+    const TilePtr p = tile_ptrs(L, ws, (int64_t)first * H + h, C, D);
+    stage_load(rw, p.w, C, D);
+    stage_load(rk, p.ke, C, D);
+  }
   for (int ci = 0; ci < nch; ++ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
     const TilePtr p = tile_ptrs(L, ws, tile, C, D);
     float *sc = reinterpret_cast<float *>(ws + L.sc) + tile * D * D;
-    for (int e = tid; e < D * 16; e += blockDim.x) {
-      const int i = e / 16, j = e % 16;
-      sc[i * D + col0 + j] = sS[e];
+    __syncthreads();  // the previous chunk is done with sW, sK, sU
+    stage_store(rw, sW, C, D);
+    stage_store(rk, sK, C, D);
+    for (int e = tid; e < C * 16; e += blockDim.x) sU[e] = p.u[(e / 16) * D + col0 + e % 16];
+    for (int i = tid; i < D; i += blockDim.x) sG[i] = p.gam[i];
+    for (int e = tid; e < D * 16; e += blockDim.x) sc[(e / 16) * D + col0 + e % 16] = sS[e];
+    __syncthreads();
+    if (ci + 1 < nch) {
+      const TilePtr pn = tile_ptrs(L, ws, tile + H, C, D);
+      stage_load(rw, pn.w, C, D);
+      stage_load(rk, pn.ke, C, D);
     }
     for (int e = tid; e < C * 16; e += blockDim.x) {  // Unew = U - W S
       const int r = e / 16, j = e % 16;
-      float s = p.u[r * D + col0 + j];
-      for (int i = 0; i < D; ++i) s -= p.w[r * D + i] * sS[i * 16 + j];
-      sU[e] = s;
+      float acc = sU[e];
+      for (int i = 0; i < D; ++i) acc -= sW[r * LD + i] * sS[i * 16 + j];
+      sU[e] = acc;
     }
     __syncthreads();
     for (int e = tid; e < D * 16; e += blockDim.x) {  // S = Diag(gam) S + Ke^T Unew
       const int i = e / 16, j = e % 16;
-      float s = p.gam[i] * sS[e];
-      for (int r = 0; r < C; ++r) s += p.ke[r * D + i] * sU[r * 16 + j];
-      sS[e] = s;
+      float acc = sG[i] * sS[e];
+      for (int r = 0; r < C; ++r) acc += sK[r * LD + i] * sU[r * 16 + j];
+      sS[e] = acc;
     }
-    __syncthreads();
   }
 }
 
@@ -230,10 +323,10 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_dstate_kernel(
     const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len, int C,
     int D, const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
-  __shared__ float sD[128 * 16];
-  __shared__ float sO[64 * 16];
-  __shared__ float sU[64 * 16];
-  const int NS = D / 16;
+  extern __shared__ __align__(16) float sm[];
+  const int NS = D / 16, LD = D + 4, LP = C + 4;
+  float *sW = sm, *sK = sW + C * LD, *sQ = sK + C * LD, *sP = sQ + C * LD;
+  float *sD = sP + C * LP, *sO = sD + D * 16, *sU = sO + C * 16, *sG = sU + C * 16;
   const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
   const int seq = pair / H, h = pair % H;
   if (seq >= N) return;
@@ -247,39 +340,56 @@ __global__ __launch_bounds__(256) void bwd_dstate_kernel(
     const int i = e / 16, j = e % 16;
     sD[e] = dsf ? dsf[((int64_t)pair * D + i) * D + col0 + j] : 0.f;
   }
-  __syncthreads();
+  Stage8 rw, rk, rq, rp;
+  if (nch > 0) {
+    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + nch - 1) * H + h, C, D);
+    stage_load(rw, p.w, C, D);
+    stage_load(rk, p.ke, C, D);
+    stage_load(rq, p.qt, C, D);
+    stage_load(rp, p.pm, C, C);
+  }
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
     const TilePtr p = tile_ptrs(L, ws, tile, C, D);
     float *dse = reinterpret_cast<float *>(ws + L.dse) + tile * D * D;
     float *dun = reinterpret_cast<float *>(ws + L.dun) + tile * C * D;
     const int t0 = t_seq + ci * C, n = min(C, len - ci * C);
-    for (int e = tid; e < D * 16; e += blockDim.x) {
-      const int i = e / 16, j = e % 16;
-      dse[i * D + col0 + j] = sD[e];
-    }
+    __syncthreads();  // the previous chunk is done with the staged operands
+    stage_store(rw, sW, C, D);
+    stage_store(rk, sK, C, D);
+    stage_store(rq, sQ, C, D);
+    stage_store(rp, sP, C, C);
+    for (int i = tid; i < D; i += blockDim.x) sG[i] = p.gam[i];
+    for (int e = tid; e < D * 16; e += blockDim.x) dse[(e / 16) * D + col0 + e % 16] = sD[e];
     for (int e = tid; e < C * 16; e += blockDim.x) {
       const int r = e / 16, j = e % 16;
       sO[e] = r < n ? to_f32(d_o[(int64_t)(t0 + r) * rs + (int64_t)h * D + col0 + j]) : 0.f;
     }
     __syncthreads();
+    if (ci > 0) {
+      const TilePtr pn = tile_ptrs(L, ws, tile - H, C, D);
+      stage_load(rw, pn.w, C, D);
+      stage_load(rk, pn.ke, C, D);
+      stage_load(rq, pn.qt, C, D);
+      stage_load(rp, pn.pm, C, C);
+    }
     for (int e = tid; e < C * 16; e += blockDim.x) {  // dUnew = P^T dO + Ke dS
       const int r = e / 16, j = e % 16;
-      float s = 0.f;
-      for (int m = 0; m < C; ++m) s += p.pm[m * C + r] * sO[m * 16 + j];
-      for (int i = 0; i < D; ++i) s += p.ke[r * D + i] * sD[i * 16 + j];
-      sU[e] = s;
-      dun[r * D + col0 + j] = s;
+      float acc = 0.f;
+      for (int m = 0; m < C; ++m) acc += sP[m * LP + r] * sO[m * 16 + j];
+      for (int i = 0; i < D; ++i) acc += sK[r * LD + i] * sD[i * 16 + j];
+      sU[e] = acc;
+      dun[r * D + col0 + j] = acc;
     }
     __syncthreads();
     for (int e = tid; e < D * 16; e += blockDim.x) {  // dS = gam dS + Qt^T dO - W^T dUnew
       const int i = e / 16, j = e % 16;
-      float s = p.gam[i] * sD[e];
-      for (int r = 0; r < C; ++r) s += p.qt[r * D + i] * sO[r * 16 + j] - p.w[r * D + i] * sU[r * 16 + j];
-      sD[e] = s;
+      float acc = sG[i] * sD[e];
+      for (int r = 0; r < C; ++r) acc += sQ[r * LD + i] * sO[r * 16 + j] - sW[r * LD + i] * sU[r * 16 + j];
+      sD[e] = acc;
     }
-    __syncthreads();
   }
+  __syncthreads();
   if (ds0) {
     for (int e = tid; e < D * 16; e += blockDim.x) {
       const int i = e / 16, j = e % 16;
@@ -296,6 +406,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
   __shared__ int s_loc[4];
   __shared__ int s_scan[256];
+  __shared__ float s_mm[2 * KS * 128];
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -317,59 +428,46 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   for (int e = tid; e < C * D; e += blockDim.x) {
     const int r = e / D, i = e % D;
     dot[e] = r < n ? to_f32(d_o[(int64_t)(t0 + r) * rs + (int64_t)h * D + i]) : 0.f;
-  }
-  // Unew = U - W S
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, j = e % D;
-    float s = p.u[e];
-    for (int i = 0; i < D; ++i) s -= p.w[r * D + i] * sc[i * D + j];
-    unew[e] = s;
-  }
-  for (int i = tid; i < D; i += blockDim.x) {  // dgam = rowsum(dS_next * S)
-    float s = 0.f;
-    for (int j = 0; j < D; ++j) s += dse[i * D + j] * sc[i * D + j];
-    dgam[i] = s;
+    unew[e] = p.u[e];
   }
   __syncthreads();
-  bgemm<false, true>(dp, C, dot, D, unew, D, C, C, D, 1.f, false);       // dO Unew^T
-  bgemm<false, true>(dqt, D, dot, D, sc, D, C, D, D, 1.f, false);        // dO S^T
-  bgemm<false, true>(dke, D, unew, D, dse, D, C, D, D, 1.f, false);      // Unew dS_next^T
-  bgemm<false, true>(dw, D, dun, D, sc, D, C, D, D, -1.f, false);        // -dUnew S^T
-  __syncthreads();
+  block_mm<false, false>(unew, D, p.w, D, sc, D, C, D, D, -1.f, true, s_mm);  // U - W S
+  row_dots(dgam, dse, sc, D, D, D, false);                                    // rowsum(dS_next * S)
+  block_mm<false, true>(dp, C, dot, D, unew, D, C, C, D, 1.f, false, s_mm);   // dO Unew^T
+  block_mm<false, true>(dqt, D, dot, D, sc, D, C, D, D, 1.f, false, s_mm);    // dO S^T
+  block_mm<false, true>(dke, D, unew, D, dse, D, C, D, D, 1.f, false, s_mm);  // Unew dS_next^T
+  block_mm<false, true>(dw, D, dun, D, sc, D, C, D, D, -1.f, false, s_mm);    // -dUnew S^T
   for (int e = tid; e < C * C; e += blockDim.x)
     if (e % C > e / C) dp[e] = 0.f;  // dP lower incl. diagonal
   __syncthreads();
-  bgemm<false, false>(dqt, D, dp, C, p.kh, D, C, D, C, 1.f, true);       // + dP Kh
-  // dT = dW (beta Kt)^T + dUnew (beta V)^T
-  for (int e = tid; e < C * C; e += blockDim.x) {
-    const int r = e / C, s = e % C;
-    float a = 0.f;
-    for (int i = 0; i < D; ++i) a += dw[r * D + i] * p.kt[s * D + i] + dun[r * D + i] * p.vr[s * D + i];
-    dt[e] = p.bt[s] * a;
-  }
-  bgemm<true, false>(dbkt, D, p.tm, C, dw, D, C, D, C, 1.f, false);      // T^T dW
-  bgemm<true, false>(dbv, D, p.tm, C, dun, D, C, D, C, 1.f, false);      // T^T dUnew
+  block_mm<false, false>(dqt, D, dp, C, p.kh, D, C, D, C, 1.f, true, s_mm);   // + dP Kh
+  // dT = (dW Kt^T + dUnew V^T) Diag(beta)
+  block_mm<false, true>(dt, C, dw, D, p.kt, D, C, C, D, 1.f, false, s_mm);
+  block_mm<false, true>(dt, C, dun, D, p.vr, D, C, C, D, 1.f, true, s_mm);
+  for (int e = tid; e < C * C; e += blockDim.x) dt[e] *= p.bt[e % C];
   __syncthreads();
-  bgemm<true, false>(xm, C, p.tm, C, dt, C, C, C, C, 1.f, false);        // T^T dT
-  __syncthreads();
-  bgemm<false, true>(da, C, xm, C, p.tm, C, C, C, C, -1.f, false);       // -T^T dT T^T
-  __syncthreads();
+  block_mm<true, false>(dbkt, D, p.tm, C, dw, D, C, D, C, 1.f, false, s_mm);  // T^T dW
+  block_mm<true, false>(dbv, D, p.tm, C, dun, D, C, D, C, 1.f, false, s_mm);  // T^T dUnew
+  block_mm<true, false>(xm, C, p.tm, C, dt, C, C, C, C, 1.f, false, s_mm);    // T^T dT
+  block_mm<false, true>(da, C, xm, C, p.tm, C, C, C, C, -1.f, false, s_mm);   // -T^T dT T^T
   for (int e = tid; e < C * C; e += blockDim.x) {
     const int r = e / C, s = e % C;
     if (s >= r) da[e] = 0.f;  // strictly lower
   }
   __syncthreads();
-  // dKt = beta dBKt + dM Kh, dKh = dM^T Kt + dP^T Qt, dM = Diag(beta) dA
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, i = e % D;
-    float a = 0.f, b = 0.f;
-    for (int s = 0; s < C; ++s) {
-      a += p.bt[r] * da[r * C + s] * p.kh[s * D + i];
-      b += p.bt[s] * da[s * C + r] * p.kt[s * D + i] + dp[s * C + r] * p.qt[s * D + i];
-    }
-    dkt[e] = p.bt[r] * dbkt[e] + a;
-    dkh[e] = b;
-  }
+  // dbeta = rowsum(dA * M) + rowsum(dBKt * Kt) + rowsum(dBV * V), before dA
+  // is scaled into dM below
+  float *dbr = xm;  // [C], xm is free now
+  row_dots(dbr, da, p.mm, C, C, C, false);
+  row_dots(dbr, dbkt, p.kt, D, C, D, true);
+  row_dots(dbr, dbv, p.vr, D, C, D, true);
+  for (int e = tid; e < C * C; e += blockDim.x) da[e] *= p.bt[e / C];  // dM = Diag(beta) dA
+  __syncthreads();
+  // dKt = Diag(beta) dBKt + dM Kh; dKh = dM^T Kt + dP^T Qt
+  block_mm<false, false>(dkt, D, da, C, p.kh, D, C, D, C, 1.f, false, s_mm);
+  block_mm<true, false>(dkh, D, da, C, p.kt, D, C, D, C, 1.f, false, s_mm);
+  block_mm<true, false>(dkh, D, dp, C, p.qt, D, C, D, C, 1.f, true, s_mm);
+  for (int e = tid; e < C * D; e += blockDim.x) dkt[e] += p.bt[e / D] * dbkt[e];
   __syncthreads();
   // outputs per row: dq, dk, dv, dbeta
   for (int e = tid; e < C * D; e += blockDim.x) {
@@ -381,12 +479,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
     dk[at] = from_f32<T>(dkt[e] * __expf(G) + dkh[e] * __expf(-G) + dke[e] * __expf(Gn - G));
     dv[at] = from_f32<T>(p.bt[r] * dbv[e]);
   }
-  for (int r = tid; r < n; r += blockDim.x) {
-    float s = 0.f;
-    for (int m = 0; m < C; ++m) s += da[r * C + m] * p.mm[r * C + m];
-    for (int i = 0; i < D; ++i) s += dbkt[r * D + i] * p.kt[r * D + i] + dbv[r * D + i] * p.vr[r * D + i];
-    dbeta[(int64_t)(t0 + r) * H + h] = s;
-  }
+  for (int r = tid; r < n; r += blockDim.x) dbeta[(int64_t)(t0 + r) * H + h] = dbr[r];
   // dg: reverse cumulative sum of dG over the chunk plus dG_n, per channel
   for (int i = tid; i < D; i += blockDim.x) {
     float dgn = dgam[i] * p.gam[i];
@@ -410,9 +503,23 @@ static hipError_t launch_bwd_t(const BwdArgs &a) {
     hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(tiles), dim3(256), 0, a.stream, q, k, v, a.g,
                        a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d,
                        a.lay, a.ws);
-  hipLaunchKernelGGL(bwd_state_kernel, dim3(slices), dim3(256), 0, a.stream, a.cu_seqlens,
-                     a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d, a.s0, a.lay, a.ws);
-  hipLaunchKernelGGL(bwd_dstate_kernel<T>, dim3(slices), dim3(256), 0, a.stream, d_o,
+  const int C = a.chunk, D = a.d;
+  const size_t lds_state = sizeof(float) * (2 * C * (D + 4) + D * 16 + C * 16 + D);
+  const size_t lds_dstate =
+      sizeof(float) * (3 * C * (D + 4) + C * (C + 4) + D * 16 + 2 * C * 16 + D);
+  // the largest shapes (d = 128, C = 64): 80,384 and 135,680 bytes
+  static const hipError_t a1 = hipFuncSetAttribute(
+      (const void *)bwd_state_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(sizeof(float) * (2 * 64 * 132 + 128 * 16 + 64 * 16 + 128)));
+  static const hipError_t a2 = hipFuncSetAttribute(
+      (const void *)bwd_dstate_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(sizeof(float) * (3 * 64 * 132 + 64 * 68 + 128 * 16 + 2 * 64 * 16 + 128)));
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+  hipLaunchKernelGGL(bwd_state_kernel, dim3(slices), dim3(256), lds_state, a.stream,
+                     a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d, a.s0,
+                     a.lay, a.ws);
+  hipLaunchKernelGGL(bwd_dstate_kernel<T>, dim3(slices), dim3(256), lds_dstate, a.stream, d_o,
                      a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d, a.dsf,
                      a.ds0, a.lay, a.ws);
   if (tiles > 0)
