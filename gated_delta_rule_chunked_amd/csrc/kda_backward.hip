@@ -24,7 +24,9 @@
 //   dG = dKt*Kt - dKh*Kh + dQt*Qt - dKe*Ke, dG_n = colsum(dKe*Ke) + dgam*gam,
 //   dg_s = sum_{r >= s} dG_r + dG_n.
 //
-// Four launches, all in fp32 over a per-tile fp32 workspace (BwdLayout):
+// Four launches, all in fp32 over a per-tile fp32 workspace (BwdLayout),
+// each instantiated per (head dim d, chunk C) so that every loop bound and
+// register block is a compile-time constant:
 //   bwd_prep_kernel   per (chunk, head): G, Kt, Kh, Qt, Ke, gam, M, P, T, W, U
 //   bwd_state_kernel  per (sequence, head, 16-column slice): chunk start states
 //   bwd_dstate_kernel per (sequence, head, 16-column slice), chunks in reverse:
@@ -32,10 +34,12 @@
 //   bwd_grad_kernel   per (chunk, head): dq, dk, dv, dg, dbeta
 // The state columns never mix (in the forward and in dS), which is what makes
 // the column slices of the two chains exact.  Rows past a chunk's end are
-// zero (beta = 0, q = k = v = 0, dO = 0) and contribute nothing.  Products run
-// through block_mm: K slices of both operands are staged in LDS with
-// coalesced loads and every thread accumulates a register block of the
-// output in fp32.
+// zero (beta = 0, q = k = v = 0, dO = 0) and contribute nothing.  Every
+// product runs on the fp32 matrix cores in 16 x 16 output tiles: the per-tile
+// products through block_mm (K slices of both operands staged in LDS with
+// 16-byte loads, the next slice in flight while the current one is used),
+// the two chains on chunk operands staged whole in LDS, the next chunk's
+// being loaded into registers while the current one is computed.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -43,71 +47,144 @@ namespace kda {
 
 namespace {
 
-constexpr int KS = 16;  // contraction slice staged in LDS
+constexpr int NT = 256;  // threads per workgroup, all kernels
+// LDS floats that block_mm<M, N, K> stages (at most 6,912 for 64 x 128 x 32 slices)
+template <int M, int N, int K>
+constexpr int mm_lds() {
+  return (M + N) * ((K < 32 ? K : 32) + 4);
+}
 
 // out[i][j] = alpha * sum_k A(i, k) B(k, j) (+ out[i][j] when acc) for
 // i < M, j < N, with A(i, k) = TA ? A[k][i] : A[i][k] and
-// B(k, j) = TB ? B[j][k] : B[k][j] (row-major, leading dimensions given).
-// M, N, K are multiples of 16 and M, N <= 128; out may be global memory or
-// LDS and must not alias A or B.  256 threads: thread (ty, tx) = (tid / 16,
-// tid % 16) owns rows ty + 16 a and columns tx + 16 b.  `lds` holds
-// 2 * KS * 128 floats.  Ends with a barrier, so the block may use `out` right
-// after.
-template <bool TA, bool TB>
-__device__ void block_mm(float *out, int ldo, const float *A, int lda, const float *B, int ldb,
-                         int M, int N, int K, float alpha, bool acc, float *lds) {
-  float *sa = lds, *sb = lds + KS * 128;  // sa[kk][i], sb[kk][j]
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const int ma = M / 16, nb = N / 16;
-  float c[8][8];
+// B(k, j) = TB ? B[j][k] : B[k][j] (row-major, leading dimensions a multiple
+// of 4, all pointers 16-byte aligned).  M <= 64, N <= 128, all multiples of
+// 16; out may be global memory or LDS and must not alias A or B.  The output
+// is cut into 16 x 16 tiles computed on the fp32 matrix cores (mma_f32_k16),
+// tile t = (t / (N/16), t % (N/16)) by wavefront t % 4.  K slices of 32 are
+// staged in LDS with 16-byte loads (the next slice in flight while this one
+// is used): A by rows and B by columns, both with the contraction index
+// contiguous, so that each operand of a 16-deep step is one 16-byte read per
+// lane.  `lds` holds mm_lds<M, N, K>() floats, 16-byte aligned.  Ends with a
+// barrier, so the block may use `out` at once.
+template <int M, int N, int K, bool TA, bool TB>
+__device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
+                                         const float *B, int ldb, float alpha, bool acc,
+                                         float *lds) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 64 && N <= 128, "shape");
+  constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, LDS row stride
+  constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + 3) / 4;
+  constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
+  constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
+  float *sa = lds, *sb = lds + M * LK;  // sa[i][kk] = A(i, k0 + kk), sb[j][kk] = B(k0 + kk, j)
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4 ra[PA], rb[PB];
+  auto load = [&](int k0) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int p = 0; p < PA; ++p) {
+      const int f = tid + NT * p;
+      if (FA % NT == 0 || f < FA) {
+        if (TA) {
+          const int kk = f / (M / 4), i4 = f % (M / 4);
+          ra[p] = *reinterpret_cast<const f32x4 *>(A + (k0 + kk) * lda + 4 * i4);
+        } else {
+          const int i = f / (KS / 4), k4 = f % (KS / 4);
+          ra[p] = *reinterpret_cast<const f32x4 *>(A + i * lda + k0 + 4 * k4);
+        }
+      }
+    }
 #pragma unroll
-    for (int b = 0; b < 8; ++b) c[a][b] = 0.f;
+    for (int p = 0; p < PB; ++p) {
+      const int f = tid + NT * p;
+      if (FB % NT == 0 || f < FB) {
+        if (TB) {
+          const int j = f / (KS / 4), k4 = f % (KS / 4);
+          rb[p] = *reinterpret_cast<const f32x4 *>(B + j * ldb + k0 + 4 * k4);
+        } else {
+          const int kk = f / (N / 4), j4 = f % (N / 4);
+          rb[p] = *reinterpret_cast<const f32x4 *>(B + (k0 + kk) * ldb + 4 * j4);
+        }
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const int f = tid + NT * p;
+      if (FA % NT == 0 || f < FA) {
+        if (TA) {
+          const int kk = f / (M / 4), i4 = f % (M / 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sa[(4 * i4 + u) * LK + kk] = ra[p][u];
+        } else {
+          const int i = f / (KS / 4), k4 = f % (KS / 4);
+          *reinterpret_cast<f32x4 *>(sa + i * LK + 4 * k4) = ra[p];
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const int f = tid + NT * p;
+      if (FB % NT == 0 || f < FB) {
+        if (TB) {
+          const int j = f / (KS / 4), k4 = f % (KS / 4);
+          *reinterpret_cast<f32x4 *>(sb + j * LK + 4 * k4) = rb[p];
+        } else {
+          const int kk = f / (N / 4), j4 = f % (N / 4);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) sb[(4 * j4 + u) * LK + kk] = rb[p][u];
+        }
+      }
+    }
+  };
+  f32x4 c[TPW];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) c[q] = zero4();
+  load(0);
+#pragma unroll
   for (int k0 = 0; k0 < K; k0 += KS) {
-    for (int e = tid; e < M * KS; e += 256) {
-      int i, kk;
-      if (TA) { kk = e / M; i = e % M; } else { i = e / KS; kk = e % KS; }
-      sa[kk * M + i] = TA ? A[(k0 + kk) * lda + i] : A[i * lda + k0 + kk];
-    }
-    for (int e = tid; e < N * KS; e += 256) {
-      int j, kk;
-      if (TB) { j = e / KS; kk = e % KS; } else { kk = e / N; j = e % N; }
-      sb[kk * N + j] = TB ? B[j * ldb + k0 + kk] : B[(k0 + kk) * ldb + j];
-    }
+    store();
     __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < KS; ++kk) {
-      float av[8], bv[8];
+    if (k0 + KS < K) load(k0 + KS);  // next slice in flight during this one
 #pragma unroll
-      for (int a = 0; a < 8; ++a) av[a] = a < ma ? sa[kk * M + ty + 16 * a] : 0.f;
+    for (int ks = 0; ks < KS; ks += 16) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) bv[b] = b < nb ? sb[kk * N + tx + 16 * b] : 0.f;
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) c[a][b] += av[a] * bv[b];
+      for (int q = 0; q < TPW; ++q) {
+        // waves past the last tile repeat it (no branch around the matrix
+        // instructions) and store nothing
+        const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(sa + (16 * (t / TN) + lr) * LK + ks + 4 * lg);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(sb + (16 * (t % TN) + lr) * LK + ks + 4 * lg);
+        c[q] = mma_f32_k16(a, b, c[q]);
+      }
     }
     __syncthreads();
   }
+  // the results reach ordinary registers here, in straight-line code, before
+  // the branch on the tile index below
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int q = 0; q < TPW; ++q) asm volatile("" : "+v"(c[q]));
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
-      if (a < ma && b < nb) {
-        float *o = out + (ty + 16 * a) * ldo + tx + 16 * b;
-        *o = alpha * c[a][b] + (acc ? *o : 0.f);
-      }
+  for (int q = 0; q < TPW; ++q) {
+    const int t = wv + 4 * q;
+    if (TT % 4 == 0 || t < TT) {
+      float *o = out + (16 * (t / TN) + 4 * lg) * ldo + 16 * (t % TN) + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i * ldo] = alpha * c[q][i] + (acc ? o[i * ldo] : 0.f);
+    }
+  }
   __syncthreads();
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
 // length L (leading dimension ld), one wavefront per row.
-__device__ void row_dots(float *out, const float *X, const float *Y, int ld, int R, int L,
-                         bool acc) {
+template <int R, int L>
+__device__ __forceinline__ void row_dots(float *out, const float *X, const float *Y, int ld,
+                                         bool acc) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int r = wv; r < R; r += 4) {
+  for (int r = wv; r < R; r += NT / 64) {
     float s = 0.f;
+#pragma unroll
     for (int j = lane; j < L; j += 64) s += X[r * ld + j] * Y[r * ld + j];
     s = group_sum<64>(s);
     if (lane == 0) out[r] = s + (acc ? out[r] : 0.f);
@@ -157,15 +234,16 @@ __device__ void seq_chunks(int seq, const int *cu, int seq_len, int C, const int
 }  // namespace
 
 // ---- 1. per-tile recompute ------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
+template <typename T, int D, int C>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int *__restrict__ cu,
-    int N, int H, int seq_len, int C, int D, BwdLayout L, char *ws) {
+    int N, int H, int seq_len, BwdLayout L, char *ws) {
+  constexpr int LA = C + 4;
   __shared__ int s_loc[4];
-  __shared__ int s_scan[256];
-  __shared__ float s_mm[2 * KS * 128];
-  __shared__ float s_a[64 * 65];  // A = strict_lower(beta M), for the substitution
+  __shared__ int s_scan[NT];
+  __shared__ __align__(16) float s_mm[mm_lds<C, D, D>()];
+  __shared__ __align__(16) float s_a[C * LA];  // A = strict_lower(beta M), for the substitution
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -174,239 +252,396 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
   float *bkt = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
-  float *bvv = bkt + (int64_t)C * D;  // Diag(beta) Kt and Diag(beta) V (scratch)
+  float *bvv = bkt + C * D;  // Diag(beta) Kt and Diag(beta) V (scratch)
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
-  // cumulative log-decay per channel (rows past the end add nothing)
-  for (int i = tid; i < D; i += blockDim.x) {
+  // cumulative log-decay per channel (rows past the end add nothing); every
+  // row's load is issued before the running sum needs it
+  if (tid < D) {
+    const float *gp = g + (int64_t)t0 * rs + (int64_t)h * D + tid;
+    float gv[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) gv[r] = gp[(int64_t)min(r, n - 1) * rs];
     float run = 0.f;
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      if (r < n) run += g[(int64_t)(t0 + r) * rs + (int64_t)h * D + i];
-      p.gc[r * D + i] = run;
+      run += r < n ? gv[r] : 0.f;
+      p.gc[r * D + tid] = run;
     }
-    p.gam[i] = __expf(run);
+    p.gam[tid] = __expf(run);
   }
-  for (int r = tid; r < C; r += blockDim.x) p.bt[r] = r < n ? beta[(int64_t)(t0 + r) * H + h] : 0.f;
+  for (int r = tid; r < C; r += NT) p.bt[r] = r < n ? beta[(int64_t)(t0 + r) * H + h] : 0.f;
   __syncthreads();
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, i = e % D;
-    const bool live = r < n;
-    const int64_t at = (int64_t)(t0 + r) * rs + (int64_t)h * D + i;
-    const float qv = live ? to_f32(q[at]) : 0.f, kv = live ? to_f32(k[at]) : 0.f;
-    const float vv = live ? to_f32(v[at]) : 0.f;
-    const float G = p.gc[e], Gn = p.gc[(C - 1) * D + i];
-    p.kt[e] = kv * __expf(G);
-    p.kh[e] = kv * __expf(-G);
-    p.qt[e] = qv * __expf(G);
-    p.ke[e] = kv * __expf(Gn - G);
-    p.vr[e] = vv;
-    bkt[e] = p.bt[r] * kv * __expf(G);
-    bvv[e] = p.bt[r] * vv;
+  for (int e4 = tid; e4 < C * D / 4; e4 += NT) {
+    const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
+    const float live = r < n ? 1.f : 0.f;
+    const int64_t at = (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i;
+    const f32x4 qv = load4_f32<T>(q + at) * live, kv = load4_f32<T>(k + at) * live;
+    const f32x4 vv = load4_f32<T>(v + at) * live;
+    const f32x4 G = *reinterpret_cast<const f32x4 *>(p.gc + r * D + i);
+    const f32x4 Gn = *reinterpret_cast<const f32x4 *>(p.gc + (C - 1) * D + i);
+    f32x4 eg, emg, egn;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      eg[u] = __expf(G[u]);
+      emg[u] = __expf(-G[u]);
+      egn[u] = __expf(Gn[u] - G[u]);
+    }
+    const float b = p.bt[r];
+    const int e = r * D + i;
+    *reinterpret_cast<f32x4 *>(p.kt + e) = kv * eg;
+    *reinterpret_cast<f32x4 *>(p.kh + e) = kv * emg;
+    *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
+    *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
+    *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
+    *reinterpret_cast<f32x4 *>(bkt + e) = kv * eg * b;
+    *reinterpret_cast<f32x4 *>(bvv + e) = vv * b;
   }
   __syncthreads();
-  block_mm<false, true>(p.mm, C, p.kt, D, p.kh, D, C, C, D, 1.f, false, s_mm);  // M = Kt Kh^T
-  block_mm<false, true>(p.pm, C, p.qt, D, p.kh, D, C, C, D, 1.f, false, s_mm);  // Qt Kh^T
-  for (int e = tid; e < C * C; e += blockDim.x) {
+  block_mm<C, C, D, false, true>(p.mm, C, p.kt, D, p.kh, D, 1.f, false, s_mm);  // M = Kt Kh^T
+  block_mm<C, C, D, false, true>(p.pm, C, p.qt, D, p.kh, D, 1.f, false, s_mm);  // Qt Kh^T
+  for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, s = e % C;
     if (s > r) p.pm[e] = 0.f;  // P = lower incl. diagonal
-    s_a[r * 65 + s] = s < r ? p.bt[r] * p.mm[e] : 0.f;
+    s_a[r * LA + s] = s < r ? p.bt[r] * p.mm[e] : 0.f;
   }
   __syncthreads();
-  // T = (I + A)^-1: column j by thread j, forward substitution row by row
-  for (int j = tid; j < C; j += blockDim.x) {
-    float tcol[64];
+  // T = (I + A)^-1 by forward substitution, column j by thread j:
+  // T[r][j] = [r == j] - sum_{m < r} A[r][m] T[m][j].  Entries not yet
+  // computed are still zero, so the sums run over whole 4-vectors of a row.
+  if (tid < C) {
+    const int j = tid;
+    float t[C];
 #pragma unroll
-    for (int r = 0; r < 64; ++r) tcol[r] = 0.f;
+    for (int r = 0; r < C; ++r) t[r] = 0.f;
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      float t = r == j ? 1.f : 0.f;
-      if (r > j) {
-        float s = 0.f;
-        for (int m = j; m < r; ++m) s += s_a[r * 65 + m] * tcol[m];
-        t = -s;
+      float s = 0.f;
+#pragma unroll
+      for (int m4 = 0; m4 < (r + 3) / 4; ++m4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(s_a + r * LA + 4 * m4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s += a4[u] * t[4 * m4 + u];
       }
-      tcol[r] = t;
-      p.tm[r * C + j] = t;
+      t[r] = r < j ? 0.f : (r == j ? 1.f : -s);
+      p.tm[r * C + j] = t[r];
     }
   }
   __syncthreads();
-  block_mm<false, false>(p.w, D, p.tm, C, bkt, D, C, D, C, 1.f, false, s_mm);  // W = T (beta Kt)
-  block_mm<false, false>(p.u, D, p.tm, C, bvv, D, C, D, C, 1.f, false, s_mm);  // U = T (beta V)
+  block_mm<C, D, C, false, false>(p.w, D, p.tm, C, bkt, D, 1.f, false, s_mm);  // W = T (beta Kt)
+  block_mm<C, D, C, false, false>(p.u, D, p.tm, C, bvv, D, 1.f, false, s_mm);  // U = T (beta V)
 }
 
 // ---- chain helpers ----------------------------------------------------------
-// A chunk's [rows][cols] fp32 matrix, cols % 4 == 0, moved as float4 through
-// registers (rows * cols / 1024 float4 per thread; at most 8 here) into LDS
-// rows of stride cols + 4.
-struct Stage8 {
-  f32x4 r[8];
+// A chunk's [R][CO] fp32 matrix moved as float4 through registers into LDS
+// rows of stride CO + 4.
+template <int R, int CO>
+struct Stage {
+  static constexpr int N4 = R * CO / 4, P = (N4 + NT - 1) / NT;
+  f32x4 r[P];
+  __device__ __forceinline__ void load(const float *src) {
+#pragma unroll
+    for (int m = 0; m < P; ++m) {
+      const int e = threadIdx.x + NT * m;
+      if (N4 % NT == 0 || e < N4) r[m] = reinterpret_cast<const f32x4 *>(src)[e];
+    }
+  }
+  __device__ __forceinline__ void store(float *dst) const {
+#pragma unroll
+    for (int m = 0; m < P; ++m) {
+      const int e = threadIdx.x + NT * m;
+      if (N4 % NT == 0 || e < N4)
+        *reinterpret_cast<f32x4 *>(dst + (e / (CO / 4)) * (CO + 4) + 4 * (e % (CO / 4))) = r[m];
+    }
+  }
 };
 
-__device__ void stage_load(Stage8 &st, const float *src, int rows, int cols) {
-  const int n4 = rows * cols / 4;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int e = threadIdx.x + 256 * m;
-    if (e < n4) st.r[m] = reinterpret_cast<const f32x4 *>(src)[e];
-  }
-}
+// The two chains run their per-chunk products on the fp32 matrix cores in
+// 16 x 16 output tiles (mma_f32_k16: lane l = 16 g + c supplies A[c][4g + i]
+// and B[4g + i][c] and holds D[4g + i][c]).  Wave w owns token block w of the
+// chunk (rows 16 w ..) and channel blocks w*CBW .. of the state slice.  The
+// right-hand operands sit transposed in LDS (column c of the slice is a row),
+// so that both operands of every step are one 16-byte read per lane.  Matrix
+// results are read (stored or combined) in straight-line code right after
+// the instructions that produce them.
+template <int D, int C>
+struct ChainShape {
+  static constexpr int NS = D / 16, LD = D + 4, LU = C + 4, LP = C + 4;
+  static constexpr int NRB = C / 16, NCB = D / 16, CBW = (NCB + 3) / 4;
+};
 
-__device__ void stage_store(const Stage8 &st, float *dst, int rows, int cols) {
-  const int n4 = rows * cols / 4, c4 = cols / 4;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int e = threadIdx.x + 256 * m;
-    if (e < n4) *reinterpret_cast<f32x4 *>(dst + (e / c4) * (cols + 4) + 4 * (e % c4)) = st.r[m];
-  }
+template <int D, int C>
+constexpr size_t state_lds_bytes() {
+  using Sh = ChainShape<D, C>;
+  return sizeof(float) * (2 * C * Sh::LD + 16 * Sh::LD + 16 * Sh::LU);
+}
+template <int D, int C>
+constexpr size_t dstate_lds_bytes() {
+  using Sh = ChainShape<D, C>;
+  return sizeof(float) * (3 * C * Sh::LD + C * Sh::LP + 16 * Sh::LD + 2 * 16 * Sh::LU);
 }
 
 // ---- 2. chunk start states ------------------------------------------------
-// One block per (sequence, head, 16-column slice); the slice of S lives in LDS
-// and each chunk's W and Ke are staged whole in LDS, the next chunk's being
+// One block per (sequence, head, 16-column slice); each chunk's W and Ke are
+// staged whole in LDS, the next chunk's (and its U tile and gamma) being
 // loaded into registers while this one is computed.
-__global__ __launch_bounds__(256) void bwd_state_kernel(
-    const int *__restrict__ cu, int N, int H, int seq_len, int C, int D,
-    const float *__restrict__ s0, BwdLayout L, char *ws) {
+template <int D, int C>
+__global__ __launch_bounds__(NT) void bwd_state_kernel(
+    const int *__restrict__ cu, int N, int H, int seq_len, const float *__restrict__ s0,
+    BwdLayout L, char *ws) {
+  using Sh = ChainShape<D, C>;
+  constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, NRB = Sh::NRB, NCB = Sh::NCB;
+  constexpr int CBW = Sh::CBW;
   extern __shared__ __align__(16) float sm[];
-  const int NS = D / 16, LD = D + 4;
-  float *sW = sm, *sK = sW + C * LD, *sS = sK + C * LD, *sU = sS + D * 16, *sG = sU + C * 16;
+  float *sW = sm, *sK = sW + C * LD;          // [C][LD] row-major
+  float *sSt = sK + C * LD, *sUt = sSt + 16 * LD;  // S^T [16][LD], Unew^T [16][LU]
   const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
   const int seq = pair / H, h = pair % H;
   if (seq >= N) return;
-  const int col0 = slice * 16, tid = threadIdx.x;
+  const int col0 = slice * 16;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_rb = wv < NRB;
   int first, nch, len;
   seq_chunks(seq, cu, seq_len, C, reinterpret_cast<const int *>(ws + L.seq_first), &first,
              &nch, &len);
-  for (int e = tid; e < D * 16; e += blockDim.x) {
-    const int i = e / 16, j = e % 16;
-    sS[e] = s0 ? s0[((int64_t)pair * D + i) * D + col0 + j] : 0.f;
+  if (nch == 0) return;
+  // S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
+  f32x4 S[CBW];
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = wv * CBW + j;
+    S[j] = zero4();
+    if (s0 && cb < NCB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[j][i] = s0[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
+    }
   }
-  Stage8 rw, rk;
-  if (nch > 0) {
-    const TilePtr p = tile_ptrs(L, ws, (int64_t)first * H + h, C, D);
-    stage_load(rw, p.w, C, D);
-    stage_load(rk, p.ke, C, D);
-  }
+  Stage<C, D> rw, rk;
+  f32x4 un = zero4(), gn[CBW];
+  auto fetch = [&](int64_t tile) {
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    rw.load(p.w);
+    rk.load(p.ke);
+    if (has_rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) un[i] = p.u[(16 * wv + 4 * lg + i) * D + col0 + lr];
+    }
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = min(wv * CBW + j, NCB - 1);
+      gn[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+    }
+  };
+  fetch((int64_t)first * H + h);
   for (int ci = 0; ci < nch; ++ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
-    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
     float *sc = reinterpret_cast<float *>(ws + L.sc) + tile * D * D;
-    __syncthreads();  // the previous chunk is done with sW, sK, sU
-    stage_store(rw, sW, C, D);
-    stage_store(rk, sK, C, D);
-    for (int e = tid; e < C * 16; e += blockDim.x) sU[e] = p.u[(e / 16) * D + col0 + e % 16];
-    for (int i = tid; i < D; i += blockDim.x) sG[i] = p.gam[i];
-    for (int e = tid; e < D * 16; e += blockDim.x) sc[(e / 16) * D + col0 + e % 16] = sS[e];
-    __syncthreads();
-    if (ci + 1 < nch) {
-      const TilePtr pn = tile_ptrs(L, ws, tile + H, C, D);
-      stage_load(rw, pn.w, C, D);
-      stage_load(rk, pn.ke, C, D);
+    __syncthreads();  // the previous chunk is done with the LDS operands
+    rw.store(sW);
+    rk.store(sK);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+        *reinterpret_cast<f32x4 *>(sSt + lr * LD + 16 * cb + 4 * lg) = S[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[(16 * cb + 4 * lg + i) * D + col0 + lr] = S[j][i];
+      }
     }
-    for (int e = tid; e < C * 16; e += blockDim.x) {  // Unew = U - W S
-      const int r = e / 16, j = e % 16;
-      float acc = sU[e];
-      for (int i = 0; i < D; ++i) acc -= sW[r * LD + i] * sS[i * 16 + j];
-      sU[e] = acc;
+    const f32x4 u0 = un;
+    f32x4 gam[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) gam[j] = gn[j];
+    __syncthreads();
+    if (ci + 1 < nch) fetch(tile + H);
+    // Unew = U - W S for the wave's token block
+    if (has_rb) {
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(sW + (16 * wv + lr) * LD + k0 + 4 * lg);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(sSt + lr * LD + k0 + 4 * lg);
+        if ((k0 / 16) & 1) a1 = mma_f32_k16(a, b, a1);
+        else a0 = mma_f32_k16(a, b, a0);
+      }
+      *reinterpret_cast<f32x4 *>(sUt + lr * LU + 16 * wv + 4 * lg) = u0 - (a0 + a1);
     }
     __syncthreads();
-    for (int e = tid; e < D * 16; e += blockDim.x) {  // S = Diag(gam) S + Ke^T Unew
-      const int i = e / 16, j = e % 16;
-      float acc = sG[i] * sS[e];
-      for (int r = 0; r < C; ++r) acc += sK[r * LD + i] * sU[r * 16 + j];
-      sS[e] = acc;
+    // S = Diag(gam) S + Ke^T Unew for the wave's channel blocks
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (NCB % 4 == 0 || cb < NCB) {
+        f32x4 acc = S[j] * gam[j];
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 16) {
+          f32x4 a;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) a[u] = sK[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
+          const f32x4 b = *reinterpret_cast<const f32x4 *>(sUt + lr * LU + k0 + 4 * lg);
+          acc = mma_f32_k16(a, b, acc);
+        }
+        S[j] = acc + 0.f;  // a real VALU read of the result, before any branch
+      }
     }
   }
 }
 
 // ---- 3. state gradients, chunks in reverse ---------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_dstate_kernel(
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len, int C,
-    int D, const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
+template <typename T, int D, int C>
+__global__ __launch_bounds__(NT) void bwd_dstate_kernel(
+    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
+    const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
+  using Sh = ChainShape<D, C>;
+  constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, LP = Sh::LP, NRB = Sh::NRB;
+  constexpr int NCB = Sh::NCB, CBW = Sh::CBW;
   extern __shared__ __align__(16) float sm[];
-  const int NS = D / 16, LD = D + 4, LP = C + 4;
-  float *sW = sm, *sK = sW + C * LD, *sQ = sK + C * LD, *sP = sQ + C * LD;
-  float *sD = sP + C * LP, *sO = sD + D * 16, *sU = sO + C * 16, *sG = sU + C * 16;
+  float *sW = sm, *sK = sW + C * LD, *sQ = sK + C * LD, *sP = sQ + C * LD;  // row-major
+  float *sDt = sP + C * LP, *sOt = sDt + 16 * LD, *sUt = sOt + 16 * LU;     // transposed
   const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
   const int seq = pair / H, h = pair % H;
   if (seq >= N) return;
-  const int col0 = slice * 16, tid = threadIdx.x;
+  const int col0 = slice * 16;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_rb = wv < NRB;
   const int64_t rs = (int64_t)H * D;
   int first, nch, len;
   seq_chunks(seq, cu, seq_len, C, reinterpret_cast<const int *>(ws + L.seq_first), &first,
              &nch, &len);
   const int t_seq = cu ? cu[seq] : seq * seq_len;
-  for (int e = tid; e < D * 16; e += blockDim.x) {
-    const int i = e / 16, j = e % 16;
-    sD[e] = dsf ? dsf[((int64_t)pair * D + i) * D + col0 + j] : 0.f;
+  // dS[j][i] = dS_next[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
+  f32x4 dS[CBW];
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = wv * CBW + j;
+    dS[j] = zero4();
+    if (dsf && cb < NCB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dS[j][i] = dsf[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
+    }
   }
-  Stage8 rw, rk, rq, rp;
-  if (nch > 0) {
-    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + nch - 1) * H + h, C, D);
-    stage_load(rw, p.w, C, D);
-    stage_load(rk, p.ke, C, D);
-    stage_load(rq, p.qt, C, D);
-    stage_load(rp, p.pm, C, C);
-  }
+  Stage<C, D> rw, rk, rq;
+  Stage<C, C> rp;
+  f32x4 on = zero4(), gn[CBW];
+  auto fetch = [&](int ci) {
+    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + ci) * H + h, C, D);
+    rw.load(p.w);
+    rk.load(p.ke);
+    rq.load(p.qt);
+    rp.load(p.pm);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = min(wv * CBW + j, NCB - 1);
+      gn[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+    }
+    if (has_rb) {  // dO[16 wv + 4 lg + i][col0 + lr], zero past the chunk's end
+      const int n = min(C, len - ci * C);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wv + 4 * lg + i;
+        const float x =
+            to_f32(d_o[(int64_t)(t_seq + ci * C + min(r, n - 1)) * rs + (int64_t)h * D + col0 + lr]);
+        on[i] = r < n ? x : 0.f;
+      }
+    }
+  };
+  if (nch > 0) fetch(nch - 1);
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
-    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
     float *dse = reinterpret_cast<float *>(ws + L.dse) + tile * D * D;
     float *dun = reinterpret_cast<float *>(ws + L.dun) + tile * C * D;
-    const int t0 = t_seq + ci * C, n = min(C, len - ci * C);
-    __syncthreads();  // the previous chunk is done with the staged operands
-    stage_store(rw, sW, C, D);
-    stage_store(rk, sK, C, D);
-    stage_store(rq, sQ, C, D);
-    stage_store(rp, sP, C, C);
-    for (int i = tid; i < D; i += blockDim.x) sG[i] = p.gam[i];
-    for (int e = tid; e < D * 16; e += blockDim.x) dse[(e / 16) * D + col0 + e % 16] = sD[e];
-    for (int e = tid; e < C * 16; e += blockDim.x) {
-      const int r = e / 16, j = e % 16;
-      sO[e] = r < n ? to_f32(d_o[(int64_t)(t0 + r) * rs + (int64_t)h * D + col0 + j]) : 0.f;
+    __syncthreads();  // the previous chunk is done with the LDS operands
+    rw.store(sW);
+    rk.store(sK);
+    rq.store(sQ);
+    rp.store(sP);
+    if (has_rb) *reinterpret_cast<f32x4 *>(sOt + lr * LU + 16 * wv + 4 * lg) = on;
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+        *reinterpret_cast<f32x4 *>(sDt + lr * LD + 16 * cb + 4 * lg) = dS[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dse[(16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
+      }
+    }
+    f32x4 gam[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) gam[j] = gn[j];
+    __syncthreads();
+    if (ci > 0) fetch(ci - 1);
+    // dUnew = P^T dO + Ke dS_next for the wave's token block
+    if (has_rb) {
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        f32x4 a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[u] = sP[(k0 + 4 * lg + u) * LP + 16 * wv + lr];
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(sOt + lr * LU + k0 + 4 * lg);
+        a0 = mma_f32_k16(a, b, a0);
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(sK + (16 * wv + lr) * LD + k0 + 4 * lg);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(sDt + lr * LD + k0 + 4 * lg);
+        a1 = mma_f32_k16(a, b, a1);
+      }
+      const f32x4 du = a0 + a1;
+      *reinterpret_cast<f32x4 *>(sUt + lr * LU + 16 * wv + 4 * lg) = du;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dun[(16 * wv + 4 * lg + i) * D + col0 + lr] = du[i];
     }
     __syncthreads();
-    if (ci > 0) {
-      const TilePtr pn = tile_ptrs(L, ws, tile - H, C, D);
-      stage_load(rw, pn.w, C, D);
-      stage_load(rk, pn.ke, C, D);
-      stage_load(rq, pn.qt, C, D);
-      stage_load(rp, pn.pm, C, C);
-    }
-    for (int e = tid; e < C * 16; e += blockDim.x) {  // dUnew = P^T dO + Ke dS
-      const int r = e / 16, j = e % 16;
-      float acc = 0.f;
-      for (int m = 0; m < C; ++m) acc += sP[m * LP + r] * sO[m * 16 + j];
-      for (int i = 0; i < D; ++i) acc += sK[r * LD + i] * sD[i * 16 + j];
-      sU[e] = acc;
-      dun[r * D + col0 + j] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < D * 16; e += blockDim.x) {  // dS = gam dS + Qt^T dO - W^T dUnew
-      const int i = e / 16, j = e % 16;
-      float acc = sG[i] * sD[e];
-      for (int r = 0; r < C; ++r) acc += sQ[r * LD + i] * sO[r * 16 + j] - sW[r * LD + i] * sU[r * 16 + j];
-      sD[e] = acc;
+    // dS = Diag(gam) dS_next + Qt^T dO - W^T dUnew for the wave's channel blocks
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (NCB % 4 == 0 || cb < NCB) {
+        f32x4 aq = zero4(), aw = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 16) {
+          f32x4 qa, wa;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            qa[u] = sQ[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
+            wa[u] = sW[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
+          }
+          const f32x4 ob = *reinterpret_cast<const f32x4 *>(sOt + lr * LU + k0 + 4 * lg);
+          const f32x4 ub = *reinterpret_cast<const f32x4 *>(sUt + lr * LU + k0 + 4 * lg);
+          aq = mma_f32_k16(qa, ob, aq);
+          aw = mma_f32_k16(wa, ub, aw);
+        }
+        dS[j] = dS[j] * gam[j] + (aq - aw);
+      }
     }
   }
-  __syncthreads();
   if (ds0) {
-    for (int e = tid; e < D * 16; e += blockDim.x) {
-      const int i = e / 16, j = e % 16;
-      ds0[((int64_t)pair * D + i) * D + col0 + j] = sD[e];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ds0[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
+      }
     }
   }
 }
 
 // ---- 4. per-tile gradients -------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_grad_kernel(
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len, int C,
-    int D, T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
+template <typename T, int D, int C>
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
+    T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
   __shared__ int s_loc[4];
-  __shared__ int s_scan[256];
-  __shared__ float s_mm[2 * KS * 128];
+  __shared__ int s_scan[NT];
+  __shared__ __align__(16) float s_mm[mm_lds<C, D, D>()];
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -414,7 +649,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-  const int64_t cd = (int64_t)C * D, cc = (int64_t)C * C;
+  constexpr int cd = C * D, cc = C * C;
   const float *sc = reinterpret_cast<const float *>(ws + L.sc) + tile * D * D;
   const float *dse = reinterpret_cast<const float *>(ws + L.dse) + tile * D * D;
   const float *dun = reinterpret_cast<const float *>(ws + L.dun) + tile * cd;
@@ -425,32 +660,35 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   float *dgam = da + cc;
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, i = e % D;
-    dot[e] = r < n ? to_f32(d_o[(int64_t)(t0 + r) * rs + (int64_t)h * D + i]) : 0.f;
-    unew[e] = p.u[e];
+  for (int e4 = tid; e4 < cd / 4; e4 += NT) {
+    const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
+    const float live = r < n ? 1.f : 0.f;
+    const f32x4 o4 =
+        load4_f32<T>(d_o + (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i) * live;
+    *reinterpret_cast<f32x4 *>(dot + 4 * e4) = o4;
+    *reinterpret_cast<f32x4 *>(unew + 4 * e4) = reinterpret_cast<const f32x4 *>(p.u)[e4];
   }
   __syncthreads();
-  block_mm<false, false>(unew, D, p.w, D, sc, D, C, D, D, -1.f, true, s_mm);  // U - W S
-  row_dots(dgam, dse, sc, D, D, D, false);                                    // rowsum(dS_next * S)
-  block_mm<false, true>(dp, C, dot, D, unew, D, C, C, D, 1.f, false, s_mm);   // dO Unew^T
-  block_mm<false, true>(dqt, D, dot, D, sc, D, C, D, D, 1.f, false, s_mm);    // dO S^T
-  block_mm<false, true>(dke, D, unew, D, dse, D, C, D, D, 1.f, false, s_mm);  // Unew dS_next^T
-  block_mm<false, true>(dw, D, dun, D, sc, D, C, D, D, -1.f, false, s_mm);    // -dUnew S^T
-  for (int e = tid; e < C * C; e += blockDim.x)
+  block_mm<C, D, D, false, false>(unew, D, p.w, D, sc, D, -1.f, true, s_mm);  // U - W S
+  row_dots<D, D>(dgam, dse, sc, D, false);                                    // rowsum(dS_next * S)
+  block_mm<C, C, D, false, true>(dp, C, dot, D, unew, D, 1.f, false, s_mm);   // dO Unew^T
+  block_mm<C, D, D, false, true>(dqt, D, dot, D, sc, D, 1.f, false, s_mm);    // dO S^T
+  block_mm<C, D, D, false, true>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
+  block_mm<C, D, D, false, true>(dw, D, dun, D, sc, D, -1.f, false, s_mm);    // -dUnew S^T
+  for (int e = tid; e < cc; e += NT)
     if (e % C > e / C) dp[e] = 0.f;  // dP lower incl. diagonal
   __syncthreads();
-  block_mm<false, false>(dqt, D, dp, C, p.kh, D, C, D, C, 1.f, true, s_mm);   // + dP Kh
+  block_mm<C, D, C, false, false>(dqt, D, dp, C, p.kh, D, 1.f, true, s_mm);   // + dP Kh
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
-  block_mm<false, true>(dt, C, dw, D, p.kt, D, C, C, D, 1.f, false, s_mm);
-  block_mm<false, true>(dt, C, dun, D, p.vr, D, C, C, D, 1.f, true, s_mm);
-  for (int e = tid; e < C * C; e += blockDim.x) dt[e] *= p.bt[e % C];
+  block_mm<C, C, D, false, true>(dt, C, dw, D, p.kt, D, 1.f, false, s_mm);
+  block_mm<C, C, D, false, true>(dt, C, dun, D, p.vr, D, 1.f, true, s_mm);
+  for (int e = tid; e < cc; e += NT) dt[e] *= p.bt[e % C];
   __syncthreads();
-  block_mm<true, false>(dbkt, D, p.tm, C, dw, D, C, D, C, 1.f, false, s_mm);  // T^T dW
-  block_mm<true, false>(dbv, D, p.tm, C, dun, D, C, D, C, 1.f, false, s_mm);  // T^T dUnew
-  block_mm<true, false>(xm, C, p.tm, C, dt, C, C, C, C, 1.f, false, s_mm);    // T^T dT
-  block_mm<false, true>(da, C, xm, C, p.tm, C, C, C, C, -1.f, false, s_mm);   // -T^T dT T^T
-  for (int e = tid; e < C * C; e += blockDim.x) {
+  block_mm<C, D, C, true, false>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);  // T^T dW
+  block_mm<C, D, C, true, false>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);  // T^T dUnew
+  block_mm<C, C, C, true, false>(xm, C, p.tm, C, dt, C, 1.f, false, s_mm);    // T^T dT
+  block_mm<C, C, C, false, true>(da, C, xm, C, p.tm, C, -1.f, false, s_mm);   // -T^T dT T^T
+  for (int e = tid; e < cc; e += NT) {
     const int r = e / C, s = e % C;
     if (s >= r) da[e] = 0.f;  // strictly lower
   }
@@ -458,82 +696,115 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(
   // dbeta = rowsum(dA * M) + rowsum(dBKt * Kt) + rowsum(dBV * V), before dA
   // is scaled into dM below
   float *dbr = xm;  // [C], xm is free now
-  row_dots(dbr, da, p.mm, C, C, C, false);
-  row_dots(dbr, dbkt, p.kt, D, C, D, true);
-  row_dots(dbr, dbv, p.vr, D, C, D, true);
-  for (int e = tid; e < C * C; e += blockDim.x) da[e] *= p.bt[e / C];  // dM = Diag(beta) dA
+  row_dots<C, C>(dbr, da, p.mm, C, false);
+  row_dots<C, D>(dbr, dbkt, p.kt, D, true);
+  row_dots<C, D>(dbr, dbv, p.vr, D, true);
+  for (int e = tid; e < cc; e += NT) da[e] *= p.bt[e / C];  // dM = Diag(beta) dA
   __syncthreads();
   // dKt = Diag(beta) dBKt + dM Kh; dKh = dM^T Kt + dP^T Qt
-  block_mm<false, false>(dkt, D, da, C, p.kh, D, C, D, C, 1.f, false, s_mm);
-  block_mm<true, false>(dkh, D, da, C, p.kt, D, C, D, C, 1.f, false, s_mm);
-  block_mm<true, false>(dkh, D, dp, C, p.qt, D, C, D, C, 1.f, true, s_mm);
-  for (int e = tid; e < C * D; e += blockDim.x) dkt[e] += p.bt[e / D] * dbkt[e];
-  __syncthreads();
-  // outputs per row: dq, dk, dv, dbeta
-  for (int e = tid; e < C * D; e += blockDim.x) {
-    const int r = e / D, i = e % D;
+  block_mm<C, D, C, false, false>(dkt, D, da, C, p.kh, D, 1.f, false, s_mm);
+  block_mm<C, D, C, true, false>(dkh, D, da, C, p.kt, D, 1.f, false, s_mm);
+  block_mm<C, D, C, true, false>(dkh, D, dp, C, p.qt, D, 1.f, true, s_mm);
+  // outputs per row: dq, dk, dv (4 channels per thread)
+  for (int e4 = tid; e4 < cd / 4; e4 += NT) {
+    const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4)), e = 4 * e4;
     if (r >= n) continue;
-    const float G = p.gc[e], Gn = p.gc[(C - 1) * D + i];
+    const f32x4 G = *reinterpret_cast<const f32x4 *>(p.gc + e);
+    const f32x4 Gn = *reinterpret_cast<const f32x4 *>(p.gc + (C - 1) * D + i);
+    const f32x4 vqt = *reinterpret_cast<const f32x4 *>(dqt + e);
+    const f32x4 vkt = *reinterpret_cast<const f32x4 *>(dkt + e) +
+                      p.bt[r] * *reinterpret_cast<const f32x4 *>(dbkt + e);
+    const f32x4 vkh = *reinterpret_cast<const f32x4 *>(dkh + e);
+    const f32x4 vke = *reinterpret_cast<const f32x4 *>(dke + e);
+    const f32x4 vbv = *reinterpret_cast<const f32x4 *>(dbv + e);
+    f32x4 oq, ok;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float eg = __expf(G[u]);
+      oq[u] = vqt[u] * eg;
+      ok[u] = vkt[u] * eg + vkh[u] * __expf(-G[u]) + vke[u] * __expf(Gn[u] - G[u]);
+    }
     const int64_t at = (int64_t)(t0 + r) * rs + (int64_t)h * D + i;
-    dq[at] = from_f32<T>(dqt[e] * __expf(G));
-    dk[at] = from_f32<T>(dkt[e] * __expf(G) + dkh[e] * __expf(-G) + dke[e] * __expf(Gn - G));
-    dv[at] = from_f32<T>(p.bt[r] * dbv[e]);
+    store4_f32<T>(dq + at, oq);
+    store4_f32<T>(dk + at, ok);
+    store4_f32<T>(dv + at, vbv * p.bt[r]);
   }
-  for (int r = tid; r < n; r += blockDim.x) dbeta[(int64_t)(t0 + r) * H + h] = dbr[r];
+  for (int r = tid; r < n; r += NT) dbeta[(int64_t)(t0 + r) * H + h] = dbr[r];
   // dg: reverse cumulative sum of dG over the chunk plus dG_n, per channel
-  for (int i = tid; i < D; i += blockDim.x) {
+  // (dKt here is the full Diag(beta) dBKt + dM Kh)
+  if (tid < D) {
+    const int i = tid;
     float dgn = dgam[i] * p.gam[i];
+#pragma unroll 8
     for (int r = 0; r < C; ++r) dgn += dke[r * D + i] * p.ke[r * D + i];
     float run = dgn;
     for (int r = n - 1; r >= 0; --r) {
       const int e = r * D + i;
-      run += dkt[e] * p.kt[e] - dkh[e] * p.kh[e] + dqt[e] * p.qt[e] - dke[e] * p.ke[e];
+      run += (dkt[e] + p.bt[r] * dbkt[e]) * p.kt[e] - dkh[e] * p.kh[e] + dqt[e] * p.qt[e] -
+             dke[e] * p.ke[e];
       dg[(int64_t)(t0 + r) * rs + (int64_t)h * D + i] = run;
     }
   }
 }
 
-template <typename T>
-static hipError_t launch_bwd_t(const BwdArgs &a) {
+template <typename T, int D, int C>
+static hipError_t launch_bwd_dc(const BwdArgs &a) {
   const unsigned tiles = (unsigned)(a.grid_chunks * a.num_heads);
-  const unsigned slices = (unsigned)(a.num_seqs * a.num_heads * (a.d / 16));
+  const unsigned slices = (unsigned)(a.num_seqs * a.num_heads * (D / 16));
   const T *q = reinterpret_cast<const T *>(a.q), *k = reinterpret_cast<const T *>(a.k);
   const T *v = reinterpret_cast<const T *>(a.v), *d_o = reinterpret_cast<const T *>(a.d_o);
-  if (tiles > 0)
-    hipLaunchKernelGGL(bwd_prep_kernel<T>, dim3(tiles), dim3(256), 0, a.stream, q, k, v, a.g,
-                       a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d,
-                       a.lay, a.ws);
-  const int C = a.chunk, D = a.d;
-  const size_t lds_state = sizeof(float) * (2 * C * (D + 4) + D * 16 + C * 16 + D);
-  const size_t lds_dstate =
-      sizeof(float) * (3 * C * (D + 4) + C * (C + 4) + D * 16 + 2 * C * 16 + D);
-  // the largest shapes (d = 128, C = 64): 80,384 and 135,680 bytes
+  constexpr size_t lds_state = state_lds_bytes<D, C>(), lds_dstate = dstate_lds_bytes<D, C>();
+  // the largest shapes (d = 128, C = 64): 80,384 and 135,936 bytes
   static const hipError_t a1 = hipFuncSetAttribute(
-      (const void *)bwd_state_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(sizeof(float) * (2 * 64 * 132 + 128 * 16 + 64 * 16 + 128)));
+      (const void *)bwd_state_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds_state);
   static const hipError_t a2 = hipFuncSetAttribute(
-      (const void *)bwd_dstate_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(sizeof(float) * (3 * 64 * 132 + 64 * 68 + 128 * 16 + 2 * 64 * 16 + 128)));
+      (const void *)bwd_dstate_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds_dstate);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
-  hipLaunchKernelGGL(bwd_state_kernel, dim3(slices), dim3(256), lds_state, a.stream,
-                     a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d, a.s0,
-                     a.lay, a.ws);
-  hipLaunchKernelGGL(bwd_dstate_kernel<T>, dim3(slices), dim3(256), lds_dstate, a.stream, d_o,
-                     a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d, a.dsf,
+  if (tiles > 0)
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
+                       a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.lay,
+                       a.ws);
+  hipLaunchKernelGGL((bwd_state_kernel<D, C>), dim3(slices), dim3(NT), lds_state, a.stream,
+                     a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
+  hipLaunchKernelGGL((bwd_dstate_kernel<T, D, C>), dim3(slices), dim3(NT), lds_dstate,
+                     a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf,
                      a.ds0, a.lay, a.ws);
   if (tiles > 0)
-    hipLaunchKernelGGL(bwd_grad_kernel<T>, dim3(tiles), dim3(256), 0, a.stream, d_o,
-                       a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.chunk, a.d,
+    hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, d_o,
+                       a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
                        reinterpret_cast<T *>(a.dq), reinterpret_cast<T *>(a.dk),
                        reinterpret_cast<T *>(a.dv), a.dg, a.dbeta, a.lay, a.ws);
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static hipError_t launch_bwd_d(const BwdArgs &a) {
+  switch (a.chunk) {
+    case 16: return launch_bwd_dc<T, D, 16>(a);
+    case 32: return launch_bwd_dc<T, D, 32>(a);
+    case 64: return launch_bwd_dc<T, D, 64>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd(const BwdArgs &a, kda_dtype dt) {
   if (a.grid_chunks == 0 && a.ds0 == nullptr) return hipSuccess;
-  if (dt == KDA_DTYPE_BF16) return launch_bwd_t<bf16>(a);
-  return launch_bwd_t<float>(a);
+  if (dt == KDA_DTYPE_BF16) {
+    switch (a.d) {
+      case 32: return launch_bwd_d<bf16, 32>(a);
+      case 64: return launch_bwd_d<bf16, 64>(a);
+      case 128: return launch_bwd_d<bf16, 128>(a);
+    }
+  } else {
+    switch (a.d) {
+      case 32: return launch_bwd_d<float, 32>(a);
+      case 64: return launch_bwd_d<float, 64>(a);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kda

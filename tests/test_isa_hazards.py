@@ -1,14 +1,14 @@
-"""CPU check of the compiled gfx950 code of the prefill kernels.
+"""CPU check of the compiled gfx950 code of the prefill and backward kernels.
 
 A read of a matrix-core (MFMA) result placed right behind a branch or a
 branch target has been seen to return the register's previous contents on
 gfx950: the wait states the hardware needs between the instruction and the
 read were missing on that path.  The kernels are written so that results are
-read only in straight-line code after their MFMA; this test compiles both
-prefill kernels to assembly (no GPU needed) and, for every MFMA, follows
-every control-flow path for a few dozen instructions, failing on a read of
-its destination registers after a branch or label with fewer than MIN_WAIT
-wait states in between.
+read only in straight-line code after their MFMA; this test compiles the
+sources that use the matrix cores to assembly (no GPU needed) and, for
+every MFMA, follows every control-flow path for a few dozen instructions,
+failing on a read of its destination registers after a branch or label
+with fewer than MIN_WAIT wait states in between.
 """
 import os
 import re
@@ -113,7 +113,7 @@ def _suspect_reads(lines):
     return sorted(found)
 
 
-@pytest.mark.parametrize("source", ["kda_intra.hip", "kda_inter.hip"])
+@pytest.mark.parametrize("source", ["kda_intra.hip", "kda_inter.hip", "kda_backward.hip"])
 def test_no_mfma_result_read_across_a_branch(source, tmp_path):
     from gated_delta_rule_chunked_amd import build
     out = tmp_path / "k.s"
