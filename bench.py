@@ -54,6 +54,7 @@ from gated_delta_rule_chunked_amd import inputs as kin  # noqa: E402
 # bf16 matrix throughput.
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
+FP32_MFMA_PEAK_TFLOPS = 157.3  # dense fp32 on the matrix cores
 
 METRIC = "KDA prefill tokens/s + decode steps/s on 1 GPU; % of MFMA / HBM roofline"
 
@@ -83,6 +84,16 @@ def prefill_flops_per_token_head(d, C):
 
 def state_bytes(d):
     return 4 * d * d
+
+
+def backward_flops_per_token_head(d, C):
+    """Matrix-core work of kda_bwd_chunked as computed (triangular blocks in
+    full), per token-head: per tile of C tokens the recompute (M, P, W, U:
+    4 C^2 d; T: C^3 / 6), the two state chains (2 C d^2 and C^2 d + 3 C d^2)
+    and the per-tile gradients (4 C d^2 + 9 C^2 d + 2 C^3), 2 flops a
+    multiply-add."""
+    macs = 9 * C * d * d + 14 * C * C * d + (2 + 1 / 6) * C ** 3
+    return 2 * macs / C
 
 
 def backward_bytes_per_token_head(d, E):
@@ -285,13 +296,16 @@ def time_backward(torch, kda, w, steps, warmup, d, E):
     ms = e0.elapsed_time(e1) / steps
     th = w.total_tokens * w.num_heads
     byts = th * backward_bytes_per_token_head(d, E) + w.num_seqs * w.num_heads * state_bytes(d)
-    ach = byts / (ms * 1e-3) / 1e9
+    flops = th * backward_flops_per_token_head(d, w.chunk_size)
+    tf = flops / (ms * 1e-3) / 1e12
     return dict(tokens_per_s=w.total_tokens / (ms * 1e-3), ms_per_step=ms,
-                algorithmic_bytes=byts, roofline_frac=ach / HBM_PEAK_GBS,
-                roofline=dict(bound="hbm", achieved=ach, peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=ach / HBM_PEAK_GBS, traffic=None,
-                              kernel="kda_bwd_chunked (4 kernels)", bytes_per_launch=byts,
-                              avg_launch_us=ms * 1e3))
+                algorithmic_bytes=byts, algorithmic_flops=flops,
+                hbm_frac=byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                roofline_frac=tf / FP32_MFMA_PEAK_TFLOPS,
+                roofline=dict(bound="mfma", achieved=tf, peak=FP32_MFMA_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=tf / FP32_MFMA_PEAK_TFLOPS, traffic=None,
+                              kernel="kda_bwd_chunked (4 kernels, fp32 matrix cores)",
+                              flops_per_launch=flops, avg_launch_us=ms * 1e3))
 
 
 # ---------------------------------------------------------------- decode

@@ -1,8 +1,15 @@
-"""fp64 CPU oracle for Kimi Delta Attention (ctypes wrapper of kda_oracle.c).
+"""fp64 CPU oracle for Kimi Delta Attention.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package
 smoke check and the CPU-baseline leg of the benchmark may import this
 module.  It shares no code with the HIP path and the HIP path never calls it.
+
+The recurrence, its chunked form, the decode step, the chunk-local
+cumulative sum and the UT inverse are ctypes wrappers of kda_oracle.c.  The
+input-side transforms (gate functions, q/k normalisation, beta from logits)
+and the output epilogue (RMSNorm, output gate) are plain numpy in fp64.  The
+backward (recurrent_backward) is torch autograd in fp64 on the CPU over the
+token-by-token recurrence.
 
 Every function takes numpy arrays of any real dtype, converts them to
 contiguous float64 (bf16 inputs must be expanded to float first; the
@@ -10,9 +17,12 @@ conversion is exact) and returns float64 arrays.  Layouts follow the
 operator's: q, k, g [T, H, d_k]; v, o [T, H, d_v]; beta [T, H];
 states [N, H, d_k, d_v]; cu_seqlens [N + 1].
 
-Parity status: every function here is pinned by tests/test_oracle.py to
-closed forms, special cases and brute-force dense products taken from the
-pages (see that file); none is "parity unpinned".
+Parity status: every function here is pinned to closed forms, special cases
+and brute-force dense products taken from the pages: the C functions by
+tests/test_oracle.py, the transforms and the epilogue by
+tests/test_oracle_inputs.py, the backward by tests/test_oracle_backward.py
+(central finite differences of the C forward, closed forms); none is
+"parity unpinned".
 """
 import ctypes
 import os
