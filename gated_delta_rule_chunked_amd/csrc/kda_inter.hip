@@ -151,8 +151,13 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *pp = pm + tile * (C * CK) + (rb * KC * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) B.qA[ks] = load8<T>(qq + ks * 512);
+    // P is lower triangular: a token K-step that starts past the wave's last
+    // row is zero and is not loaded (saves a quarter of P's bytes when C = 64)
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) B.pA[ks] = load8<T>(pp + ks * 512);  // upper blocks are zero
+    for (int ks = 0; ks < KC; ++ks) {
+      if (32 * ks <= 16 * rb + 15) B.pA[ks] = load8<T>(pp + ks * 512);
+      else B.pA[ks] = F{};
+    }
   };
   auto load_kg = [&](Buf &B, int ci) {
     const int64_t tile = tile_of(ci);
