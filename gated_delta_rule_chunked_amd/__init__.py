@@ -10,7 +10,8 @@ Submodules are loaded on first use so that ``gated_delta_rule_chunked_amd.inputs
 """
 _BINDING_NAMES = ("fwd_chunked", "decode_step", "workspace_size", "library",
                   "KdaError", "library_path", "bind_fwd", "bind_decode", "bwd_chunked",
-                  "bind_bwd", "bwd_workspace_size")
+                  "bind_bwd", "bwd_workspace_size", "FLAG_DECAY_RANGE",
+                  "FLAG_BAD_CU_SEQLENS")
 
 __all__ = list(_BINDING_NAMES)
 

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "kda")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_decode.hip",
-           "kda_epilogue.hip", "kda_backward.hip"]
+           "kda_epilogue.hip", "kda_backward.hip", "kda_check.hip"]
 ARCH = "gfx950"
 
 

@@ -52,6 +52,10 @@ kda_status resolve_options(const kda_options *in, OptArgs *out) {
     out->out_gate = in->out_gate;
     out->norm_eps = in->out_norm_eps;
   }
+  if (in->flags && !aligned(in->flags, 4)) return KDA_ERROR_INVALID_VALUE;
+  if (in->check_inputs && !in->flags) return KDA_ERROR_INVALID_VALUE;
+  out->flags = in->flags;
+  out->check = in->check_inputs != 0;
   return KDA_SUCCESS;
 }
 
@@ -160,6 +164,9 @@ kda_status fwd_run(unsigned mask, const kda_options *options, const void *q, con
   a.lay = lay;
   a.stream = reinterpret_cast<hipStream_t>(stream);
 
+  if (in.check && cu_seqlens &&
+      launch_check_cu(cu_seqlens, num_seqs, total_tokens, in.flags, a.stream) != hipSuccess)
+    return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 1u) && launch_intra(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 2u) && launch_inter(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 2u) && in.norm_w && total_tokens > 0 &&

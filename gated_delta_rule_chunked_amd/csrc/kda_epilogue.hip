@@ -20,7 +20,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void out_epilogue_kernel(T *__restrict__ o,
                                                            const T *__restrict__ z,
                                                            const float *__restrict__ w,
-                                                           float eps, int64_t rows) {
+                                                           float eps, int64_t rows,
+                                                           const OptArgs in) {
+  if (inputs_rejected(in)) return;
   constexpr int L = D / 8;        // lanes per row
   constexpr int RPB = 256 / L;    // rows per block
   const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / L;
@@ -51,7 +53,7 @@ static hipError_t launch_epi(void *o, const OptArgs &in, int64_t rows, hipStream
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((out_epilogue_kernel<T, D>), grid, dim3(256), 0, s,
                      reinterpret_cast<T *>(o), reinterpret_cast<const T *>(in.out_gate),
-                     in.norm_w, in.norm_eps, rows);
+                     in.norm_w, in.norm_eps, rows, in);
   return hipGetLastError();
 }
 

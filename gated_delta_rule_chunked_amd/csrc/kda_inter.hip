@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const float *__restrict__ gam, const int *__restrict__ cu,
     const int *__restrict__ seq_first, int N, int H, int seq_len,
     const float *__restrict__ s0, float *__restrict__ s_final,
-    const int *__restrict__ slots, int num_slots, T *__restrict__ o) {
+    const int *__restrict__ slots, int num_slots, const OptArgs in, T *__restrict__ o) {
   using Ops = InterOps<T, D, C>;
   using F = typename Ops::F;
   using V4 = typename Ops::V4;
@@ -77,6 +77,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   __shared__ V4 sS[NCB][64];     // S (operand type), one output tile per channel block
   __shared__ V4 sU[2 * KC][64];  // Unew (operand type), one tile per token block
 
+  if (inputs_rejected(in)) return;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int slice = local % NS, unit = local / NS;
@@ -291,7 +292,7 @@ static hipError_t launch_inter_c(const FwdArgs &a) {
                      reinterpret_cast<const float *>(ws + a.lay.gam), a.cu_seqlens,
                      reinterpret_cast<const int *>(ws + a.lay.seq_first), a.num_seqs,
                      a.num_heads, a.seq_len, a.s0, a.s_final, a.in.slots, a.in.num_slots,
-                     reinterpret_cast<T *>(a.o));
+                     a.in, reinterpret_cast<T *>(a.o));
   return hipGetLastError();
 }
 

@@ -76,7 +76,15 @@ struct OptArgs {
   const void *out_gate = nullptr;
   float norm_eps = 0.f;
   int heads = 0;  // decode: heads per sequence, to find A of state p
+  int *flags = nullptr;  // KDA_FLAG_* bits are ORed in here, or nullptr
+  int check = 0;         // nonzero: cu_seqlens was validated into flags first
 };
+
+// With OptArgs::check, every prefill kernel returns at once when the
+// validation kernel has flagged cu_seqlens (read after a kernel boundary).
+__device__ inline bool inputs_rejected(const OptArgs &in) {
+  return in.check && (*in.flags & KDA_FLAG_BAD_CU_SEQLENS) != 0;
+}
 
 // Arguments common to the two prefill launches.
 struct FwdArgs {
@@ -157,6 +165,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
+// Validates cu_seqlens [N + 1] (cu[0] = 0, non-decreasing, cu[N] = total) and
+// ORs KDA_FLAG_BAD_CU_SEQLENS into *flags when it fails.
+hipError_t launch_check_cu(const int *cu, int N, int64_t total, int *flags, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &a, kda_dtype dt);
 hipError_t launch_inter(const FwdArgs &a, kda_dtype dt);
 // In place on o [rows, d]: o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(z).

@@ -158,6 +158,7 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
 
   // heads vary fastest over the grid: the tiles resident together then read
   // whole token rows of the [T, H, d] inputs instead of one head's slice
+  if (inputs_rejected(in)) return;
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
   const int t0 = __builtin_amdgcn_readfirstlane(s_loc[1]);
@@ -238,7 +239,12 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       tot += x;
     }
     const f32x4 etot = {__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
-    if (rg == 0) *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
+    if (rg == 0) {
+      *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
+      // precondition of the chunk-start reference: summed log-decay > -80
+      if (in.flags && (tot[0] <= -80.f || tot[1] <= -80.f || tot[2] <= -80.f || tot[3] <= -80.f))
+        atomicOr(in.flags, KDA_FLAG_DECAY_RANGE);
+    }
     // e^-G = 1 / e^G and e^(G_n - G) = e^G_n / e^G: in range for G > -80
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {

@@ -26,12 +26,18 @@ GATES = {"log_alpha": 0, "softplus": 1, "sigmoid": 2}
 
 class KdaOptions(ctypes.Structure):
     """kda_options (include/kda.h): input-side fusion, state slots, output
-    epilogue."""
+    epilogue, diagnostics."""
     _fields_ = [("gate", ctypes.c_int), ("gate_A", ctypes.c_void_p),
                 ("gate_min", ctypes.c_float), ("l2norm_qk", ctypes.c_int32),
                 ("beta_logits", ctypes.c_int32), ("state_slots", ctypes.c_void_p),
                 ("num_slots", ctypes.c_int32), ("out_norm_weight", ctypes.c_void_p),
-                ("out_gate", ctypes.c_void_p), ("out_norm_eps", ctypes.c_float)]
+                ("out_gate", ctypes.c_void_p), ("out_norm_eps", ctypes.c_float),
+                ("flags", ctypes.c_void_p), ("check_inputs", ctypes.c_int32)]
+
+
+# bits of kda_options.flags (include/kda.h)
+FLAG_DECAY_RANGE = 1
+FLAG_BAD_CU_SEQLENS = 2
 
 
 class KdaError(RuntimeError):
@@ -122,7 +128,7 @@ STAGES = {"intra": 0, "inter": 1}
 
 
 def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
-            num_slots=0, n=None, epilogue=None):
+            num_slots=0, n=None, epilogue=None, flags=None, check_inputs=False):
     """kda_options for the options, or None for the plain call, and the
     tensors it points to.  `epilogue` = (out_norm_weight, out_gate,
     out_norm_eps, d, out_gate_shape, dtype) or None."""
@@ -130,15 +136,21 @@ def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
         raise KdaError(f"unknown gate {gate!r}; one of {sorted(GATES)}")
     no_epi = epilogue is None or (epilogue[0] is None and epilogue[1] is None)
     if (gate == "log_alpha" and not l2norm_qk and not beta_logits and state_slots is None
-            and no_epi):
+            and no_epi and flags is None and not check_inputs):
         return None, ()
     keep = ()
+    f_ptr = None
+    if flags is not None:
+        _need(flags, "flags", torch.int32, (1,))
+        f_ptr, keep = flags.data_ptr(), (flags,)
+    elif check_inputs:
+        raise KdaError("check_inputs needs a flags tensor (int32 [1]) to report into")
     a_ptr = None
     if gate == "softplus":
         if gate_A is None:
             raise KdaError("gate='softplus' needs gate_A, fp32 [H]")
         _need(gate_A, "gate_A", torch.float32, (H,))
-        a_ptr, keep = gate_A.data_ptr(), (gate_A,)
+        a_ptr, keep = gate_A.data_ptr(), keep + (gate_A,)
     s_ptr = None
     if state_slots is not None:
         _need(state_slots, "state_slots", torch.int32, (n,))
@@ -156,7 +168,7 @@ def _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, H, state_slots=None,
             z_ptr, keep = z.data_ptr(), keep + (z,)
     return ctypes.pointer(KdaOptions(GATES[gate], a_ptr, float(gate_min), int(bool(l2norm_qk)),
                                      int(bool(beta_logits)), s_ptr, int(num_slots), w_ptr,
-                                     z_ptr, float(eps))), keep
+                                     z_ptr, float(eps), f_ptr, int(bool(check_inputs)))), keep
 
 
 def _need_gate(g, gate, dtype, shape):
@@ -231,6 +243,7 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                 beta_logits: bool = False, state_slots: Optional[torch.Tensor] = None,
                 out_norm_weight: Optional[torch.Tensor] = None,
                 out_gate: Optional[torch.Tensor] = None, out_norm_eps: float = 1e-6,
+                flags: Optional[torch.Tensor] = None, check_inputs: bool = False,
                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill (kda_fwd_chunked, or kda_fwd_chunked_ex with
     input-side fusion).
@@ -254,6 +267,12 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     out_norm_weight (fp32 [d]) turns on the output epilogue: every output
     row becomes o / sqrt(mean(o^2) + out_norm_eps) * out_norm_weight *
     sigmoid(out_gate) (out_gate [T, H, d] in v's dtype, or None).
+
+    Diagnostics: `flags` (int32 [1] device tensor, zeroed by the caller)
+    collects FLAG_DECAY_RANGE (a chunk's summed log-decay reached -80, the
+    precondition of the chunk algorithm) and, with check_inputs,
+    FLAG_BAD_CU_SEQLENS (cu_seqlens failed validation on the device; nothing
+    was computed).  Read it after synchronising.
     """
     if stage is not None and stage not in STAGES:
         raise KdaError(f"unknown stage {stage!r}; one of {sorted(STAGES)}")
@@ -264,7 +283,7 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     opt, _keep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
                          state_slots, nsl, args[6],
                          (out_norm_weight, out_gate, out_norm_eps, q.shape[2], tuple(o.shape),
-                          v.dtype))
+                          v.dtype), flags, check_inputs)
     if opt is not None:
         mask = 3 if stage is None else 1 << STAGES[stage]
         _check(library().kda_fwd_chunked_ex(opt, mask, *args), "kda_fwd_chunked_ex")
@@ -298,13 +317,15 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
              initial_state=None, chunk_size=64, output_final_state=True,
              out=None, final_state=None, workspace=None, gate="log_alpha", gate_A=None,
              gate_min=-5.0, l2norm_qk=False, beta_logits=False, state_slots=None,
-             out_norm_weight=None, out_gate=None, out_norm_eps=1e-6):
+             out_norm_weight=None, out_gate=None, out_norm_eps=1e-6, flags=None,
+             check_inputs=False):
     """Validate and marshal a kda_fwd_chunked call once, for repeated calls.
 
     Nothing is launched here.  Returns (call, stage_calls, o, final_state):
     `call()` runs the whole prefill and `stage_calls[name]()` one of its
     kernels ("intra", "inter"; kda_fwd_chunked_stage) on the same workspace.
-    The input-side fusion options are those of fwd_chunked.
+    The options (input-side fusion, slots, epilogue, diagnostics) are those
+    of fwd_chunked.
     """
     args, o, fs, ws, nsl = _prep_fwd(q, k, v, log_alpha, beta, cu_seqlens, num_seqs,
                                      initial_state, chunk_size, output_final_state, out,
@@ -312,7 +333,7 @@ def bind_fwd(q, k, v, log_alpha, beta, cu_seqlens=None, num_seqs=None,
     opt, akeep = _inputs(gate, gate_A, gate_min, l2norm_qk, beta_logits, q.shape[1],
                          state_slots, nsl, args[6],
                          (out_norm_weight, out_gate, out_norm_eps, q.shape[2], tuple(o.shape),
-                          v.dtype))
+                          v.dtype), flags, check_inputs)
     keep = (q, k, v, log_alpha, beta, cu_seqlens, initial_state, fs, o, ws, opt) + akeep
     lib = library()
     if opt is None:

@@ -114,7 +114,8 @@ size_t kda_fwd_chunked_workspace_size(int64_t total_tokens, int32_t num_seqs,
  * numerique de la decroissance cumulee"): inside any chunk the summed
  * log-decay of every channel must stay above -80, so that exp(-G) stays in
  * fp32/bf16 range.  Larger decays give inf/NaN outputs; use a smaller
- * chunk_size for such inputs.
+ * chunk_size for such inputs.  kda_fwd_chunked_ex reports a breach in
+ * kda_options.flags (KDA_FLAG_DECAY_RANGE).
  *
  * q, k, v, o and the states must be 16-byte aligned; log_alpha 16-byte;
  * beta and cu_seqlens 4-byte.  chunk_size must be 16, 32 or 64.
@@ -209,7 +210,27 @@ typedef struct {
   const float *out_norm_weight; /* [d_v] fp32, shared by the heads, or NULL */
   const void *out_gate;         /* [tokens or batch, H, d_v] in dtype, or NULL */
   float out_norm_eps;           /* > 0, finite                              */
+  /* -- diagnostics (prefill).  flags: an int32 device word, 4-byte aligned,
+     into which the prefill kernels OR the KDA_FLAG_* bits below; the caller
+     zeroes it before the call and reads it after synchronising.  NULL = no
+     diagnostics.  check_inputs != 0 (needs flags) first validates
+     cu_seqlens on the device: cu[0] = 0, non-decreasing, cu[num_seqs] =
+     total_tokens.  If that fails, KDA_FLAG_BAD_CU_SEQLENS is set and every
+     prefill kernel of the call returns without reading the inputs or
+     writing o, final_state or the workspace (contents that break the rules
+     are otherwise undefined behaviour).  kda_decode_step_ex ignores both. */
+  int32_t *flags;
+  int32_t check_inputs;
 } kda_options;
+
+/* Bits of kda_options.flags. */
+#define KDA_FLAG_DECAY_RANGE 1    /* some chunk's summed log-decay reached -80
+                                     in a channel: outside the precondition of
+                                     the chunk algorithm (see kda_fwd_chunked);
+                                     that chunk's outputs may be inf/NaN.  Set
+                                     by the intra-chunk kernel.               */
+#define KDA_FLAG_BAD_CU_SEQLENS 2 /* check_inputs: cu_seqlens failed
+                                     validation; nothing was computed.        */
 
 /*
  * kda_fwd_chunked with options (input-side fusion, state slots, output

@@ -180,6 +180,12 @@ def test_fwd_ex_rejects_bad_options_on_host(lib):
     assert _fwd_ex(lib, epi((1 << 20) + 4, None, 1e-6)) == 1     # weight 16-byte aligned
     assert _fwd_ex(lib, epi(1 << 20, (1 << 20) + 8, 1e-6)) == 1  # out_gate 16-byte aligned
     assert _fwd_ex(lib, epi(1 << 20, 1 << 20, 1e-6), wsb=16) == 1
+    def diag(flags, check):
+        return ctypes.pointer(kda.KdaOptions(0, None, 0.0, 0, 0, None, 0, None, None, 0.0,
+                                             flags, check))
+    assert _fwd_ex(lib, diag(None, 1)) == 1                      # check_inputs needs flags
+    assert _fwd_ex(lib, diag((1 << 20) + 2, 0)) == 1             # flags 4-byte aligned
+    assert _fwd_ex(lib, diag(1 << 20, 1), wsb=16) == 1           # valid, still size-checked
 
 
 def test_decode_ex_rejects_bad_options_on_host(lib):

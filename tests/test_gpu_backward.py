@@ -71,3 +71,31 @@ def test_backward_equal_lengths_no_final_gradient():
     w = kin.make_prefill(77, B=2, T=256, H=2, d=128, dtype=kin.BF16, chunk_size=64)
     do, _ = kin.backward_inputs(78, w.total_tokens, 2, 128, 2, kin.BF16)
     _check(w, do, None, _run(w, do, None, 64))
+
+
+def test_backward_headline_size_sampled_pairs():
+    """The headline prefill (B=2, H=8, T=2048, d=128, C=64, bf16) with a
+    final-state gradient, in the launch configuration the benchmark times;
+    (sequence, head) pairs are independent, so two sampled pairs are checked
+    against the fp64 oracle on their own tokens."""
+    print("[backward] headline B=2 H=8 T=2048 d=128, sampled pairs", flush=True)
+    w = kin.workload(1)
+    H, d, T = w.num_heads, 128, w.total_tokens // w.num_seqs
+    do, dsf = kin.backward_inputs(7, w.total_tokens, H, d, w.num_seqs, w.dtype)
+    got = _run(w, do, dsf, w.chunk_size)
+    q, k, v, g, b, s0 = w.f64()
+    do64 = kin.as_f64(do, w.dtype)
+    for seq, h in ((0, 3), (1, 6)):
+        rows = slice(seq * T, (seq + 1) * T)
+        pick = lambda a: a[rows, h:h + 1]
+        ref = oracle.recurrent_backward(
+            pick(q), pick(k), pick(v), pick(g), pick(b), pick(do64),
+            dsf[seq:seq + 1, h:h + 1].astype(np.float64),
+            initial_state=None if s0 is None else s0[seq:seq + 1, h:h + 1])
+        mine = {key: pick(got[key]) for key in ("dq", "dk", "dv", "dg", "dbeta")}
+        mine["ds0"] = got["ds0"][seq:seq + 1, h:h + 1]
+        errs = {key: relerr(mine[key], ref[key]) for key in mine}
+        print(f"  pair ({seq}, {h}) relerr " + " ".join(f"{kk}={e:.2e}" for kk, e in errs.items()),
+              flush=True)
+        for key, e in errs.items():
+            assert e <= TOL[w.dtype], f"pair ({seq}, {h}) {key} error {e:.3e}"
