@@ -377,6 +377,18 @@ def time_decode(torch, kda, cfg, n_steps, warmup):
 
 # ---------------------------------------------------------------- CPU oracle
 
+def _cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_prefill(w, seconds):
     """The fp64 oracle on whole copies of the headline batch, repeated until
     `seconds` of wall time have passed."""
@@ -392,7 +404,7 @@ def cpu_baseline_prefill(w, seconds):
         if el >= seconds:
             break
     return dict(value=reps * w.total_tokens / el, unit="tokens/s",
-                cores=oracle.num_threads(), kind="oracle",
+                cores=oracle.num_threads(), cpu=_cpu_model(), kind="oracle",
                 sample=f"{reps} whole passes of the headline prefill batch "
                        f"({w.total_tokens} tokens x {w.num_heads} heads), fp64, {el:.1f} s")
 
@@ -409,7 +421,8 @@ def cpu_baseline_decode(cfg, seconds):
         _, st = oracle.decode(*x, st)
         spent += time.perf_counter() - t0
         n += 1
-    return dict(value=n / spent, unit="steps/s", cores=oracle.num_threads(), kind="oracle",
+    return dict(value=n / spent, unit="steps/s", cores=oracle.num_threads(), cpu=_cpu_model(),
+                kind="oracle",
                 sample=f"{n} dependent decode steps of the full batch ({B} x {H} states), "
                        f"fp64, {spent:.1f} s (input generation excluded)")
 

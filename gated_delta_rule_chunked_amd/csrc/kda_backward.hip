@@ -48,31 +48,38 @@ namespace kda {
 namespace {
 
 constexpr int NT = 256;  // threads per workgroup, all kernels
-// LDS floats that block_mm<M, N, K> stages (at most 6,912 for 64 x 128 x 32 slices)
+
+// Products of the backward, on the fp32 matrix cores.  An M x N output
+// (M <= 64, N <= 128, multiples of 16) is cut into 16 x 16 tiles, tile
+// t = (t / (N/16), t % (N/16)) computed by wavefront t % 4 with
+// mma_f32_k16.  Operands: A(i, k) = TA ? A[k][i] : A[i][k] and
+// B(k, j) = TB ? B[j][k] : B[k][j], row-major with leading dimensions a
+// multiple of 4, 16-byte aligned, in global memory or LDS.  K slices of 32
+// are staged in LDS with 16-byte loads (the next slice in flight while this
+// one is used): A by rows and B by columns, the contraction index
+// contiguous, so that each operand of a 16-deep step is one 16-byte read
+// per lane.  Waves past the last tile repeat it (no branch around the
+// matrix instructions) and store nothing.
+template <int M, int N>
+struct MmTiles {
+  static_assert(M % 16 == 0 && N % 16 == 0 && M <= 64 && N <= 128, "shape");
+  static constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + 3) / 4;
+};
+
+// LDS floats that a product with contraction K stages (6,912 at most)
 template <int M, int N, int K>
 constexpr int mm_lds() {
   return (M + N) * ((K < 32 ? K : 32) + 4);
 }
 
-// out[i][j] = alpha * sum_k A(i, k) B(k, j) (+ out[i][j] when acc) for
-// i < M, j < N, with A(i, k) = TA ? A[k][i] : A[i][k] and
-// B(k, j) = TB ? B[j][k] : B[k][j] (row-major, leading dimensions a multiple
-// of 4, all pointers 16-byte aligned).  M <= 64, N <= 128, all multiples of
-// 16; out may be global memory or LDS and must not alias A or B.  The output
-// is cut into 16 x 16 tiles computed on the fp32 matrix cores (mma_f32_k16),
-// tile t = (t / (N/16), t % (N/16)) by wavefront t % 4.  K slices of 32 are
-// staged in LDS with 16-byte loads (the next slice in flight while this one
-// is used): A by rows and B by columns, both with the contraction index
-// contiguous, so that each operand of a 16-deep step is one 16-byte read per
-// lane.  `lds` holds mm_lds<M, N, K>() floats, 16-byte aligned.  Ends with a
-// barrier, so the block may use `out` at once.
+// c[q] (MmTiles<M, N>::TPW accumulators) += the wave's tiles of A B
+// (contraction K).  Ends with a barrier.
 template <int M, int N, int K, bool TA, bool TB>
-__device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
-                                         const float *B, int ldb, float alpha, bool acc,
-                                         float *lds) {
-  static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0 && M <= 64 && N <= 128, "shape");
+__device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
+                                              int ldb, float *lds) {
+  static_assert(K % 16 == 0, "contraction");
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, LDS row stride
-  constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + 3) / 4;
+  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
   constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
   float *sa = lds, *sb = lds + M * LK;  // sa[i][kk] = A(i, k0 + kk), sb[j][kk] = B(k0 + kk, j)
@@ -137,9 +144,6 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
       }
     }
   };
-  f32x4 c[TPW];
-#pragma unroll
-  for (int q = 0; q < TPW; ++q) c[q] = zero4();
   load(0);
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += KS) {
@@ -150,8 +154,6 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
     for (int ks = 0; ks < KS; ks += 16) {
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        // waves past the last tile repeat it (no branch around the matrix
-        // instructions) and store nothing
         const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
         const f32x4 a = *reinterpret_cast<const f32x4 *>(sa + (16 * (t / TN) + lr) * LK + ks + 4 * lg);
         const f32x4 b = *reinterpret_cast<const f32x4 *>(sb + (16 * (t % TN) + lr) * LK + ks + 4 * lg);
@@ -160,6 +162,16 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
     }
     __syncthreads();
   }
+}
+
+// out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
+// leading dimension ldo for both).  Ends with a barrier.
+template <int M, int N>
+__device__ __forceinline__ void mm_store(float *out, int ldo, const float *init, float alpha,
+                                         f32x4 *c) {
+  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the results reach ordinary registers here, in straight-line code, before
   // the branch on the tile index below
 #pragma unroll
@@ -168,12 +180,50 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
   for (int q = 0; q < TPW; ++q) {
     const int t = wv + 4 * q;
     if (TT % 4 == 0 || t < TT) {
-      float *o = out + (16 * (t / TN) + 4 * lg) * ldo + 16 * (t % TN) + lr;
+      const int at = (16 * (t / TN) + 4 * lg) * ldo + 16 * (t % TN) + lr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i * ldo] = alpha * c[q][i] + (acc ? o[i * ldo] : 0.f);
+      for (int i = 0; i < 4; ++i)
+        out[at + i * ldo] = alpha * c[q][i] + (init ? init[at + i * ldo] : 0.f);
     }
   }
   __syncthreads();
+}
+
+// out = alpha A B (+ out when acc).  `lds` holds mm_lds<M, N, K>() floats.
+template <int M, int N, int K, bool TA, bool TB>
+__device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
+                                         const float *B, int ldb, float alpha, bool acc,
+                                         float *lds) {
+  f32x4 c[MmTiles<M, N>::TPW];
+#pragma unroll
+  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K, TA, TB>(c, A, lda, B, ldb, lds);
+  mm_store<M, N>(out, ldo, acc ? out : nullptr, alpha, c);
+}
+
+// out = init + alpha A B (init has leading dimension ldo).
+template <int M, int N, int K, bool TA, bool TB>
+__device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
+                                              const float *A, int lda, const float *B, int ldb,
+                                              float *lds) {
+  f32x4 c[MmTiles<M, N>::TPW];
+#pragma unroll
+  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K, TA, TB>(c, A, lda, B, ldb, lds);
+  mm_store<M, N>(out, ldo, init, alpha, c);
+}
+
+// out = A1 B1 + A2 B2, both products accumulated in registers.
+template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2>
+__device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, int lda1,
+                                          const float *B1, int ldb1, const float *A2, int lda2,
+                                          const float *B2, int ldb2, float *lds) {
+  f32x4 c[MmTiles<M, N>::TPW];
+#pragma unroll
+  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K1, TA1, TB1>(c, A1, lda1, B1, ldb1, lds);
+  mm_accumulate<M, N, K2, TA2, TB2>(c, A2, lda2, B2, ldb2, lds);
+  mm_store<M, N>(out, ldo, nullptr, 1.f, c);
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
@@ -634,14 +684,28 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(
 }
 
 // ---- 4. per-tile gradients -------------------------------------------------
+// The C x C intermediates (dP, dT / dA, T^T dT) live in LDS; the C x d ones
+// go through the tile's workspace scratch.  Paired products accumulate in
+// registers.  The last pass forms dq, dk, dv and dbeta and, from the inputs
+// q and k, the per-element dG = k (dKt e^G - dKh e^-G - dKe e^(G_n - G)) +
+// q dQt e^G (= dKt Kt - dKh Kh + dQt Qt - dKe Ke), kept in LDS for the
+// reverse cumulative sum that gives dg.
 template <typename T, int D, int C>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
     T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
+  constexpr int MM = mm_lds<C, D, D>(), CC = C * C, CD = C * D;
+  // dG [C][D] and colsum(dKe Ke) [D] reuse the staging and dP / dM space
+  // once the last product is done; T^T dT's space then holds rowsum(dA M)
+  static_assert(CD + D <= MM + 2 * CC, "LDS reuse at the end");
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
-  __shared__ __align__(16) float s_mm[mm_lds<C, D, D>()];
+  __shared__ __align__(16) float s_big[MM + 3 * CC];
+  __shared__ float s_dgam[D];
+  float *s_mm = s_big, *s_dp = s_big + MM, *s_dt = s_dp + CC, *s_xm = s_dt + CC;
+  float *s_dG = s_big, *s_cs = s_big + CD, *s_dbr = s_xm;
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -649,99 +713,96 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-  constexpr int cd = C * D, cc = C * C;
   const float *sc = reinterpret_cast<const float *>(ws + L.sc) + tile * D * D;
   const float *dse = reinterpret_cast<const float *>(ws + L.dse) + tile * D * D;
-  const float *dun = reinterpret_cast<const float *>(ws + L.dun) + tile * cd;
+  const float *dun = reinterpret_cast<const float *>(ws + L.dun) + tile * CD;
   float *x = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
-  float *unew = x, *dot = x + cd, *dqt = x + 2 * cd, *dke = x + 3 * cd, *dw = x + 4 * cd;
-  float *dbkt = x + 5 * cd, *dbv = x + 6 * cd, *dkt = x + 7 * cd, *dkh = x + 8 * cd;
-  float *dp = x + 9 * cd, *dt = dp + cc, *xm = dp + 2 * cc, *da = dp + 3 * cc;
-  float *dgam = da + cc;
+  float *unew = x, *dot = x + CD, *dqt = x + 2 * CD, *dke = x + 3 * CD, *dw = x + 4 * CD;
+  float *dbkt = x + 5 * CD, *dbv = x + 6 * CD, *dkt = x + 7 * CD, *dkh = x + 8 * CD;
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
-  for (int e4 = tid; e4 < cd / 4; e4 += NT) {
+  for (int e4 = tid; e4 < CD / 4; e4 += NT) {
     const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
     const float live = r < n ? 1.f : 0.f;
-    const f32x4 o4 =
+    *reinterpret_cast<f32x4 *>(dot + 4 * e4) =
         load4_f32<T>(d_o + (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i) * live;
-    *reinterpret_cast<f32x4 *>(dot + 4 * e4) = o4;
-    *reinterpret_cast<f32x4 *>(unew + 4 * e4) = reinterpret_cast<const f32x4 *>(p.u)[e4];
   }
   __syncthreads();
-  block_mm<C, D, D, false, false>(unew, D, p.w, D, sc, D, -1.f, true, s_mm);  // U - W S
-  row_dots<D, D>(dgam, dse, sc, D, false);                                    // rowsum(dS_next * S)
-  block_mm<C, C, D, false, true>(dp, C, dot, D, unew, D, 1.f, false, s_mm);   // dO Unew^T
-  block_mm<C, D, D, false, true>(dqt, D, dot, D, sc, D, 1.f, false, s_mm);    // dO S^T
+  block_mm_init<C, D, D, false, false>(unew, D, p.u, -1.f, p.w, D, sc, D, s_mm);  // U - W S
+  row_dots<D, D>(s_dgam, dse, sc, D, false);                   // dgam = rowsum(dS_next * S)
+  block_mm<C, C, D, false, true>(s_dp, C, dot, D, unew, D, 1.f, false, s_mm);  // dO Unew^T
+  for (int e = tid; e < CC; e += NT)
+    if (e % C > e / C) s_dp[e] = 0.f;  // dP: lower incl. diagonal
+  __syncthreads();
+  // dQt = dO S^T + dP Kh
+  block_mm2<C, D, D, false, true, C, false, false>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D, s_mm);
   block_mm<C, D, D, false, true>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
   block_mm<C, D, D, false, true>(dw, D, dun, D, sc, D, -1.f, false, s_mm);    // -dUnew S^T
-  for (int e = tid; e < cc; e += NT)
-    if (e % C > e / C) dp[e] = 0.f;  // dP lower incl. diagonal
-  __syncthreads();
-  block_mm<C, D, C, false, false>(dqt, D, dp, C, p.kh, D, 1.f, true, s_mm);   // + dP Kh
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
-  block_mm<C, C, D, false, true>(dt, C, dw, D, p.kt, D, 1.f, false, s_mm);
-  block_mm<C, C, D, false, true>(dt, C, dun, D, p.vr, D, 1.f, true, s_mm);
-  for (int e = tid; e < cc; e += NT) dt[e] *= p.bt[e % C];
+  block_mm2<C, C, D, false, true, D, false, true>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D, s_mm);
+  for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e % C];
   __syncthreads();
-  block_mm<C, D, C, true, false>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);  // T^T dW
-  block_mm<C, D, C, true, false>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);  // T^T dUnew
-  block_mm<C, C, C, true, false>(xm, C, p.tm, C, dt, C, 1.f, false, s_mm);    // T^T dT
-  block_mm<C, C, C, false, true>(da, C, xm, C, p.tm, C, -1.f, false, s_mm);   // -T^T dT T^T
-  for (int e = tid; e < cc; e += NT) {
-    const int r = e / C, s = e % C;
-    if (s >= r) da[e] = 0.f;  // strictly lower
-  }
+  block_mm<C, D, C, true, false>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);   // T^T dW
+  block_mm<C, D, C, true, false>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);   // T^T dUnew
+  block_mm<C, C, C, true, false>(s_xm, C, p.tm, C, s_dt, C, 1.f, false, s_mm);  // T^T dT
+  block_mm<C, C, C, false, true>(s_dt, C, s_xm, C, p.tm, C, -1.f, false, s_mm); // dA (pre-mask)
+  for (int e = tid; e < CC; e += NT)
+    if (e % C >= e / C) s_dt[e] = 0.f;  // dA strictly lower
   __syncthreads();
-  // dbeta = rowsum(dA * M) + rowsum(dBKt * Kt) + rowsum(dBV * V), before dA
-  // is scaled into dM below
-  float *dbr = xm;  // [C], xm is free now
-  row_dots<C, C>(dbr, da, p.mm, C, false);
-  row_dots<C, D>(dbr, dbkt, p.kt, D, true);
-  row_dots<C, D>(dbr, dbv, p.vr, D, true);
-  for (int e = tid; e < cc; e += NT) da[e] *= p.bt[e / C];  // dM = Diag(beta) dA
+  row_dots<C, C>(s_dbr, s_dt, p.mm, C, false);  // rowsum(dA * M), before dA becomes dM
+  for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e / C];  // dM = Diag(beta) dA
   __syncthreads();
-  // dKt = Diag(beta) dBKt + dM Kh; dKh = dM^T Kt + dP^T Qt
-  block_mm<C, D, C, false, false>(dkt, D, da, C, p.kh, D, 1.f, false, s_mm);
-  block_mm<C, D, C, true, false>(dkh, D, da, C, p.kt, D, 1.f, false, s_mm);
-  block_mm<C, D, C, true, false>(dkh, D, dp, C, p.qt, D, 1.f, true, s_mm);
-  // outputs per row: dq, dk, dv (4 channels per thread)
-  for (int e4 = tid; e4 < cd / 4; e4 += NT) {
-    const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4)), e = 4 * e4;
-    if (r >= n) continue;
+  // dKt (without Diag(beta) dBKt) = dM Kh; dKh = dM^T Kt + dP^T Qt
+  block_mm<C, D, C, false, false>(dkt, D, s_dt, C, p.kh, D, 1.f, false, s_mm);
+  block_mm2<C, D, C, true, false, C, true, false>(dkh, D, s_dt, C, p.kt, D, s_dp, C, p.qt, D,
+                                                  s_mm);
+  // last pass: dq, dk, dv, dbeta, dG (LDS) and colsum(dKe Ke) (LDS)
+  for (int i = tid; i < D; i += NT) s_cs[i] = 0.f;
+  __syncthreads();
+  constexpr int RT = D / 4;  // threads per row
+  for (int e4 = tid; e4 < CD / 4; e4 += NT) {
+    const int r = e4 / RT, i = 4 * (e4 % RT), e = 4 * e4;
+    const bool live = r < n;
+    const float lm = live ? 1.f : 0.f;
+    const int64_t at = (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i;
+    const f32x4 qv = load4_f32<T>(q + at) * lm, kv = load4_f32<T>(k + at) * lm;
+    const f32x4 vv = load4_f32<T>(v + at) * lm;
     const f32x4 G = *reinterpret_cast<const f32x4 *>(p.gc + e);
     const f32x4 Gn = *reinterpret_cast<const f32x4 *>(p.gc + (C - 1) * D + i);
     const f32x4 vqt = *reinterpret_cast<const f32x4 *>(dqt + e);
-    const f32x4 vkt = *reinterpret_cast<const f32x4 *>(dkt + e) +
-                      p.bt[r] * *reinterpret_cast<const f32x4 *>(dbkt + e);
+    const f32x4 vbk = *reinterpret_cast<const f32x4 *>(dbkt + e);
     const f32x4 vkh = *reinterpret_cast<const f32x4 *>(dkh + e);
     const f32x4 vke = *reinterpret_cast<const f32x4 *>(dke + e);
     const f32x4 vbv = *reinterpret_cast<const f32x4 *>(dbv + e);
-    f32x4 oq, ok;
+    const float b = p.bt[r];
+    const f32x4 vkt = *reinterpret_cast<const f32x4 *>(dkt + e) + b * vbk;
+    f32x4 oq, ok, dG;
+    float rowp = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float eg = __expf(G[u]);
+      const float eg = __expf(G[u]), emg = __expf(-G[u]), egn = __expf(Gn[u] - G[u]);
+      const float tk = vkt[u] * eg, th = vkh[u] * emg, te = vke[u] * egn;
       oq[u] = vqt[u] * eg;
-      ok[u] = vkt[u] * eg + vkh[u] * __expf(-G[u]) + vke[u] * __expf(Gn[u] - G[u]);
+      ok[u] = tk + th + te;
+      dG[u] = kv[u] * (tk - th - te) + qv[u] * oq[u];
+      rowp += vbk[u] * kv[u] * eg + vbv[u] * vv[u];  // (dBKt * Kt) + (dBV * V)
+      atomicAdd(s_cs + i + u, te * kv[u]);           // dKe * Ke, summed over rows
     }
-    const int64_t at = (int64_t)(t0 + r) * rs + (int64_t)h * D + i;
-    store4_f32<T>(dq + at, oq);
-    store4_f32<T>(dk + at, ok);
-    store4_f32<T>(dv + at, vbv * p.bt[r]);
+    rowp = group_sum<RT>(rowp);
+    if (live) {
+      store4_f32<T>(dq + at, oq);
+      store4_f32<T>(dk + at, ok);
+      store4_f32<T>(dv + at, vbv * b);
+      *reinterpret_cast<f32x4 *>(s_dG + e) = dG;
+      if (e4 % RT == 0) dbeta[(int64_t)(t0 + r) * H + h] = s_dbr[r] + rowp;
+    }
   }
-  for (int r = tid; r < n; r += NT) dbeta[(int64_t)(t0 + r) * H + h] = dbr[r];
+  __syncthreads();
   // dg: reverse cumulative sum of dG over the chunk plus dG_n, per channel
-  // (dKt here is the full Diag(beta) dBKt + dM Kh)
-  if (tid < D) {
-    const int i = tid;
-    float dgn = dgam[i] * p.gam[i];
-#pragma unroll 8
-    for (int r = 0; r < C; ++r) dgn += dke[r * D + i] * p.ke[r * D + i];
-    float run = dgn;
+  for (int i = tid; i < D; i += NT) {
+    float run = s_dgam[i] * p.gam[i] + s_cs[i];
     for (int r = n - 1; r >= 0; --r) {
-      const int e = r * D + i;
-      run += (dkt[e] + p.bt[r] * dbkt[e]) * p.kt[e] - dkh[e] * p.kh[e] + dqt[e] * p.qt[e] -
-             dke[e] * p.ke[e];
+      run += s_dG[r * D + i];
       dg[(int64_t)(t0 + r) * rs + (int64_t)h * D + i] = run;
     }
   }
@@ -773,8 +834,8 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
                      a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf,
                      a.ds0, a.lay, a.ws);
   if (tiles > 0)
-    hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, d_o,
-                       a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
+    hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k,
+                       v, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
                        reinterpret_cast<T *>(a.dq), reinterpret_cast<T *>(a.dk),
                        reinterpret_cast<T *>(a.dv), a.dg, a.dbeta, a.lay, a.ws);
   return hipGetLastError();
