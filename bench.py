@@ -147,7 +147,10 @@ def kernel_bytes(stage, token_heads, pairs, d, E, C, with_s0, raw=False, epilogu
         return token_heads * (3 * E * d + gate + 4 + 4 * E * d + E * CK + 4 * d / C)
     if stage == "inter":      # read Qt, W, U, Ke, P, e^G_n; write o; states
         epi = 3 * E * d if epilogue else 0  # epilogue pass: read o, z_o; write o
-        return (token_heads * (5 * E * d + E * CK + 4 * d / C + epi) +
+        # P is lower triangular: with C = 64 the token K-step 32..63 of token
+        # blocks 0 and 1 is zero and not read (a quarter of P)
+        p_read = E * CK * (0.75 if C == 64 else 1.0)
+        return (token_heads * (4 * E * d + p_read + E * d + 4 * d / C + epi) +
                 pairs * state_bytes(d) * (2 if with_s0 else 1))
     raise ValueError(stage)
 
