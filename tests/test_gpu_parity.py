@@ -228,3 +228,28 @@ def test_decode_matches_one_token_prefill():
     assert e[0] < 2.0 ** -8 + 1e-5, "decode o beyond bf16 output rounding"
     assert e[1] < 1e-5, "decode state beyond fp32 rounding"
     assert max(e[2:]) < 2e-2
+
+
+def test_decode_full_batch_steps():
+    """The decode workload at full size and in the benchmark's launch
+    configuration (256 x 32 fp32 states, d = 128, bf16 inputs drawn per step
+    as the benchmark draws them): 24 dependent steps, every output and the
+    states after the last step against the oracle."""
+    cfg = kin.WORKLOADS[4]
+    B, H, d, steps = cfg["batch"], cfg["H"], cfg["d"], 24
+    print(f"[parity] decode full batch {B} x {H}, {steps} steps", flush=True)
+    kda = _kda()
+    st0 = kin.decode_states(B, H, d, s0_std=cfg["s0_std"])
+    state = f32_device(st0)
+    ref = st0.astype(np.float64)
+    worst = 0.0
+    for s in range(steps):
+        x = kin.decode_step(s, B, H, d, dtype=kin.BF16, g_mu=cfg["g_mu"], g_sigma=cfg["g_sigma"])
+        o = kda.decode_step(to_device(x.q, kin.BF16), to_device(x.k, kin.BF16),
+                            to_device(x.v, kin.BF16), f32_device(x.g), f32_device(x.beta), state)
+        q, k, v, g, b = x.f64()
+        o_ref, ref = oracle.decode(q, k, v, g, b, ref)
+        worst = max(worst, relerr(from_device(o), o_ref))
+    es = relerr(from_device(state), ref)
+    print(f"  decode relerr worst o={worst:.3e} S={es:.3e}", flush=True)
+    assert worst <= TOL[kin.BF16] and es <= TOL[kin.BF16]
