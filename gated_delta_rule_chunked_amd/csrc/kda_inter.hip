@@ -14,8 +14,8 @@
 //   S   <- Diag(e^{G_n}) S + Ke^T Unew   (state after the chunk)
 //
 // Every product multiplies S from the left, so the d_v columns of S evolve
-// independently: a workgroup owns one (sequence, head, 16-column slice) and
-// walks that sequence's chunks.  Its four wavefronts split the rows: wave w
+// independently: a workgroup owns one (sequence, head, column slice of 16 or
+// 32 columns) and walks that sequence's chunks.  Its four wavefronts split the rows: wave w
 // computes token block w of Unew and O and channel blocks w*CBW.. of S, so
 // all four SIMDs issue matrix-core work and each wave loads only its quarter
 // of W, Qt, P and Ke.  The blocks meet through two tiny LDS exchanges per
@@ -39,7 +39,7 @@
 
 namespace kda {
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, int CT>
 struct InterOps {
   using F = typename Frag<T>::type;
   using V4 = typename Vec4<T>::type;
@@ -53,13 +53,17 @@ struct InterOps {
     F wA[KD];       // W rows of the wave's token block (K = channels)
     F qA[KD];       // Qt rows of the wave's token block
     F pA[KC];       // P rows of the wave's token block (K = tokens)
-    V4 uv;          // U of the wave's token block, output-tile layout
+    V4 uv[CT];      // U of the wave's token block, one output tile per column tile
     F kA[CBW][KC];  // Ke^T rows of the wave's channel blocks (K = tokens)
     f32x4 gv[CBW];  // e^{G_n} of the wave's channel rows
   };
 };
 
-template <typename T, int D, int C, int PF>
+// CT: 16-column tiles per workgroup (a slice of 16 CT columns).  Two tiles
+// share every W, Qt, P and Ke^T fragment a wave loads, halving the operand
+// bytes per column; the launch takes them when the 16-column slices would
+// need more than one round of workgroups on the GPU.
+template <typename T, int D, int C, int PF, int CT>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *__restrict__ qt, const T *__restrict__ w, const T *__restrict__ ut,
     const T *__restrict__ ket, const T *__restrict__ pm,
@@ -67,15 +71,15 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const int *__restrict__ seq_first, int N, int H, int seq_len,
     const float *__restrict__ s0, float *__restrict__ s_final,
     const int *__restrict__ slots, int num_slots, const OptArgs in, T *__restrict__ o) {
-  using Ops = InterOps<T, D, C>;
+  using Ops = InterOps<T, D, C, CT>;
   using F = typename Ops::F;
   using V4 = typename Ops::V4;
   using Buf = typename Ops::Buf;
   constexpr int NRB = C / 16, NCB = Ops::NCB, CK = Ops::CK, KD = Ops::KD, KC = Ops::KC;
-  constexpr int CBW = Ops::CBW, NS = D / 16;
+  constexpr int CBW = Ops::CBW, NS = D / (16 * CT);
 
-  __shared__ V4 sS[NCB][64];     // S (operand type), one output tile per channel block
-  __shared__ V4 sU[2 * KC][64];  // Unew (operand type), one tile per token block
+  __shared__ V4 sS[CT][NCB][64];     // S (operand type), one output tile per channel block
+  __shared__ V4 sU[CT][2 * KC][64];  // Unew (operand type), one tile per token block
 
   if (inputs_rejected(in)) return;
   const int b = blockIdx.x;
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id());  // scalar: branches stay uniform
   const int lr = lane & 15, lg = lane >> 4;
-  const int col0 = slice * 16;
+  const int col0 = slice * 16 * CT;
   // Roles.  With C = 64 and d % 64 == 0 every wave owns a token block and
   // CBW channel blocks and nothing below branches.  Smaller shapes leave some
   // waves without a block; those still load (clamped, in-bounds) operands so
@@ -118,24 +122,30 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     spair = has_state ? (int64_t)sl * H + h : 0;
   }
 
-  // the wave's state rows: S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
-  f32x4 S[CBW];
+  // the wave's state: S[j][t][i] = S[16 cb + 4 lg + i][col0 + 16 t + lr], cb = wv CBW + j
+  f32x4 S[CBW][CT];
   const int64_t sbase = spair * D * D + col0 + lr;
 #pragma unroll
   for (int j = 0; j < CBW; ++j) {
     const int cb = wv * CBW + j;
-    f32x4 x = zero4();
-    if (cb < NCB) {
-      if (s0 && has_state) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = s0[sbase + (int64_t)(16 * cb + 4 * lg + i) * D];
+    for (int t = 0; t < CT; ++t) {
+      f32x4 x = zero4();
+      if (cb < NCB) {
+        if (s0 && has_state) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            x[i] = s0[sbase + 16 * t + (int64_t)(16 * cb + 4 * lg + i) * D];
+        }
+        sS[t][cb][lane] = vec4_from_f32<T>(x);
       }
-      sS[cb][lane] = vec4_from_f32<T>(x);
+      S[j][t] = x;
     }
-    S[j] = x;
   }
-  for (int e = tid; e < (2 * KC - NRB) * 64; e += 256)  // padding token blocks stay zero
-    sU[NRB + e / 64][e % 64] = vec4_from_f32<T>(zero4());
+  for (int e = tid; e < CT * (2 * KC - NRB) * 64; e += 256) {  // padding token blocks stay zero
+    const int t = e / ((2 * KC - NRB) * 64), r = e % ((2 * KC - NRB) * 64);
+    sU[t][NRB + r / 64][r % 64] = vec4_from_f32<T>(zero4());
+  }
   __syncthreads();
 
   auto tile_of = [&](int ci) { return (int64_t)(first + ci) * H + h; };
@@ -144,7 +154,9 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *wt = w + tile * (C * D) + (rb * KD * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < KD; ++ks) B.wA[ks] = load8<T>(wt + ks * 512);
-    B.uv = load4<T>(ut + tile * (D * C) + ((slice * NRB + rb) * 64 + lane) * 4);
+#pragma unroll
+    for (int t = 0; t < CT; ++t)
+      B.uv[t] = load4<T>(ut + tile * (D * C) + (((slice * CT + t) * NRB + rb) * 64 + lane) * 4);
   };
   auto load_qp = [&](Buf &B, int ci) {
     const int64_t tile = tile_of(ci);
@@ -182,41 +194,53 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const int tc = t0 + ci * C;
     const int rows = min(C, len - ci * C);
 
-    // S entering the chunk, as K-step operands over channels
-    F sb[KD];
+    // S entering the chunk, as K-step operands over channels, per column tile
+    F sb[CT][KD];
 #pragma unroll
-    for (int ks = 0; ks < KD; ++ks) sb[ks] = join4(sS[2 * ks][lane], sS[2 * ks + 1][lane]);
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks)
+        sb[t][ks] = join4(sS[t][2 * ks][lane], sS[t][2 * ks + 1][lane]);
 
-    // Unew = U - W S for the wave's token block (two accumulators in flight)
+    // Unew = U - W S for the wave's token block (two accumulators per tile)
     if (has_rb) {
-      f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) {
-        if (ks & 1) a1 = mma_k32(B.wA[ks], sb[ks], a1);
-        else a0 = mma_k32(B.wA[ks], sb[ks], a0);
+      for (int t = 0; t < CT; ++t) {
+        f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KD; ++ks) {
+          if (ks & 1) a1 = mma_k32(B.wA[ks], sb[t][ks], a1);
+          else a0 = mma_k32(B.wA[ks], sb[t][ks], a0);
+        }
+        sU[t][rb][lane] = vec4_from_f32<T>(to_f32x4(B.uv[t]) - (a0 + a1));
       }
-      sU[rb][lane] = vec4_from_f32<T>(to_f32x4(B.uv) - (a0 + a1));
     }
     __builtin_amdgcn_sched_barrier(0);
     load_wu(B, nxt);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
-    // Unew of the whole chunk as K-step operands over tokens
-    F ub[KC];
+    // Unew of the whole chunk as K-step operands over tokens, per column tile
+    F ub[CT][KC];
 #pragma unroll
-    for (int ks = 0; ks < KC; ++ks) ub[ks] = join4(sU[2 * ks][lane], sU[2 * ks + 1][lane]);
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks)
+        ub[t][ks] = join4(sU[t][2 * ks][lane], sU[t][2 * ks + 1][lane]);
 
     // S <- Diag(e^{G_n}) S + Ke^T Unew for the wave's channel blocks
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
       if (ALL_CB || cb < NCB) {
-        f32x4 acc = S[j] * B.gv[j];
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[ks], acc);
-        S[j] = acc;
-        sS[cb][lane] = vec4_from_f32<T>(acc);
+        for (int t = 0; t < CT; ++t) {
+          f32x4 acc = S[j][t] * B.gv[j];
+#pragma unroll
+          for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[t][ks], acc);
+          S[j][t] = acc;
+          sS[t][cb][lane] = vec4_from_f32<T>(acc);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -225,23 +249,31 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 
     // O = Qt S + P Unew for the wave's token block
     if (has_rb) {
-      f32x4 oc = zero4();
+      V4 ov[CT];
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[ks], oc);
+      for (int t = 0; t < CT; ++t) {
+        f32x4 oc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
-      // read (and convert) before any branch: matrix-core results are read
-      // only in straight-line code after the instructions that produce them;
-      // "+ 0" makes it a real VALU read also when T is fp32
-      const V4 ov = vec4_from_f32<T>(oc + 0.f);
+        for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[t][ks], oc);
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[t][ks], oc);
+        // read (and convert) before any branch: matrix-core results are read
+        // only in straight-line code after the instructions that produce them;
+        // "+ 0" makes it a real VALU read also when T is fp32
+        ov[t] = vec4_from_f32<T>(oc + 0.f);
+      }
       T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
       if (rows == C) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) op[i * rs] = ov[i];
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) op[i * rs + 16 * t] = ov[t][i];
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * rb + 4 * lg + i < rows) op[i * rs] = ov[i];
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * rb + 4 * lg + i < rows) op[i * rs + 16 * t] = ov[t][i];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -269,21 +301,37 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
       const int cb = wv * CBW + j;
       if (cb < NCB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_final[sbase + (int64_t)(16 * cb + 4 * lg + i) * D] = S[j][i];
+        for (int t = 0; t < CT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s_final[sbase + 16 * t + (int64_t)(16 * cb + 4 * lg + i) * D] = S[j][t][i];
       }
     }
   }
 }
 
-template <typename T, int D, int C>
-static hipError_t launch_inter_c(const FwdArgs &a) {
-  constexpr int NS = D / 16;
+// Compute units of the current device (0 if unknown), looked up once per
+// device ordinal.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <typename T, int D, int C, int CT>
+static hipError_t launch_inter_ct(const FwdArgs &a) {
+  constexpr int NS = D / (16 * CT);
   const int pairs = a.num_seqs * a.num_heads;
   const int units = (pairs + 7) / 8;
   const dim3 grid((unsigned)(8 * units * NS));
   char *ws = a.ws;
-  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3, CT>), grid, dim3(256), 0, a.stream,
                      reinterpret_cast<const T *>(ws + a.lay.qt),
                      reinterpret_cast<const T *>(ws + a.lay.w),
                      reinterpret_cast<const T *>(ws + a.lay.ut),
@@ -294,6 +342,16 @@ static hipError_t launch_inter_c(const FwdArgs &a) {
                      a.num_heads, a.seq_len, a.s0, a.s_final, a.in.slots, a.in.num_slots,
                      a.in, reinterpret_cast<T *>(a.o));
   return hipGetLastError();
+}
+
+// 16-column slices when they fit in one round of workgroups (one per CU),
+// 32-column slices (half the workgroups and operand bytes) otherwise.
+template <typename T, int D, int C>
+static hipError_t launch_inter_c(const FwdArgs &a) {
+  const int64_t units = ((int64_t)a.num_seqs * a.num_heads + 7) / 8;
+  const int cus = device_cus();
+  if (cus > 0 && 8 * units * (D / 16) > cus) return launch_inter_ct<T, D, C, 2>(a);
+  return launch_inter_ct<T, D, C, 1>(a);
 }
 
 template <typename T, int D>
