@@ -344,13 +344,20 @@ static hipError_t launch_inter_ct(const FwdArgs &a) {
   return hipGetLastError();
 }
 
-// 16-column slices when they fit in one round of workgroups (one per CU),
-// 32-column slices (half the workgroups and operand bytes) otherwise.
+// Slice width: the fewest rounds of workgroups (one per CU at a time), and
+// the narrowest slice among equals (shortest dependent chain per chunk).
 template <typename T, int D, int C>
 static hipError_t launch_inter_c(const FwdArgs &a) {
   const int64_t units = ((int64_t)a.num_seqs * a.num_heads + 7) / 8;
-  const int cus = device_cus();
-  if (cus > 0 && 8 * units * (D / 16) > cus) return launch_inter_ct<T, D, C, 2>(a);
+  const int64_t cus = device_cus();
+  auto rounds = [&](int ct) { return cus > 0 ? (8 * units * (D / (16 * ct)) + cus - 1) / cus : 1; };
+  int ct = 1;
+  for (int c = 2; c <= 4 && 16 * c <= D; c *= 2)
+    if (rounds(c) < rounds(ct)) ct = c;
+  if constexpr (D >= 64) {
+    if (ct == 4) return launch_inter_ct<T, D, C, 4>(a);
+  }
+  if (ct == 2) return launch_inter_ct<T, D, C, 2>(a);
   return launch_inter_ct<T, D, C, 1>(a);
 }
 
