@@ -14,8 +14,8 @@
 //   S   <- Diag(e^{G_n}) S + Ke^T Unew   (state after the chunk)
 //
 // Every product multiplies S from the left, so the d_v columns of S evolve
-// independently: a workgroup owns one (sequence, head, column slice of 16 or
-// 32 columns) and walks that sequence's chunks.  Its four wavefronts split the rows: wave w
+// independently: a workgroup owns one (sequence, head, column slice of 16,
+// 32 or 64 columns) and walks that sequence's chunks.  Its four wavefronts split the rows: wave w
 // computes token block w of Unew and O and channel blocks w*CBW.. of S, so
 // all four SIMDs issue matrix-core work and each wave loads only its quarter
 // of W, Qt, P and Ke.  The blocks meet through two tiny LDS exchanges per
