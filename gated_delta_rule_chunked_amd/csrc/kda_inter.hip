@@ -59,10 +59,10 @@ struct InterOps {
   };
 };
 
-// CT: 16-column tiles per workgroup (a slice of 16 CT columns).  Two tiles
-// share every W, Qt, P and Ke^T fragment a wave loads, halving the operand
-// bytes per column; the launch takes them when the 16-column slices would
-// need more than one round of workgroups on the GPU.
+// CT: 16-column tiles per workgroup (a slice of 16 CT columns).  The tiles
+// share every W, Qt, P and Ke^T fragment a wave loads, so wider slices halve
+// the operand bytes per column but lengthen each serial step; the launch
+// takes them only where they cut the rounds of workgroups on the GPU.
 template <typename T, int D, int C, int PF, int CT>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *__restrict__ qt, const T *__restrict__ w, const T *__restrict__ ut,

@@ -20,8 +20,10 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers, row-major and contiguous.  The
  *     caller owns and allocates every buffer, the workspace included; the
- *     library allocates nothing, keeps no state between calls and may be
- *     called from several host threads on different streams.
+ *     library allocates nothing and may be called from several host
+ *     threads on different streams.  Between calls it keeps only what it
+ *     reads once per device and kernel: the CU count (which picks the
+ *     inter-chunk slice width) and kernel LDS attributes.
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
  *     stream) and return.  Errors raised while the kernels run surface at
  *     the caller's next synchronisation, as for any HIP launch.
