@@ -253,3 +253,20 @@ def test_decode_full_batch_steps():
     es = relerr(from_device(state), ref)
     print(f"  decode relerr worst o={worst:.3e} S={es:.3e}", flush=True)
     assert worst <= TOL[kin.BF16] and es <= TOL[kin.BF16]
+
+
+@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
+                                     (kin.F32, 64), (kin.F32, 32)])
+@pytest.mark.parametrize("n_seqs", [10, 40, 65])
+def test_many_pairs_every_slice_width(dtype, d, n_seqs):
+    """Many short packed sequences (4 heads each, lengths 1..150, initial
+    states): as the (sequence, head) count grows the inter-chunk launch moves
+    from 16- to 32- and 64-column slices (on a 256-CU device: 40 and 260
+    pairs at d = 128, 160 pairs at d = 64 and 32), every width against the
+    oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"[parity] many pairs dtype={dtype} d={d} seqs={n_seqs} heads=4 cus={cus}", flush=True)
+    w = kin.make_prefill(300 + d + n_seqs, B=n_seqs, H=4, d=d, dtype=dtype, chunk_size=32,
+                         len_range=(1, 150), s0_std=0.05)
+    o, s = _run_gpu(w)
+    _check(w, o, s)
