@@ -17,10 +17,19 @@
 // once per step and would only evict other data from the caches (measured
 // about 7% faster on MI355X than plain accesses for 256 x 32 states).
 //
-// Block = one state.  Thread t owns float4 column group t % (d/4) and rows
-// r = t / (d/4) + i * (threads / (d/4)); at every step i the block reads or
-// writes a contiguous run of rows.  Column sums are reduced over the lanes of
-// a wavefront with cross-lane shuffles and over wavefronts through LDS.
+// Block = one state.  Thread t owns float4 column group t % (d/4) and the
+// RPT consecutive rows from (t / (d/4)) * RPT, so its slices of k, q and the
+// gate are a few vector loads, issued ahead of the state rows.  Column sums
+// are reduced over the lanes of a wavefront with cross-lane shuffles and over
+// wavefronts through LDS.
+//
+// Occupancy.  For d = 128 and a batch of several rounds of the GPU, each
+// workgroup also reserves LDS that it does not use, so that a CU holds two
+// workgroups (eight wavefronts, two states streaming) instead of the three
+// its registers would allow.  Measured on MI355X for 256 x 32 states: two per
+// CU streams about 6.1 TB/s, three about 5.5 and one about 5.4; the fewer
+// states are in flight, the fewer DRAM rows the CU's requests spread over,
+// until too few requests are left in flight to cover the latency.
 //
 // Input-side fusion (kda_options): with RAW the gate input is z and the gate
 // function gives g per key channel.  With l2norm_qk, q and k enter the step
@@ -42,7 +51,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   constexpr int NRG = NT / NCQ;      // row groups
   constexpr int RPT = D / NRG;       // rows per thread
   constexpr int NW = NT / 64;        // wavefronts
-  static_assert(NT % 64 == 0 && 64 % NCQ == 0 && D % NRG == 0, "decode shape");
+  static_assert(NT % 64 == 0 && 64 % NCQ == 0 && D % NRG == 0 && RPT % 4 == 0,
+                "decode shape");
 
   __shared__ f32x4 s_x[NW][NCQ];
   __shared__ f32x4 s_y[NW][NCQ];
@@ -66,30 +76,45 @@ __global__ __launch_bounds__(NT) void decode_kernel(
   const T *kp = k + p * D;
   const float eA = (RAW && in.gate == KDA_GATE_SOFTPLUS) ? __expf(in.gate_A[p % in.heads]) : 0.f;
 
+  const int r0 = rg * RPT;  // first row of this thread
+  float kr[RPT], qr[RPT], gr[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT / 4; ++j) {
+    const f32x4 k4 = to_f32x4(load4<T>(kp + r0 + 4 * j));
+    const f32x4 q4 = to_f32x4(load4<T>(qp + r0 + 4 * j));
+    f32x4 g4;
+    if constexpr (RAW) {
+      const f32x4 z4 = to_f32x4(load4<T>(reinterpret_cast<const T *>(gate) + p * D + r0 + 4 * j));
+      g4 = in.gate == KDA_GATE_SOFTPLUS ? gate_softplus(z4, eA) : gate_sigmoid(z4, in.gate_min);
+    } else {
+      g4 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(gate) + p * D + r0 +
+                                              4 * j);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kr[4 * j + e] = k4[e];
+      qr[4 * j + e] = q4[e];
+      gr[4 * j + e] = g4[e];
+    }
+  }
   f32x4 Sv[RPT];
-  float a[RPT], kr[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (r0 + i) * D + 4 * cq));
+  float a[RPT];
   f32x4 x = zero4(), y = zero4();
   float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rg + i * NRG;
-    Sv[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + r * D + 4 * cq));
-    float gr;
-    if constexpr (RAW) {
-      const float z = to_f32(reinterpret_cast<const T *>(gate)[p * D + r]);
-      gr = in.gate == KDA_GATE_SOFTPLUS ? gate_softplus(z, eA) : gate_sigmoid(z, in.gate_min);
-    } else {
-      gr = reinterpret_cast<const float *>(gate)[p * D + r];
-    }
-    a[i] = __expf(gr);
-    kr[i] = to_f32(kp[r]);
-    const float qr = to_f32(qp[r]);
-    const float ka = a[i] * kr[i], qa = a[i] * qr;
-    x += Sv[i] * ka;
-    y += Sv[i] * qa;
-    kq += kr[i] * qr;
+    a[i] = __expf(gr[i]);
+    kq += kr[i] * qr[i];
     kk += kr[i] * kr[i];
-    qq += qr * qr;
+    qq += qr[i] * qr[i];
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    x += Sv[i] * (a[i] * kr[i]);
+    y += Sv[i] * (a[i] * qr[i]);
   }
   // reduce over the row groups of this wavefront (lanes cq + NCQ * m)
 #pragma unroll
@@ -158,12 +183,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(
     store4_f32<T>(o + p * D + 4 * cq, ov);
   }
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + i * NRG;
+  for (int i = 0; i < RPT; ++i)
     __builtin_nontemporal_store(a[i] * Sv[i] + (rk * kr[i]) * u,
-                                reinterpret_cast<f32x4 *>(S + r * D + 4 * cq));
-  }
+                                reinterpret_cast<f32x4 *>(S + (r0 + i) * D + 4 * cq));
 }
+
+// LDS that a d = 128 workgroup reserves without using it: with the kernel's
+// own 4 KiB, three workgroups would need more than a CU's 160 KiB, two fit.
+constexpr unsigned kDecodeLdsReserve = 56 * 1024;
 
 template <typename T, int D, int NT>
 static void launch_decode_k(const void *q, const void *k, const void *v, const void *gate,
@@ -173,11 +200,15 @@ static void launch_decode_k(const void *q, const void *k, const void *v, const v
   const T *kk = reinterpret_cast<const T *>(k);
   const T *vv = reinterpret_cast<const T *>(v);
   T *oo = reinterpret_cast<T *>(o);
+  // two workgroups per CU once the batch takes several rounds of the GPU;
+  // a smaller batch keeps every state in flight at once
+  const int cus = device_cus();
+  const unsigned lds = (D == 128 && cus > 0 && pairs >= 4 * cus) ? kDecodeLdsReserve : 0;
   if (in.gate == KDA_GATE_LOG_ALPHA)
-    hipLaunchKernelGGL((decode_kernel<T, D, NT, false>), dim3(pairs), dim3(NT), 0, s, qq, kk,
+    hipLaunchKernelGGL((decode_kernel<T, D, NT, false>), dim3(pairs), dim3(NT), lds, s, qq, kk,
                        vv, gate, beta, in, state, oo);
   else
-    hipLaunchKernelGGL((decode_kernel<T, D, NT, true>), dim3(pairs), dim3(NT), 0, s, qq, kk,
+    hipLaunchKernelGGL((decode_kernel<T, D, NT, true>), dim3(pairs), dim3(NT), lds, s, qq, kk,
                        vv, gate, beta, in, state, oo);
 }
 

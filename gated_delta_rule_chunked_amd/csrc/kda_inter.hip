@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 
 // Compute units of the current device (0 if unknown), looked up once per
 // device ordinal.
-static int device_cus() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

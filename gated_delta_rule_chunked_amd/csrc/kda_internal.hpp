@@ -164,6 +164,8 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Compute units of the current device (0 if unknown); cached per device.
+int device_cus();
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
 // Validates cu_seqlens [N + 1] (cu[0] = 0, non-decreasing, cu[N] = total) and
 // ORs KDA_FLAG_BAD_CU_SEQLENS into *flags when it fails.
