@@ -420,6 +420,19 @@ struct ChainShape {
   static constexpr int NRB = C / 16, NCB = D / 16, CBW = (NCB + 3) / 4;
 };
 
+// Chain workgroup b serves slice (b / 8) % NS of pair 8 ((b / 8) / NS) + b % 8:
+// the slices of one (sequence, head) share blockIdx % 8, so they run on one
+// XCD and its L2 serves each chunk's operands to all of them.  The grid is
+// 8 * ceil(pairs / 8) * NS; false for a workgroup past the last pair.
+template <int NS>
+__device__ __forceinline__ bool chain_block(int b, int pairs, int *slice, int *pair) {
+  const int local = b >> 3;
+  *slice = local % NS;
+  *pair = (local / NS) * 8 + (b & 7);
+  return *pair < pairs;
+}
+inline unsigned chain_grid(int pairs, int ns) { return 8u * (unsigned)((pairs + 7) / 8) * ns; }
+
 template <int D, int C>
 constexpr size_t state_lds_bytes() {
   using Sh = ChainShape<D, C>;
@@ -436,18 +449,17 @@ constexpr size_t dstate_lds_bytes() {
 // staged whole in LDS, the next chunk's (and its U tile and gamma) being
 // loaded into registers while this one is computed.
 template <int D, int C>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(
-    const int *__restrict__ cu, int N, int H, int seq_len, const float *__restrict__ s0,
-    BwdLayout L, char *ws) {
+__device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, int N, int H,
+                                            int seq_len, const float *__restrict__ s0,
+                                            BwdLayout L, char *ws, float *sm) {
   using Sh = ChainShape<D, C>;
   constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, NRB = Sh::NRB, NCB = Sh::NCB;
   constexpr int CBW = Sh::CBW;
-  extern __shared__ __align__(16) float sm[];
   float *sW = sm, *sK = sW + C * LD;          // [C][LD] row-major
   float *sSt = sK + C * LD, *sUt = sSt + 16 * LD;  // S^T [16][LD], Unew^T [16][LU]
-  const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
+  int slice, pair;
+  if (!chain_block<NS>(b, N * H, &slice, &pair)) return;
   const int seq = pair / H, h = pair % H;
-  if (seq >= N) return;
   const int col0 = slice * 16;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -541,18 +553,19 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(
 
 // ---- 3. state gradients, chunks in reverse ---------------------------------
 template <typename T, int D, int C>
-__global__ __launch_bounds__(NT) void bwd_dstate_kernel(
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
-    const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
+__device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
+                                             const int *__restrict__ cu, int N, int H,
+                                             int seq_len, const float *__restrict__ dsf,
+                                             float *__restrict__ ds0, BwdLayout L, char *ws,
+                                             float *sm) {
   using Sh = ChainShape<D, C>;
   constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, LP = Sh::LP, NRB = Sh::NRB;
   constexpr int NCB = Sh::NCB, CBW = Sh::CBW;
-  extern __shared__ __align__(16) float sm[];
   float *sW = sm, *sK = sW + C * LD, *sQ = sK + C * LD, *sP = sQ + C * LD;  // row-major
   float *sDt = sP + C * LP, *sOt = sDt + 16 * LD, *sUt = sOt + 16 * LU;     // transposed
-  const int slice = blockIdx.x % NS, pair = blockIdx.x / NS;
+  int slice, pair;
+  if (!chain_block<NS>(b, N * H, &slice, &pair)) return;
   const int seq = pair / H, h = pair % H;
-  if (seq >= N) return;
   const int col0 = slice * 16;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -683,6 +696,41 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(
   }
 }
 
+// ---- chain launches ----------------------------------------------------------
+template <int D, int C>
+__global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ cu, int N, int H,
+                                                       int seq_len, const float *__restrict__ s0,
+                                                       BwdLayout L, char *ws) {
+  extern __shared__ __align__(16) float sm[];
+  state_chain<D, C>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
+}
+
+template <typename T, int D, int C>
+__global__ __launch_bounds__(NT) void bwd_dstate_kernel(
+    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
+    const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
+  extern __shared__ __align__(16) float sm[];
+  dstate_chain<T, D, C>((int)blockIdx.x, d_o, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+}
+
+// The two chains are independent: the state-gradient recursion reads dO, P,
+// Ke, Qt and W but never the states.  When both grids fit the GPU at once,
+// one launch runs them side by side: workgroups below `split` walk the state
+// gradients backward, the others the states forward.  `split` is a multiple
+// of 8, so each part keeps a pair's slices on one XCD.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(NT) void bwd_chains_kernel(
+    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
+    const float *__restrict__ s0, const float *__restrict__ dsf, float *__restrict__ ds0,
+    BwdLayout L, char *ws, int split) {
+  extern __shared__ __align__(16) float sm[];
+  const int b = (int)blockIdx.x;
+  if (b < split)
+    dstate_chain<T, D, C>(b, d_o, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+  else
+    state_chain<D, C>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
+}
+
 // ---- 4. per-tile gradients -------------------------------------------------
 // The C x C intermediates (dP, dT / dA, T^T dT) live in LDS; the C x d ones
 // go through the tile's workspace scratch.  Paired products accumulate in
@@ -811,10 +859,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
 template <typename T, int D, int C>
 static hipError_t launch_bwd_dc(const BwdArgs &a) {
   const unsigned tiles = (unsigned)(a.grid_chunks * a.num_heads);
-  const unsigned slices = (unsigned)(a.num_seqs * a.num_heads * (D / 16));
+  const unsigned slices = chain_grid(a.num_seqs * a.num_heads, D / 16);
   const T *q = reinterpret_cast<const T *>(a.q), *k = reinterpret_cast<const T *>(a.k);
   const T *v = reinterpret_cast<const T *>(a.v), *d_o = reinterpret_cast<const T *>(a.d_o);
   constexpr size_t lds_state = state_lds_bytes<D, C>(), lds_dstate = dstate_lds_bytes<D, C>();
+  constexpr size_t lds_chains = lds_state > lds_dstate ? lds_state : lds_dstate;
   // the largest shapes (d = 128, C = 64): 80,384 and 135,936 bytes
   static const hipError_t a1 = hipFuncSetAttribute(
       (const void *)bwd_state_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -822,17 +871,28 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   static const hipError_t a2 = hipFuncSetAttribute(
       (const void *)bwd_dstate_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds_dstate);
+  static const hipError_t a3 = hipFuncSetAttribute(
+      (const void *)bwd_chains_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)lds_chains);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
+  if (a3 != hipSuccess) return a3;
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
                        a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.lay,
                        a.ws);
-  hipLaunchKernelGGL((bwd_state_kernel<D, C>), dim3(slices), dim3(NT), lds_state, a.stream,
-                     a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
-  hipLaunchKernelGGL((bwd_dstate_kernel<T, D, C>), dim3(slices), dim3(NT), lds_dstate,
-                     a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf,
-                     a.ds0, a.lay, a.ws);
+  const int cus = device_cus();
+  if (cus > 0 && 2 * slices <= (unsigned)cus) {
+    hipLaunchKernelGGL((bwd_chains_kernel<T, D, C>), dim3(2 * slices), dim3(NT), lds_chains,
+                       a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0,
+                       a.dsf, a.ds0, a.lay, a.ws, (int)slices);
+  } else {
+    hipLaunchKernelGGL((bwd_state_kernel<D, C>), dim3(slices), dim3(NT), lds_state, a.stream,
+                       a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
+    hipLaunchKernelGGL((bwd_dstate_kernel<T, D, C>), dim3(slices), dim3(NT), lds_dstate,
+                       a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf,
+                       a.ds0, a.lay, a.ws);
+  }
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k,
                        v, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,

@@ -64,6 +64,17 @@ def test_backward_ragged(dtype, d, chunk):
     _check(w, do, dsf, _run(w, do, dsf, chunk))
 
 
+def test_backward_many_pairs_two_launches():
+    """36 (sequence, head) pairs at d=64: each chain's grid is 160 workgroups,
+    so the two no longer fit a 256-CU GPU together and run as two launches
+    (the other cases run both chains in one launch)."""
+    print("[backward] 9 seqs x 4 heads d=64 C=32", flush=True)
+    w = kin.make_prefill(909, H=4, d=64, dtype=kin.BF16, chunk_size=32,
+                         lengths=[40, 0, 7, 65, 1, 33, 64, 16, 90], s0_std=0.05)
+    do, dsf = kin.backward_inputs(910, w.total_tokens, 4, 64, w.num_seqs, kin.BF16)
+    _check(w, do, dsf, _run(w, do, dsf, 32))
+
+
 def test_backward_equal_lengths_no_final_gradient():
     """B=2 sequences of 256 tokens, H=2, d=128, C=64, zero initial state and no
     final-state gradient (the default loss sum(o * d_o))."""
