@@ -24,13 +24,17 @@
 //   dG = dKt*Kt - dKh*Kh + dQt*Qt - dKe*Ke, dG_n = colsum(dKe*Ke) + dgam*gam,
 //   dg_s = sum_{r >= s} dG_r + dG_n.
 //
-// Four launches, all in fp32 over a per-tile fp32 workspace (BwdLayout),
-// each instantiated per (head dim d, chunk C) so that every loop bound and
-// register block is a compile-time constant:
-//   bwd_prep_kernel   per (chunk, head): G, Kt, Kh, Qt, Ke, gam, M, P, T, W, U
+// Three or four launches, all in fp32 over a per-tile fp32 workspace
+// (BwdLayout), each instantiated per (head dim d, chunk C) so that every loop
+// bound and register block is a compile-time constant:
+//   bwd_prep_kernel   per (chunk, head): G, Kt, Kh, Qt, Ke, gam, M, P, T, W, U,
+//                     and the chain-independent terms X = P^T dO, Y = Qt^T dO
 //   bwd_state_kernel  per (sequence, head, 16-column slice): chunk start states
 //   bwd_dstate_kernel per (sequence, head, 16-column slice), chunks in reverse:
+//                     dUnew = X + Ke dS_next, dS = Diag(gam) dS_next + Y - W^T dUnew;
 //                     dS_next per chunk, dUnew, and the initial-state gradient
+//                     (the two chains are independent; bwd_chains_kernel runs
+//                     both in one launch when they fit the GPU together)
 //   bwd_grad_kernel   per (chunk, head): dq, dk, dv, dg, dbeta
 // The state columns never mix (in the forward and in dS), which is what makes
 // the column slices of the two chains exact.  Rows past a chunk's end are
@@ -243,7 +247,7 @@ __device__ __forceinline__ void row_dots(float *out, const float *X, const float
 }
 
 struct TilePtr {
-  float *kt, *kh, *qt, *ke, *w, *u, *vr, *gc, *tm, *pm, *mm, *gam, *bt;
+  float *kt, *kh, *qt, *ke, *w, *u, *vr, *gc, *tm, *pm, *mm, *gam, *bt, *px, *qy;
 };
 
 __device__ TilePtr tile_ptrs(const BwdLayout &L, char *ws, int64_t tile, int C, int D) {
@@ -262,6 +266,8 @@ __device__ TilePtr tile_ptrs(const BwdLayout &L, char *ws, int64_t tile, int C, 
   p.mm = reinterpret_cast<float *>(ws + L.mm) + tile * cc;
   p.gam = reinterpret_cast<float *>(ws + L.gam) + tile * D;
   p.bt = reinterpret_cast<float *>(ws + L.bt) + tile * C;
+  p.px = reinterpret_cast<float *>(ws + L.px) + tile * cd;
+  p.qy = reinterpret_cast<float *>(ws + L.qy) + tile * (int64_t)D * D;
   return p;
 }
 
@@ -287,12 +293,15 @@ __device__ void seq_chunks(int seq, const int *cu, int seq_len, int C, const int
 template <typename T, int D, int C>
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, const int *__restrict__ cu,
-    int N, int H, int seq_len, BwdLayout L, char *ws) {
+    const T *__restrict__ d_o, const float *__restrict__ g, const float *__restrict__ beta,
+    const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
   constexpr int LA = C + 4;
+  constexpr int YM = D < 64 ? D : 64;  // row block of Qt^T dO
+  constexpr int MM = mm_lds<C, D, D>() > mm_lds<YM, D, C>() ? mm_lds<C, D, D>()
+                                                           : mm_lds<YM, D, C>();
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
-  __shared__ __align__(16) float s_mm[mm_lds<C, D, D>()];
+  __shared__ __align__(16) float s_mm[MM];
   __shared__ __align__(16) float s_a[C * LA];  // A = strict_lower(beta M), for the substitution
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-  float *bkt = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
-  float *bvv = bkt + C * D;  // Diag(beta) Kt and Diag(beta) V (scratch)
+  float *tb = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
+  float *dos = tb + C * C;  // T Diag(beta) [C][C]; dO, zero past the chunk's end (scratch)
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
   // cumulative log-decay per channel (rows past the end add nothing); every
@@ -328,6 +337,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const int64_t at = (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i;
     const f32x4 qv = load4_f32<T>(q + at) * live, kv = load4_f32<T>(k + at) * live;
     const f32x4 vv = load4_f32<T>(v + at) * live;
+    const f32x4 ov = load4_f32<T>(d_o + at) * live;
     const f32x4 G = *reinterpret_cast<const f32x4 *>(p.gc + r * D + i);
     const f32x4 Gn = *reinterpret_cast<const f32x4 *>(p.gc + (C - 1) * D + i);
     f32x4 eg, emg, egn;
@@ -337,15 +347,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
       emg[u] = __expf(-G[u]);
       egn[u] = __expf(Gn[u] - G[u]);
     }
-    const float b = p.bt[r];
     const int e = r * D + i;
     *reinterpret_cast<f32x4 *>(p.kt + e) = kv * eg;
     *reinterpret_cast<f32x4 *>(p.kh + e) = kv * emg;
     *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
     *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
     *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
-    *reinterpret_cast<f32x4 *>(bkt + e) = kv * eg * b;
-    *reinterpret_cast<f32x4 *>(bvv + e) = vv * b;
+    *reinterpret_cast<f32x4 *>(dos + e) = ov;
   }
   __syncthreads();
   block_mm<C, C, D, false, true>(p.mm, C, p.kt, D, p.kh, D, 1.f, false, s_mm);  // M = Kt Kh^T
@@ -361,6 +369,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   // computed are still zero, so the sums run over whole 4-vectors of a row.
   if (tid < C) {
     const int j = tid;
+    const float bj = p.bt[j];
     float t[C];
 #pragma unroll
     for (int r = 0; r < C; ++r) t[r] = 0.f;
@@ -375,11 +384,18 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
       }
       t[r] = r < j ? 0.f : (r == j ? 1.f : -s);
       p.tm[r * C + j] = t[r];
+      tb[r * C + j] = t[r] * bj;
     }
   }
   __syncthreads();
-  block_mm<C, D, C, false, false>(p.w, D, p.tm, C, bkt, D, 1.f, false, s_mm);  // W = T (beta Kt)
-  block_mm<C, D, C, false, false>(p.u, D, p.tm, C, bvv, D, 1.f, false, s_mm);  // U = T (beta V)
+  block_mm<C, D, C, false, false>(p.w, D, tb, C, p.kt, D, 1.f, false, s_mm);  // W = (T Diag(beta)) Kt
+  block_mm<C, D, C, false, false>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
+  // the two terms of the state-gradient recursion that do not depend on it:
+  // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke
+  block_mm<C, D, C, true, false>(p.px, D, p.pm, C, dos, D, 1.f, false, s_mm);
+#pragma unroll
+  for (int m0 = 0; m0 < D; m0 += YM)
+    block_mm<YM, D, C, true, false>(p.qy + m0 * D, D, p.qt + m0, D, dos, D, 1.f, false, s_mm);
 }
 
 // ---- chain helpers ----------------------------------------------------------
@@ -416,7 +432,7 @@ struct Stage {
 // the instructions that produce them.
 template <int D, int C>
 struct ChainShape {
-  static constexpr int NS = D / 16, LD = D + 4, LU = C + 4, LP = C + 4;
+  static constexpr int NS = D / 16, LD = D + 4, LU = C + 4;
   static constexpr int NRB = C / 16, NCB = D / 16, CBW = (NCB + 3) / 4;
 };
 
@@ -440,8 +456,7 @@ constexpr size_t state_lds_bytes() {
 }
 template <int D, int C>
 constexpr size_t dstate_lds_bytes() {
-  using Sh = ChainShape<D, C>;
-  return sizeof(float) * (3 * C * Sh::LD + C * Sh::LP + 16 * Sh::LD + 2 * 16 * Sh::LU);
+  return state_lds_bytes<D, C>();  // W, Ke, the transposed dS_next and dUnew
 }
 
 // ---- 2. chunk start states ------------------------------------------------
@@ -552,17 +567,16 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
 }
 
 // ---- 3. state gradients, chunks in reverse ---------------------------------
-template <typename T, int D, int C>
-__device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
-                                             const int *__restrict__ cu, int N, int H,
+template <int D, int C>
+__device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, int N, int H,
                                              int seq_len, const float *__restrict__ dsf,
                                              float *__restrict__ ds0, BwdLayout L, char *ws,
                                              float *sm) {
   using Sh = ChainShape<D, C>;
-  constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, LP = Sh::LP, NRB = Sh::NRB;
+  constexpr int NS = Sh::NS, LD = Sh::LD, LU = Sh::LU, NRB = Sh::NRB;
   constexpr int NCB = Sh::NCB, CBW = Sh::CBW;
-  float *sW = sm, *sK = sW + C * LD, *sQ = sK + C * LD, *sP = sQ + C * LD;  // row-major
-  float *sDt = sP + C * LP, *sOt = sDt + 16 * LD, *sUt = sOt + 16 * LU;     // transposed
+  float *sW = sm, *sK = sW + C * LD;               // [C][LD] row-major
+  float *sDt = sK + C * LD, *sUt = sDt + 16 * LD;  // dS_next^T [16][LD], dUnew^T [16][LU]
   int slice, pair;
   if (!chain_block<NS>(b, N * H, &slice, &pair)) return;
   const int seq = pair / H, h = pair % H;
@@ -570,11 +584,9 @@ __device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool has_rb = wv < NRB;
-  const int64_t rs = (int64_t)H * D;
   int first, nch, len;
   seq_chunks(seq, cu, seq_len, C, reinterpret_cast<const int *>(ws + L.seq_first), &first,
              &nch, &len);
-  const int t_seq = cu ? cu[seq] : seq * seq_len;
   // dS[j][i] = dS_next[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
   f32x4 dS[CBW];
 #pragma unroll
@@ -587,29 +599,24 @@ __device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
         dS[j][i] = dsf[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
     }
   }
-  Stage<C, D> rw, rk, rq;
-  Stage<C, C> rp;
-  f32x4 on = zero4(), gn[CBW];
+  Stage<C, D> rw, rk;
+  // next chunk's X = P^T dO (the wave's token block) and Y = Qt^T dO (its
+  // channel blocks), columns col0 .. col0 + 15
+  f32x4 xn = zero4(), yn[CBW], gn[CBW];
   auto fetch = [&](int ci) {
     const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + ci) * H + h, C, D);
     rw.load(p.w);
     rk.load(p.ke);
-    rq.load(p.qt);
-    rp.load(p.pm);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = min(wv * CBW + j, NCB - 1);
       gn[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
-    }
-    if (has_rb) {  // dO[16 wv + 4 lg + i][col0 + lr], zero past the chunk's end
-      const int n = min(C, len - ci * C);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wv + 4 * lg + i;
-        const float x =
-            to_f32(d_o[(int64_t)(t_seq + ci * C + min(r, n - 1)) * rs + (int64_t)h * D + col0 + lr]);
-        on[i] = r < n ? x : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) yn[j][i] = p.qy[(16 * cb + 4 * lg + i) * D + col0 + lr];
+    }
+    if (has_rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xn[i] = p.px[(16 * wv + 4 * lg + i) * D + col0 + lr];
     }
   };
   if (nch > 0) fetch(nch - 1);
@@ -620,9 +627,6 @@ __device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
     __syncthreads();  // the previous chunk is done with the LDS operands
     rw.store(sW);
     rk.store(sK);
-    rq.store(sQ);
-    rp.store(sP);
-    if (has_rb) *reinterpret_cast<f32x4 *>(sOt + lr * LU + 16 * wv + 4 * lg) = on;
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
@@ -632,29 +636,26 @@ __device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
         for (int i = 0; i < 4; ++i) dse[(16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
       }
     }
-    f32x4 gam[CBW];
+    const f32x4 x0 = xn;
+    f32x4 gam[CBW], y0[CBW];
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) gam[j] = gn[j];
+    for (int j = 0; j < CBW; ++j) {
+      gam[j] = gn[j];
+      y0[j] = yn[j];
+    }
     __syncthreads();
     if (ci > 0) fetch(ci - 1);
     // dUnew = P^T dO + Ke dS_next for the wave's token block
     if (has_rb) {
       f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 16) {
-        f32x4 a;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) a[u] = sP[(k0 + 4 * lg + u) * LP + 16 * wv + lr];
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(sOt + lr * LU + k0 + 4 * lg);
-        a0 = mma_f32_k16(a, b, a0);
-      }
-#pragma unroll
       for (int k0 = 0; k0 < D; k0 += 16) {
         const f32x4 a = *reinterpret_cast<const f32x4 *>(sK + (16 * wv + lr) * LD + k0 + 4 * lg);
         const f32x4 b = *reinterpret_cast<const f32x4 *>(sDt + lr * LD + k0 + 4 * lg);
-        a1 = mma_f32_k16(a, b, a1);
+        if ((k0 / 16) & 1) a1 = mma_f32_k16(a, b, a1);
+        else a0 = mma_f32_k16(a, b, a0);
       }
-      const f32x4 du = a0 + a1;
+      const f32x4 du = x0 + (a0 + a1);
       *reinterpret_cast<f32x4 *>(sUt + lr * LU + 16 * wv + 4 * lg) = du;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dun[(16 * wv + 4 * lg + i) * D + col0 + lr] = du[i];
@@ -665,21 +666,16 @@ __device__ __forceinline__ void dstate_chain(int b, const T *__restrict__ d_o,
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
       if (NCB % 4 == 0 || cb < NCB) {
-        f32x4 aq = zero4(), aw = zero4();
+        f32x4 aw = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 16) {
-          f32x4 qa, wa;
+          f32x4 wa;
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            qa[u] = sQ[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
-            wa[u] = sW[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
-          }
-          const f32x4 ob = *reinterpret_cast<const f32x4 *>(sOt + lr * LU + k0 + 4 * lg);
+          for (int u = 0; u < 4; ++u) wa[u] = sW[(k0 + 4 * lg + u) * LD + 16 * cb + lr];
           const f32x4 ub = *reinterpret_cast<const f32x4 *>(sUt + lr * LU + k0 + 4 * lg);
-          aq = mma_f32_k16(qa, ob, aq);
           aw = mma_f32_k16(wa, ub, aw);
         }
-        dS[j] = dS[j] * gam[j] + (aq - aw);
+        dS[j] = dS[j] * gam[j] + (y0[j] - aw);
       }
     }
   }
@@ -705,28 +701,28 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ c
   state_chain<D, C>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
 }
 
-template <typename T, int D, int C>
-__global__ __launch_bounds__(NT) void bwd_dstate_kernel(
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
-    const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws) {
+template <int D, int C>
+__global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ cu, int N, int H,
+                                                        int seq_len, const float *__restrict__ dsf,
+                                                        float *__restrict__ ds0, BwdLayout L,
+                                                        char *ws) {
   extern __shared__ __align__(16) float sm[];
-  dstate_chain<T, D, C>((int)blockIdx.x, d_o, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+  dstate_chain<D, C>((int)blockIdx.x, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
 }
 
-// The two chains are independent: the state-gradient recursion reads dO, P,
-// Ke, Qt and W but never the states.  When both grids fit the GPU at once,
+// The two chains are independent: the state-gradient recursion reads W, Ke
+// and the products X, Y of the per-tile pass, but never the states.  When both grids fit the GPU at once,
 // one launch runs them side by side: workgroups below `split` walk the state
 // gradients backward, the others the states forward.  `split` is a multiple
 // of 8, so each part keeps a pair's slices on one XCD.
-template <typename T, int D, int C>
+template <int D, int C>
 __global__ __launch_bounds__(NT) void bwd_chains_kernel(
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
-    const float *__restrict__ s0, const float *__restrict__ dsf, float *__restrict__ ds0,
-    BwdLayout L, char *ws, int split) {
+    const int *__restrict__ cu, int N, int H, int seq_len, const float *__restrict__ s0,
+    const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws, int split) {
   extern __shared__ __align__(16) float sm[];
   const int b = (int)blockIdx.x;
   if (b < split)
-    dstate_chain<T, D, C>(b, d_o, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+    dstate_chain<D, C>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
   else
     state_chain<D, C>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
 }
@@ -864,34 +860,34 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   const T *v = reinterpret_cast<const T *>(a.v), *d_o = reinterpret_cast<const T *>(a.d_o);
   constexpr size_t lds_state = state_lds_bytes<D, C>(), lds_dstate = dstate_lds_bytes<D, C>();
   constexpr size_t lds_chains = lds_state > lds_dstate ? lds_state : lds_dstate;
-  // the largest shapes (d = 128, C = 64): 80,384 and 135,936 bytes
+  // 80,384 bytes at the largest shape (d = 128, C = 64)
   static const hipError_t a1 = hipFuncSetAttribute(
       (const void *)bwd_state_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds_state);
   static const hipError_t a2 = hipFuncSetAttribute(
-      (const void *)bwd_dstate_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (const void *)bwd_dstate_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds_dstate);
   static const hipError_t a3 = hipFuncSetAttribute(
-      (const void *)bwd_chains_kernel<T, D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (const void *)bwd_chains_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)lds_chains);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   if (a3 != hipSuccess) return a3;
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
-                       a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.lay,
-                       a.ws);
+                       d_o, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
+                       a.lay, a.ws);
   const int cus = device_cus();
   if (cus > 0 && 2 * slices <= (unsigned)cus) {
-    hipLaunchKernelGGL((bwd_chains_kernel<T, D, C>), dim3(2 * slices), dim3(NT), lds_chains,
-                       a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0,
-                       a.dsf, a.ds0, a.lay, a.ws, (int)slices);
+    hipLaunchKernelGGL((bwd_chains_kernel<D, C>), dim3(2 * slices), dim3(NT), lds_chains,
+                       a.stream, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.dsf,
+                       a.ds0, a.lay, a.ws, (int)slices);
   } else {
     hipLaunchKernelGGL((bwd_state_kernel<D, C>), dim3(slices), dim3(NT), lds_state, a.stream,
                        a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
-    hipLaunchKernelGGL((bwd_dstate_kernel<T, D, C>), dim3(slices), dim3(NT), lds_dstate,
-                       a.stream, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf,
-                       a.ds0, a.lay, a.ws);
+    hipLaunchKernelGGL((bwd_dstate_kernel<D, C>), dim3(slices), dim3(NT), lds_dstate, a.stream,
+                       a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf, a.ds0, a.lay,
+                       a.ws);
   }
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k,

@@ -114,8 +114,8 @@ struct BwdLayout {
   int64_t tiles = 0;
   int64_t scratch_per_tile = 0;  // floats
   size_t seq_first = 0, kt = 0, kh = 0, qt = 0, ke = 0, w = 0, u = 0, vr = 0, gc = 0,
-         tm = 0, pm = 0, mm = 0, gam = 0, bt = 0, sc = 0, dse = 0, dun = 0, scratch = 0,
-         total = 0;
+         tm = 0, pm = 0, mm = 0, gam = 0, bt = 0, px = 0, qy = 0, sc = 0, dse = 0, dun = 0,
+         scratch = 0, total = 0;
 };
 
 inline BwdLayout bwd_layout(int64_t T, int64_t N, int64_t H, int64_t D, int64_t C) {
@@ -143,6 +143,8 @@ inline BwdLayout bwd_layout(int64_t T, int64_t N, int64_t H, int64_t D, int64_t 
   L.mm = take(f * t * C * C);
   L.gam = take(f * t * D);
   L.bt = take(f * t * C);
+  L.px = take(f * t * C * D);  // P^T dO
+  L.qy = take(f * t * D * D);  // Qt^T dO
   L.sc = take(f * t * D * D);
   L.dse = take(f * t * D * D);
   L.dun = take(f * t * C * D);

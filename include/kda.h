@@ -314,7 +314,7 @@ kda_status kda_decode_step_ex(const kda_options *options, const void *q, const v
  *   dbeta         [total_tokens, H] fp32 (output).
  *   d_initial_state [num_seqs, H, d_k, d_v] fp32 (output), or NULL to skip.
  *   workspace     at least kda_bwd_chunked_workspace_size() bytes, 256-byte
- *                 aligned, clobbered (about 0.7 MiB per (chunk, head) tile
+ *                 aligned, clobbered (about 0.9 MiB per (chunk, head) tile
  *                 for d = 128, C = 64).
  * Alignment rules are those of kda_fwd_chunked (d_o, dq, dk, dv 16-byte;
  * dlog_alpha 16-byte; dbeta 4-byte).  The decay precondition is the
