@@ -70,23 +70,35 @@ struct MmTiles {
   static constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + 3) / 4;
 };
 
-// LDS floats that a product with contraction K stages (6,912 at most)
+// LDS floats that a product with contraction K stages, for either layout
+// of each operand (7,200 at most)
 template <int M, int N, int K>
 constexpr int mm_lds() {
-  return (M + N) * ((K < 32 ? K : 32) + 4);
+  return (M + N + 8) * ((K < 32 ? K : 32) + 4);
 }
 
 // c[q] (MmTiles<M, N>::TPW accumulators) += the wave's tiles of A B
-// (contraction K).  Ends with a barrier.
+// (contraction K).  Each K slice is staged in LDS in the order its global
+// rows come in, so every staging store is one 16-byte write:
+//   A: sa[i][kk] = A(i, k0 + kk), row stride KS + 4, when A is read by rows
+//      (TA false); sa[kk][i], row stride M + 4, when it is read transposed;
+//   B: sb[j][kk] = B(k0 + kk, j), row stride KS + 4, when TB; sb[kk][j], row
+//      stride N + 4, otherwise.
+// A matrix-core step reads a lane's four contraction values as one 16-byte
+// read in the first layouts and as four 4-byte reads in the others; the
+// padding of 4 keeps both free of bank conflicts.  Ends with a barrier.
 template <int M, int N, int K, bool TA, bool TB>
 __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
                                               int ldb, float *lds) {
   static_assert(K % 16 == 0, "contraction");
-  constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, LDS row stride
+  constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
+  constexpr int LMA = M + 4, LNB = N + 4;           // row strides of the transposed layouts
   constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
   constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
-  float *sa = lds, *sb = lds + M * LK;  // sa[i][kk] = A(i, k0 + kk), sb[j][kk] = B(k0 + kk, j)
+  constexpr int SA = TA ? KS * LMA : M * LK, SB = TB ? N * LK : KS * LNB;
+  static_assert(SA + SB <= mm_lds<M, N, K>(), "staging space");
+  float *sa = lds, *sb = lds + SA;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   f32x4 ra[PA], rb[PB];
@@ -125,8 +137,7 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
       if (FA % NT == 0 || f < FA) {
         if (TA) {
           const int kk = f / (M / 4), i4 = f % (M / 4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) sa[(4 * i4 + u) * LK + kk] = ra[p][u];
+          *reinterpret_cast<f32x4 *>(sa + kk * LMA + 4 * i4) = ra[p];
         } else {
           const int i = f / (KS / 4), k4 = f % (KS / 4);
           *reinterpret_cast<f32x4 *>(sa + i * LK + 4 * k4) = ra[p];
@@ -142,10 +153,31 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
           *reinterpret_cast<f32x4 *>(sb + j * LK + 4 * k4) = rb[p];
         } else {
           const int kk = f / (N / 4), j4 = f % (N / 4);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) sb[(4 * j4 + u) * LK + kk] = rb[p][u];
+          *reinterpret_cast<f32x4 *>(sb + kk * LNB + 4 * j4) = rb[p];
         }
       }
+    }
+  };
+  // a lane's operands of a 16-deep step: A(16 rt + lr, ks + 4 lg + u) and
+  // B(ks + 4 lg + u, 16 ct + lr), u = 0 .. 3
+  auto frag_a = [&](int rt, int ks) -> f32x4 {
+    if constexpr (TA) {
+      f32x4 a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = sa[(ks + 4 * lg + u) * LMA + 16 * rt + lr];
+      return a;
+    } else {
+      return *reinterpret_cast<const f32x4 *>(sa + (16 * rt + lr) * LK + ks + 4 * lg);
+    }
+  };
+  auto frag_b = [&](int ct, int ks) -> f32x4 {
+    if constexpr (TB) {
+      return *reinterpret_cast<const f32x4 *>(sb + (16 * ct + lr) * LK + ks + 4 * lg);
+    } else {
+      f32x4 b;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[u] = sb[(ks + 4 * lg + u) * LNB + 16 * ct + lr];
+      return b;
     }
   };
   load(0);
@@ -156,12 +188,27 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
     if (k0 + KS < K) load(k0 + KS);  // next slice in flight during this one
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 16) {
+      if constexpr (TN % 4 == 0) {
+        // wave wv owns tile columns wv + 4 cc of every tile row (q = row * CW
+        // + cc, the same tiles as t = wv + 4 q): each A and B fragment is read
+        // from LDS once per step and used for a whole row or column of tiles
+        constexpr int TM = M / 16, CW = TN / 4;
+        f32x4 af[TM], bf[CW];
 #pragma unroll
-      for (int q = 0; q < TPW; ++q) {
-        const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(sa + (16 * (t / TN) + lr) * LK + ks + 4 * lg);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(sb + (16 * (t % TN) + lr) * LK + ks + 4 * lg);
-        c[q] = mma_f32_k16(a, b, c[q]);
+        for (int rr = 0; rr < TM; ++rr) af[rr] = frag_a(rr, ks);
+#pragma unroll
+        for (int cc = 0; cc < CW; ++cc) bf[cc] = frag_b(wv + 4 * cc, ks);
+#pragma unroll
+        for (int rr = 0; rr < TM; ++rr)
+#pragma unroll
+          for (int cc = 0; cc < CW; ++cc)
+            c[rr * CW + cc] = mma_f32_k16(af[rr], bf[cc], c[rr * CW + cc]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) {
+          const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
+          c[q] = mma_f32_k16(frag_a(t / TN, ks), frag_b(t % TN, ks), c[q]);
+        }
       }
     }
     __syncthreads();
@@ -231,17 +278,36 @@ __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, 
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
-// length L (leading dimension ld), one wavefront per row.
+// length L (leading dimension ld, a multiple of 4; 16-byte aligned rows).
+// TPR consecutive threads share a row, each reading float4s part, part +
+// TPR, ...; a thread's rows are r0, r0 + NT / TPR, ..., all loaded before
+// any of the sums is reduced.  Ends with a barrier.
 template <int R, int L>
 __device__ __forceinline__ void row_dots(float *out, const float *X, const float *Y, int ld,
                                          bool acc) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int r = wv; r < R; r += NT / 64) {
-    float s = 0.f;
+  constexpr int TPR = L / 4 < 16 ? L / 4 : 16;  // threads per row
+  constexpr int V = L / (4 * TPR);              // float4 per thread and row
+  constexpr int RPP = NT / TPR;                 // rows per pass of the block
+  constexpr int NP = (R + RPP - 1) / RPP;       // passes
+  static_assert(TPR >= 4 && L % (4 * TPR) == 0, "row_dots shape");
+  const int part = threadIdx.x % TPR, r0 = threadIdx.x / TPR;
+  float s[NP];
 #pragma unroll
-    for (int j = lane; j < L; j += 64) s += X[r * ld + j] * Y[r * ld + j];
-    s = group_sum<64>(s);
-    if (lane == 0) out[r] = s + (acc ? out[r] : 0.f);
+  for (int pp = 0; pp < NP; ++pp) {
+    const int r = min(r0 + RPP * pp, R - 1);
+    s[pp] = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(X + r * ld + 4 * (part + TPR * v));
+      const f32x4 y = *reinterpret_cast<const f32x4 *>(Y + r * ld + 4 * (part + TPR * v));
+      s[pp] += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp) {
+    const float t = group_sum<TPR>(s[pp]);
+    const int r = r0 + RPP * pp;
+    if (part == 0 && r < R) out[r] = t + (acc ? out[r] : 0.f);
   }
   __syncthreads();
 }
