@@ -493,9 +493,10 @@ struct Stage {
 // and B[4g + i][c] and holds D[4g + i][c]).  Wave w owns token block w of the
 // chunk (rows 16 w ..) and channel blocks w*CBW .. of the state slice.  The
 // right-hand operands sit transposed in LDS (column c of the slice is a row),
-// so that both operands of every step are one 16-byte read per lane.  Matrix
-// results are read (stored or combined) in straight-line code right after
-// the instructions that produce them.
+// so that they are one 16-byte read per lane; a left-hand operand used
+// transposed (Ke^T, W^T) is four 4-byte reads, free of bank conflicts with
+// the row padding of 4.  Matrix results are read (stored or combined) in
+// straight-line code right after the instructions that produce them.
 template <int D, int C>
 struct ChainShape {
   static constexpr int NS = D / 16, LD = D + 4, LU = C + 4;
