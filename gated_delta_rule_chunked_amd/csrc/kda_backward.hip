@@ -71,7 +71,11 @@ struct MmTiles {
 };
 
 // LDS floats that a product with contraction K stages, for either layout
-// of each operand (7,200 at most)
+// of each operand (7,200 at most).  The products take their staging buffer
+// as an array reference, so its size is checked against every product at
+// compile time.
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <int M, int N, int K>
 constexpr int mm_lds() {
   return (M + N + 8) * ((K < 32 ? K : 32) + 4);
@@ -87,9 +91,9 @@ constexpr int mm_lds() {
 // A matrix-core step reads a lane's four contraction values as one 16-byte
 // read in the first layouts and as four 4-byte reads in the others; the
 // padding of 4 keeps both free of bank conflicts.  Ends with a barrier.
-template <int M, int N, int K, bool TA, bool TB>
+template <int M, int N, int K, bool TA, bool TB, int CAP>
 __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
-                                              int ldb, float *lds) {
+                                              int ldb, float (&lds)[CAP]) {
   static_assert(K % 16 == 0, "contraction");
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
   constexpr int LMA = M + 4, LNB = N + 4;           // row strides of the transposed layouts
@@ -97,7 +101,8 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
   constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
   constexpr int SA = TA ? KS * LMA : M * LK, SB = TB ? N * LK : KS * LNB;
-  static_assert(SA + SB <= mm_lds<M, N, K>(), "staging space");
+  static_assert(SA + SB <= mm_lds<M, N, K>() && mm_lds<M, N, K>() <= CAP,
+                "the caller's LDS buffer holds this product's staging");
   float *sa = lds, *sb = lds + SA;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,11 +245,12 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
   __syncthreads();
 }
 
-// out = alpha A B (+ out when acc).  `lds` holds mm_lds<M, N, K>() floats.
-template <int M, int N, int K, bool TA, bool TB>
+// out = alpha A B (+ out when acc).  `lds` holds at least mm_lds<M, N, K>()
+// floats.
+template <int M, int N, int K, bool TA, bool TB, int CAP>
 __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
                                          const float *B, int ldb, float alpha, bool acc,
-                                         float *lds) {
+                                         float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
@@ -253,10 +259,10 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
 }
 
 // out = init + alpha A B (init has leading dimension ldo).
-template <int M, int N, int K, bool TA, bool TB>
+template <int M, int N, int K, bool TA, bool TB, int CAP>
 __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
                                               const float *A, int lda, const float *B, int ldb,
-                                              float *lds) {
+                                              float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
@@ -265,10 +271,10 @@ __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *
 }
 
 // out = A1 B1 + A2 B2, both products accumulated in registers.
-template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2>
+template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2, int CAP>
 __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, int lda1,
                                           const float *B1, int ldb1, const float *A2, int lda2,
-                                          const float *B2, int ldb2, float *lds) {
+                                          const float *B2, int ldb2, float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
@@ -363,8 +369,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
   constexpr int LA = C + 4;
   constexpr int YM = D < 64 ? D : 64;  // row block of Qt^T dO
-  constexpr int MM = mm_lds<C, D, D>() > mm_lds<YM, D, C>() ? mm_lds<C, D, D>()
-                                                           : mm_lds<YM, D, C>();
+  constexpr int MM = cmax(cmax(mm_lds<C, C, D>(), mm_lds<C, D, C>()), mm_lds<YM, D, C>());
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_mm[MM];
@@ -807,7 +812,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
     const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
     T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
-  constexpr int MM = mm_lds<C, D, D>(), CC = C * C, CD = C * D;
+  constexpr int MM = cmax(cmax(mm_lds<C, D, D>(), mm_lds<C, C, D>()),
+                          cmax(mm_lds<C, D, C>(), mm_lds<C, C, C>()));
+  constexpr int CC = C * C, CD = C * D;
   // dG [C][D] and colsum(dKe Ke) [D] reuse the staging and dP / dM space
   // once the last product is done; T^T dT's space then holds rowsum(dA M)
   static_assert(CD + D <= MM + 2 * CC, "LDS reuse at the end");
@@ -815,7 +822,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_big[MM + 3 * CC];
   __shared__ float s_dgam[D];
-  float *s_mm = s_big, *s_dp = s_big + MM, *s_dt = s_dp + CC, *s_xm = s_dt + CC;
+  float(&s_mm)[MM] = *reinterpret_cast<float(*)[MM]>(s_big);  // product staging
+  float *s_dp = s_big + MM, *s_dt = s_dp + CC, *s_xm = s_dt + CC;
   float *s_dG = s_big, *s_cs = s_big + CD, *s_dbr = s_xm;
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);

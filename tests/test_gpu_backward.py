@@ -64,6 +64,23 @@ def test_backward_ragged(dtype, d, chunk):
     _check(w, do, dsf, _run(w, do, dsf, chunk))
 
 
+_EVERY_SHAPE = [(dt, d, c) for dt in (kin.BF16, kin.F32) for d in (32, 64, 128)
+                for c in (16, 32, 64) if not (dt == kin.F32 and d == 128)]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", _EVERY_SHAPE)
+def test_backward_every_shape(dtype, d, chunk):
+    """Every supported (dtype, head size, chunk size): one full chunk plus a
+    tail, a one-token sequence and two chunks plus a tail, one head, with
+    initial states and a final-state gradient.  Each shape instantiates its
+    own product tilings (whole tile columns per wave or not, 16-row tiles)."""
+    print(f"[backward] every shape dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill(700 + d + chunk, H=1, d=d, dtype=dtype, chunk_size=chunk,
+                         lengths=[chunk + 5, 1, 2 * chunk + 3], s0_std=0.05)
+    do, dsf = kin.backward_inputs(701 + d + chunk, w.total_tokens, 1, d, w.num_seqs, dtype)
+    _check(w, do, dsf, _run(w, do, dsf, chunk))
+
+
 def test_backward_many_pairs_two_launches():
     """36 (sequence, head) pairs at d=64: each chain's grid is 160 workgroups,
     so the two no longer fit a 256-CU GPU together and run as two launches
