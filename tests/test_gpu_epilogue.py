@@ -56,7 +56,8 @@ def _check_epilogue(y, y_ref, o_ref, wn, tol):
 
 @pytest.mark.parametrize("with_gate", [True, False])
 @pytest.mark.parametrize("dtype,d,chunk", [(kin.BF16, 128, 64), (kin.BF16, 64, 16),
-                                           (kin.BF16, 32, 32), (kin.F32, 32, 16)])
+                                           (kin.BF16, 32, 32), (kin.F32, 32, 16),
+                                           (kin.F32, 64, 32)])
 def test_prefill_epilogue(dtype, d, chunk, with_gate):
     print(f"[epilogue] prefill dtype={dtype} d={d} C={chunk} gate={with_gate}", flush=True)
     kda = _kda()
@@ -81,7 +82,8 @@ def test_prefill_epilogue(dtype, d, chunk, with_gate):
     _check_epilogue(from_device(o), y_ref, o_ref, wn, TOL[dtype])
 
 
-@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 32), (kin.F32, 64)])
+@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
+                                     (kin.F32, 128), (kin.F32, 64), (kin.F32, 32)])
 def test_decode_epilogue_fused(dtype, d):
     """The decode kernel applies the epilogue to its fp32 output row."""
     print(f"[epilogue] decode dtype={dtype} d={d}", flush=True)

@@ -94,6 +94,22 @@ def test_fused_prefill_ragged(gate, dtype, d, chunk):
     _check(w, o, s)
 
 
+_EVERY_SHAPE = [(dt, d, c) for dt in (kin.BF16, kin.F32) for d in (32, 64, 128)
+                for c in (16, 32, 64) if not (dt == kin.F32 and d == 128)]
+
+
+@pytest.mark.parametrize("dtype,d,chunk", _EVERY_SHAPE)
+def test_fused_prefill_every_shape(dtype, d, chunk):
+    """Every supported (dtype, head size, chunk size) with the softplus gate:
+    a full chunk plus a tail, a one-token sequence, two chunks plus a tail."""
+    print(f"[fused] prefill every shape dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill_raw(400 + d + chunk, H=2, d=d, dtype=dtype, chunk_size=chunk,
+                             gate="softplus", lengths=[chunk + 5, 1, 2 * chunk + 3],
+                             s0_std=0.05)
+    o, s = _run_raw(w)
+    _check(w, o, s)
+
+
 def test_fused_headline_raw_workload():
     """The B=2, H=8, T=2048 prefill in raw form (softplus gate), every output
     and final state, run stage by stage through kda_fwd_chunked_ex."""
@@ -125,7 +141,8 @@ def test_ex_entry_without_options_is_the_plain_call():
 
 
 @pytest.mark.parametrize("gate", ["softplus", "sigmoid"])
-@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 32), (kin.F32, 64)])
+@pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
+                                     (kin.F32, 128), (kin.F32, 64), (kin.F32, 32)])
 def test_fused_decode_steps(gate, dtype, d):
     """Dependent decode steps with raw inputs against oracle.decode on the
     transformed inputs."""
