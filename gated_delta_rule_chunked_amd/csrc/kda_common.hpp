@@ -89,13 +89,6 @@ __device__ __forceinline__ void store8<float>(float *p, const float (&x)[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-template <typename T>
-__device__ __forceinline__ void load8_f32(const T *p, float (&x)[8]) {
-  const typename Frag<T>::type v = load8<T>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = to_f32(v[i]);
-}
-
 // 8 fp32 values converted to a fragment of T.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::type frag_from_f32(const float *p) {
@@ -164,6 +157,13 @@ __host__ __device__ constexpr int kperm_idx(int pos) {  // position -> index
   return (pos & ~31) + (((pos & 7) < 4) ? 4 * ((pos & 31) >> 3) + (pos & 3)
                                         : 16 + 4 * ((pos & 31) >> 3) + (pos & 3));
 }
+// the two maps are inverse permutations of every group of 32
+constexpr bool kperm_is_permutation() {
+  for (int i = 0; i < 64; ++i)
+    if (kperm_idx(kperm_pos(i)) != i || kperm_pos(kperm_idx(i)) != i) return false;
+  return true;
+}
+static_assert(kperm_is_permutation(), "kperm order");
 
 // Two output-tile row quads (rows 4g..4g+3 of tiles 2s and 2s+1) packed as
 // one K-step operand fragment in the order above.
