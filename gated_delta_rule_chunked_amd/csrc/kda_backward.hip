@@ -567,29 +567,34 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
         S[j][i] = s0[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
     }
   }
-  Stage<C, D> rw, rk;
-  f32x4 un = zero4(), gn[CBW];
-  auto fetch = [&](int64_t tile) {
-    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-    rw.load(p.w);
-    rk.load(p.ke);
+  // one chunk's operands: W and Ke whole, the wave's U tile, e^{G_n}
+  struct Buf {
+    Stage<C, D> w, k;
+    f32x4 u, g[CBW];
+  };
+  auto fetch = [&](Buf &B, int ci) {  // chunk min(ci, nch - 1): always in range
+    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + min(ci, nch - 1)) * H + h, C, D);
+    B.w.load(p.w);
+    B.k.load(p.ke);
+    B.u = zero4();
     if (has_rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) un[i] = p.u[(16 * wv + 4 * lg + i) * D + col0 + lr];
+      for (int i = 0; i < 4; ++i) B.u[i] = p.u[(16 * wv + 4 * lg + i) * D + col0 + lr];
     }
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = min(wv * CBW + j, NCB - 1);
-      gn[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+      B.g[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
     }
   };
-  fetch((int64_t)first * H + h);
-  for (int ci = 0; ci < nch; ++ci) {
+  // Two buffers in turn: a chunk's operands are requested two steps before
+  // their use, so their loads overlap two steps of products.
+  auto step = [&](Buf &B, int ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
     float *sc = reinterpret_cast<float *>(ws + L.sc) + tile * D * D;
     __syncthreads();  // the previous chunk is done with the LDS operands
-    rw.store(sW);
-    rk.store(sK);
+    B.w.store(sW);
+    B.k.store(sK);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
@@ -599,12 +604,12 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
         for (int i = 0; i < 4; ++i) sc[(16 * cb + 4 * lg + i) * D + col0 + lr] = S[j][i];
       }
     }
-    const f32x4 u0 = un;
+    const f32x4 u0 = B.u;
     f32x4 gam[CBW];
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) gam[j] = gn[j];
+    for (int j = 0; j < CBW; ++j) gam[j] = B.g[j];
     __syncthreads();
-    if (ci + 1 < nch) fetch(tile + H);
+    fetch(B, ci + 2);
     // Unew = U - W S for the wave's token block
     if (has_rb) {
       f32x4 a0 = zero4(), a1 = zero4();
@@ -635,6 +640,13 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
         S[j] = acc + 0.f;  // a real VALU read of the result, before any branch
       }
     }
+  };
+  Buf b0, b1;
+  fetch(b0, 0);
+  fetch(b1, 1);
+  for (int ci = 0; ci < nch; ci += 2) {
+    step(b0, ci);
+    if (ci + 1 < nch) step(b1, ci + 1);
   }
 }
 
@@ -671,34 +683,37 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
         dS[j][i] = dsf[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
     }
   }
-  Stage<C, D> rw, rk;
-  // next chunk's X = P^T dO (the wave's token block) and Y = Qt^T dO (its
-  // channel blocks), columns col0 .. col0 + 15
-  f32x4 xn = zero4(), yn[CBW], gn[CBW];
-  auto fetch = [&](int ci) {
-    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + ci) * H + h, C, D);
-    rw.load(p.w);
-    rk.load(p.ke);
+  // one chunk's operands: W and Ke whole, the wave's tiles of X = P^T dO
+  // (its token block) and of Y = Qt^T dO (its channel blocks), e^{G_n}
+  struct Buf {
+    Stage<C, D> w, k;
+    f32x4 x, y[CBW], g[CBW];
+  };
+  auto fetch = [&](Buf &B, int ci) {  // chunk max(ci, 0): always in range
+    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + max(ci, 0)) * H + h, C, D);
+    B.w.load(p.w);
+    B.k.load(p.ke);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = min(wv * CBW + j, NCB - 1);
-      gn[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+      B.g[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yn[j][i] = p.qy[(16 * cb + 4 * lg + i) * D + col0 + lr];
+      for (int i = 0; i < 4; ++i) B.y[j][i] = p.qy[(16 * cb + 4 * lg + i) * D + col0 + lr];
     }
+    B.x = zero4();
     if (has_rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xn[i] = p.px[(16 * wv + 4 * lg + i) * D + col0 + lr];
+      for (int i = 0; i < 4; ++i) B.x[i] = p.px[(16 * wv + 4 * lg + i) * D + col0 + lr];
     }
   };
-  if (nch > 0) fetch(nch - 1);
-  for (int ci = nch - 1; ci >= 0; --ci) {
+  // Two buffers in turn, as in the state chain (here in reverse chunk order).
+  auto step = [&](Buf &B, int ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
     float *dse = reinterpret_cast<float *>(ws + L.dse) + tile * D * D;
     float *dun = reinterpret_cast<float *>(ws + L.dun) + tile * C * D;
     __syncthreads();  // the previous chunk is done with the LDS operands
-    rw.store(sW);
-    rk.store(sK);
+    B.w.store(sW);
+    B.k.store(sK);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
@@ -708,15 +723,15 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
         for (int i = 0; i < 4; ++i) dse[(16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
       }
     }
-    const f32x4 x0 = xn;
+    const f32x4 x0 = B.x;
     f32x4 gam[CBW], y0[CBW];
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-      gam[j] = gn[j];
-      y0[j] = yn[j];
+      gam[j] = B.g[j];
+      y0[j] = B.y[j];
     }
     __syncthreads();
-    if (ci > 0) fetch(ci - 1);
+    fetch(B, ci - 2);
     // dUnew = P^T dO + Ke dS_next for the wave's token block
     if (has_rb) {
       f32x4 a0 = zero4(), a1 = zero4();
@@ -750,6 +765,15 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
         dS[j] = dS[j] * gam[j] + (y0[j] - aw);
       }
     }
+  };
+  Buf b0, b1;
+  if (nch > 0) {  // an empty sequence has no tiles: only dS_0 = dS_final below
+    fetch(b0, nch - 1);
+    fetch(b1, nch - 2);
+  }
+  for (int ci = nch - 1; ci >= 0; ci -= 2) {
+    step(b0, ci);
+    if (ci > 0) step(b1, ci - 1);
   }
   if (ds0) {
 #pragma unroll
