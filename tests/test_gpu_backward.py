@@ -81,15 +81,18 @@ def test_backward_every_shape(dtype, d, chunk):
     _check(w, do, dsf, _run(w, do, dsf, chunk))
 
 
-def test_backward_many_pairs_two_launches():
-    """36 (sequence, head) pairs at d=64: each chain's grid is 160 workgroups,
-    so the two no longer fit a 256-CU GPU together and run as two launches
-    (the other cases run both chains in one launch)."""
-    print("[backward] 9 seqs x 4 heads d=64 C=32", flush=True)
-    w = kin.make_prefill(909, H=4, d=64, dtype=kin.BF16, chunk_size=32,
+@pytest.mark.parametrize("dtype,d,chunk,H", [(kin.BF16, 64, 32, 4), (kin.BF16, 128, 64, 2),
+                                             (kin.F32, 64, 16, 4)])
+def test_backward_many_pairs_two_launches(dtype, d, chunk, H):
+    """Nine sequences: 36 (sequence, head) pairs at d=64 (chain grids of 160
+    workgroups) or 18 at d=128 (192 workgroups), so the two chains no longer
+    fit a 256-CU GPU together and run as two launches (the other cases run
+    both chains in one launch)."""
+    print(f"[backward] 9 seqs x {H} heads dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill(909 + d, H=H, d=d, dtype=dtype, chunk_size=chunk,
                          lengths=[40, 0, 7, 65, 1, 33, 64, 16, 90], s0_std=0.05)
-    do, dsf = kin.backward_inputs(910, w.total_tokens, 4, 64, w.num_seqs, kin.BF16)
-    _check(w, do, dsf, _run(w, do, dsf, 32))
+    do, dsf = kin.backward_inputs(910 + d, w.total_tokens, H, d, w.num_seqs, dtype)
+    _check(w, do, dsf, _run(w, do, dsf, chunk))
 
 
 def test_backward_equal_lengths_no_final_gradient():
