@@ -14,8 +14,8 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool head_dims_supported(int32_t d_k, int32_t d_v, kda_dtype dtype) {
   if (d_k != d_v) return false;
-  if (dtype == KDA_DTYPE_BF16) return d_k == 32 || d_k == 64 || d_k == 128;
-  if (dtype == KDA_DTYPE_F32) return d_k == 32 || d_k == 64;
+  if (dtype == KDA_DTYPE_BF16 || dtype == KDA_DTYPE_F32)
+    return d_k == 32 || d_k == 64 || d_k == 128;
   return false;
 }
 

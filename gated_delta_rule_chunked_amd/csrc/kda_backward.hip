@@ -1018,6 +1018,7 @@ hipError_t launch_bwd(const BwdArgs &a, kda_dtype dt) {
     switch (a.d) {
       case 32: return launch_bwd_d<float, 32>(a);
       case 64: return launch_bwd_d<float, 64>(a);
+      case 128: return launch_bwd_d<float, 128>(a);
     }
   }
   return hipErrorInvalidValue;

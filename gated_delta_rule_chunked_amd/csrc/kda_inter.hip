@@ -346,18 +346,23 @@ static hipError_t launch_inter_ct(const FwdArgs &a) {
 
 // Slice width: the fewest rounds of workgroups (one per CU at a time), and
 // the narrowest slice among equals (shortest dependent chain per chunk).
+// fp32 operands at d = 128 keep 16-column slices: the wider slices' fp32
+// fragments do not fit the registers.
 template <typename T, int D, int C>
 static hipError_t launch_inter_c(const FwdArgs &a) {
+  constexpr int MAX_CT = (sizeof(T) == 4 && D == 128) ? 1 : (D >= 64 ? 4 : 2);
   const int64_t units = ((int64_t)a.num_seqs * a.num_heads + 7) / 8;
   const int64_t cus = device_cus();
   auto rounds = [&](int ct) { return cus > 0 ? (8 * units * (D / (16 * ct)) + cus - 1) / cus : 1; };
   int ct = 1;
-  for (int c = 2; c <= 4 && 16 * c <= D; c *= 2)
+  for (int c = 2; c <= MAX_CT; c *= 2)
     if (rounds(c) < rounds(ct)) ct = c;
-  if constexpr (D >= 64) {
+  if constexpr (MAX_CT >= 4) {
     if (ct == 4) return launch_inter_ct<T, D, C, 4>(a);
   }
-  if (ct == 2) return launch_inter_ct<T, D, C, 2>(a);
+  if constexpr (MAX_CT >= 2) {
+    if (ct == 2) return launch_inter_ct<T, D, C, 2>(a);
+  }
   return launch_inter_ct<T, D, C, 1>(a);
 }
 
@@ -382,6 +387,7 @@ hipError_t launch_inter(const FwdArgs &a, kda_dtype dt) {
     switch (a.d) {
       case 32: return launch_inter_d<float, 32>(a);
       case 64: return launch_inter_d<float, 64>(a);
+      case 128: return launch_inter_d<float, 128>(a);
     }
   }
   return hipErrorInvalidValue;

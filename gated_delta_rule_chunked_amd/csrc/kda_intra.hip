@@ -480,6 +480,7 @@ hipError_t launch_intra(const FwdArgs &a, kda_dtype dt) {
     switch (a.d) {
       case 32: return launch_intra_d<float, 32>(a);
       case 64: return launch_intra_d<float, 64>(a);
+      case 128: return launch_intra_d<float, 128>(a);
     }
   }
   return hipErrorInvalidValue;

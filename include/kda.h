@@ -34,9 +34,8 @@
  *     operands on the matrix cores with fp32 accumulation) or
  *     KDA_DTYPE_F32 (fp32 throughout).  log_alpha, beta and the states are
  *     always fp32.
- *   - Supported head sizes: d_k == d_v in {32, 64, 128}; with fp32
- *     operands the prefill and the backward take {32, 64} and the decode
- *     step all three.  Other shapes return KDA_ERROR_NOT_SUPPORTED.
+ *   - Supported head sizes: d_k == d_v in {32, 64, 128}, for both
+ *     dtypes; other shapes return KDA_ERROR_NOT_SUPPORTED.
  *   - Size limits (KDA_ERROR_NOT_SUPPORTED beyond them): total_tokens <=
  *     2^30, num_seqs * num_heads <= 2^26, num_heads <= 65535 and at most
  *     2^22 (chunk, head) tiles, where a call has at most

@@ -53,7 +53,8 @@ def test_workspace_size(lib):
     assert ws(4096, 2, 8, 128, 128, 64, 1) > 0
     assert ws(4096, 2, 8, 96, 96, 64, 1) == 0      # unsupported head size
     assert ws(4096, 2, 8, 128, 128, 48, 1) == 0    # unsupported chunk
-    assert ws(4096, 2, 8, 128, 128, 64, 0) == 0    # fp32 needs d <= 64
+    assert ws(4096, 2, 8, 128, 128, 64, 0) > 0     # fp32 at d = 128
+    assert ws(4096, 2, 8, 96, 96, 64, 0) == 0      # unsupported head size
     assert ws(4096, 2, 8, 128, 64, 64, 1) == 0     # d_k != d_v
     assert ws(-1, 2, 8, 128, 128, 64, 1) == 0
     assert ws(0, 1, 1, 32, 32, 16, 0) > 0
@@ -89,7 +90,6 @@ def test_fwd_rejects_bad_arguments_on_host(lib):
     assert _fwd(lib, dk=96, dv=96) == 2
     assert _fwd(lib, dk=128, dv=64) == 2
     assert _fwd(lib, C=128) == 2
-    assert _fwd(lib, dt=0) == 2                      # fp32 with d = 128
     assert _fwd(lib, n=1, T=1 << 24, H=1024) == 2    # 2^28 (chunk, head) tiles
     assert _fwd(lib, n=1, T=1 << 22, H=64, wsb=16) == 1  # 2^22 tiles pass, workspace fails
 

@@ -57,7 +57,7 @@ def _check_epilogue(y, y_ref, o_ref, wn, tol):
 @pytest.mark.parametrize("with_gate", [True, False])
 @pytest.mark.parametrize("dtype,d,chunk", [(kin.BF16, 128, 64), (kin.BF16, 64, 16),
                                            (kin.BF16, 32, 32), (kin.F32, 32, 16),
-                                           (kin.F32, 64, 32)])
+                                           (kin.F32, 64, 32), (kin.F32, 128, 64)])
 def test_prefill_epilogue(dtype, d, chunk, with_gate):
     print(f"[epilogue] prefill dtype={dtype} d={d} C={chunk} gate={with_gate}", flush=True)
     kda = _kda()

@@ -91,7 +91,7 @@ def test_varlen_sampled_heads():
 
 
 @pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
-                                     (kin.F32, 32), (kin.F32, 64)])
+                                     (kin.F32, 32), (kin.F32, 64), (kin.F32, 128)])
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_ragged_varlen_shapes(dtype, d, chunk):
     """Several tiles, ragged tails, an empty sequence and a one-token sequence,
@@ -256,7 +256,7 @@ def test_decode_full_batch_steps():
 
 
 @pytest.mark.parametrize("dtype,d", [(kin.BF16, 128), (kin.BF16, 64), (kin.BF16, 32),
-                                     (kin.F32, 64), (kin.F32, 32)])
+                                     (kin.F32, 128), (kin.F32, 64), (kin.F32, 32)])
 @pytest.mark.parametrize("n_seqs", [10, 40, 65])
 def test_many_pairs_every_slice_width(dtype, d, n_seqs):
     """Many short packed sequences (4 heads each, lengths 1..150, initial
