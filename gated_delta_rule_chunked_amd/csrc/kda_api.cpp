@@ -1,6 +1,8 @@
 // kda_api.cpp -- the C ABI declared in include/kda.h: host-side argument
 // validation, workspace layout and the ordered launches of the prefill
-// kernels (intra-chunk -> inter-chunk) and of the decode kernel.  Nothing here allocates memory or keeps state.
+// kernels (intra-chunk -> inter-chunk) and of the decode kernel.  Nothing
+// here allocates memory or keeps state; the kernels' launch code keeps, per
+// device, only the CU count and which kernels have had their LDS limit raised.
 #include <hip/hip_runtime.h>
 
 #include "kda.h"

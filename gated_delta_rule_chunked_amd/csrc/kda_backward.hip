@@ -960,18 +960,13 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   constexpr size_t lds_state = state_lds_bytes<D, C>(), lds_dstate = dstate_lds_bytes<D, C>();
   constexpr size_t lds_chains = lds_state > lds_dstate ? lds_state : lds_dstate;
   // 80,384 bytes at the largest shape (d = 128, C = 64)
-  static const hipError_t a1 = hipFuncSetAttribute(
-      (const void *)bwd_state_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)lds_state);
-  static const hipError_t a2 = hipFuncSetAttribute(
-      (const void *)bwd_dstate_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)lds_dstate);
-  static const hipError_t a3 = hipFuncSetAttribute(
-      (const void *)bwd_chains_kernel<D, C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)lds_chains);
-  if (a1 != hipSuccess) return a1;
-  if (a2 != hipSuccess) return a2;
-  if (a3 != hipSuccess) return a3;
+  static std::atomic<unsigned long long> raised1{0}, raised2{0}, raised3{0};
+  hipError_t e = raise_lds_limit((const void *)bwd_state_kernel<D, C>, (int)lds_state, raised1);
+  if (e == hipSuccess)
+    e = raise_lds_limit((const void *)bwd_dstate_kernel<D, C>, (int)lds_dstate, raised2);
+  if (e == hipSuccess)
+    e = raise_lds_limit((const void *)bwd_chains_kernel<D, C>, (int)lds_chains, raised3);
+  if (e != hipSuccess) return e;
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
                        d_o, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,

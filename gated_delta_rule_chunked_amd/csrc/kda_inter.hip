@@ -313,15 +313,14 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 // Compute units of the current device (0 if unknown), looked up once per
 // device ordinal.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // zero-initialised: not looked up yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      cus[dev] = n;
-  }
-  return cus[dev];
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0 &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    cus[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <typename T, int D, int C, int CT>

@@ -2,6 +2,7 @@
 // launchers: the prefill workspace layout and the launcher entry points.
 #pragma once
 
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -168,6 +169,22 @@ struct BwdArgs {
 
 // Compute units of the current device (0 if unknown); cached per device.
 int device_cus();
+
+// Raises `kernel`'s dynamic-LDS limit to `bytes` on the current device, once
+// per device (the limit is a per-device property of a kernel): `done` is the
+// launch site's own bit set of devices already raised.  Concurrent first
+// calls may both raise it, which is harmless.  Allocates nothing.
+inline hipError_t raise_lds_limit(const void *kernel, int bytes,
+                                  std::atomic<unsigned long long> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
 // Validates cu_seqlens [N + 1] (cu[0] = 0, non-decreasing, cu[N] = total) and
 // ORs KDA_FLAG_BAD_CU_SEQLENS into *flags when it fails.

@@ -437,8 +437,8 @@ template <typename T, int D, int C, bool RAW>
 static hipError_t launch_intra_t(const FwdArgs &a) {
   using Cfg = IntraCfg<T, D, C>;
   auto kern = intra_chunk_kernel<T, D, C, RAW>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS_BYTES);
+  static std::atomic<unsigned long long> lds_raised{0};
+  const hipError_t attr = raise_lds_limit((const void *)kern, Cfg::LDS_BYTES, lds_raised);
   if (attr != hipSuccess) return attr;
   const dim3 grid((unsigned)a.grid_chunks * (unsigned)a.num_heads);
   char *ws = a.ws;
