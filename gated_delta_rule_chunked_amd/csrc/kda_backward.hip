@@ -374,6 +374,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_mm[MM];
   __shared__ __align__(16) float s_a[C * LA];  // A = strict_lower(beta M), for the substitution
+  __shared__ __align__(16) float s_do[C * D];  // dO, zero past the chunk's end
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
   int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
   locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
@@ -381,8 +382,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-  float *tb = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
-  float *dos = tb + C * C;  // T Diag(beta) [C][C]; dO, zero past the chunk's end (scratch)
+  float *tb = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;  // T Diag(beta)
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
   // cumulative log-decay per channel (rows past the end add nothing); every
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
     *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
     *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
-    *reinterpret_cast<f32x4 *>(dos + e) = ov;
+    *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
   __syncthreads();
   block_mm<C, C, D, false, true>(p.mm, C, p.kt, D, p.kh, D, 1.f, false, s_mm);  // M = Kt Kh^T
@@ -463,10 +463,10 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   block_mm<C, D, C, false, false>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
   // the two terms of the state-gradient recursion that do not depend on it:
   // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke
-  block_mm<C, D, C, true, false>(p.px, D, p.pm, C, dos, D, 1.f, false, s_mm);
+  block_mm<C, D, C, true, false>(p.px, D, p.pm, C, s_do, D, 1.f, false, s_mm);
 #pragma unroll
   for (int m0 = 0; m0 < D; m0 += YM)
-    block_mm<YM, D, C, true, false>(p.qy + m0 * D, D, p.qt + m0, D, dos, D, 1.f, false, s_mm);
+    block_mm<YM, D, C, true, false>(p.qy + m0 * D, D, p.qt + m0, D, s_do, D, 1.f, false, s_mm);
 }
 
 // ---- chain helpers ----------------------------------------------------------
