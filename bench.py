@@ -482,7 +482,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this operator build runs on exactly one GPU; "
+        print(f"bench.py: the operator runs on one GPU only; "
               f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported", file=sys.stderr)
         sys.exit(2)
     extra = [] if args.extra in ("", "none") else args.extra.split(",")
