@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   KDA_SUCCESS = 0,
   KDA_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, bad size, small workspace */
-  KDA_ERROR_NOT_SUPPORTED = 2, /* valid request this build has no kernel for */
+  KDA_ERROR_NOT_SUPPORTED = 2, /* valid request the library has no kernel for */
   KDA_ERROR_LAUNCH_FAILED = 3  /* the HIP runtime refused a kernel launch */
 } kda_status;
 
