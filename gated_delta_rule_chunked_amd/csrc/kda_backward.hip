@@ -91,9 +91,11 @@ constexpr int mm_lds() {
 // A matrix-core step reads a lane's four contraction values as one 16-byte
 // read in the first layouts and as four 4-byte reads in the others; the
 // padding of 4 keeps both free of bank conflicts.  Ends with a barrier.
-template <int M, int N, int K, bool TA, bool TB, int CAP>
-__device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
-                                              int ldb, float (&lds)[CAP]) {
+// NA = 2: two left operands A[0], A[1] (same shape and leading dimension)
+// against one B, into c[0] and c[1], staging B once per slice.
+template <int M, int N, int K, bool TA, bool TB, int NA, int CAP>
+__device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *const *A, int lda,
+                                                const float *B, int ldb, float (&lds)[CAP]) {
   static_assert(K % 16 == 0, "contraction");
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
   constexpr int LMA = M + 4, LNB = N + 4;           // row strides of the transposed layouts
@@ -101,23 +103,27 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
   constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
   constexpr int SA = TA ? KS * LMA : M * LK, SB = TB ? N * LK : KS * LNB;
-  static_assert(SA + SB <= mm_lds<M, N, K>() && mm_lds<M, N, K>() <= CAP,
+  static_assert(NA == 1 || NA == 2, "one or two left operands");
+  static_assert(SA + SB <= mm_lds<M, N, K>() && NA * SA + SB <= CAP &&
+                    (NA > 1 || mm_lds<M, N, K>() <= CAP),
                 "the caller's LDS buffer holds this product's staging");
-  float *sa = lds, *sb = lds + SA;
+  float *sb = lds + NA * SA;  // A[a]'s slice at lds + a * SA
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  f32x4 ra[PA], rb[PB];
+  f32x4 ra[NA][PA], rb[PB];
   auto load = [&](int k0) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
       const int f = tid + NT * p;
       if (FA % NT == 0 || f < FA) {
         if (TA) {
           const int kk = f / (M / 4), i4 = f % (M / 4);
-          ra[p] = *reinterpret_cast<const f32x4 *>(A + (k0 + kk) * lda + 4 * i4);
+          ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + (k0 + kk) * lda + 4 * i4);
         } else {
           const int i = f / (KS / 4), k4 = f % (KS / 4);
-          ra[p] = *reinterpret_cast<const f32x4 *>(A + i * lda + k0 + 4 * k4);
+          ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + i * lda + k0 + 4 * k4);
         }
       }
     }
@@ -137,15 +143,18 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
   };
   auto store = [&]() {
 #pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
     for (int p = 0; p < PA; ++p) {
+      float *sa = lds + a * SA;
       const int f = tid + NT * p;
       if (FA % NT == 0 || f < FA) {
         if (TA) {
           const int kk = f / (M / 4), i4 = f % (M / 4);
-          *reinterpret_cast<f32x4 *>(sa + kk * LMA + 4 * i4) = ra[p];
+          *reinterpret_cast<f32x4 *>(sa + kk * LMA + 4 * i4) = ra[a][p];
         } else {
           const int i = f / (KS / 4), k4 = f % (KS / 4);
-          *reinterpret_cast<f32x4 *>(sa + i * LK + 4 * k4) = ra[p];
+          *reinterpret_cast<f32x4 *>(sa + i * LK + 4 * k4) = ra[a][p];
         }
       }
     }
@@ -165,7 +174,8 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
   };
   // a lane's operands of a 16-deep step: A(16 rt + lr, ks + 4 lg + u) and
   // B(ks + 4 lg + u, 16 ct + lr), u = 0 .. 3
-  auto frag_a = [&](int rt, int ks) -> f32x4 {
+  auto frag_a = [&](int a, int rt, int ks) -> f32x4 {
+    const float *sa = lds + a * SA;
     if constexpr (TA) {
       f32x4 a;
 #pragma unroll
@@ -198,26 +208,41 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda,
         // + cc, the same tiles as t = wv + 4 q): each A and B fragment is read
         // from LDS once per step and used for a whole row or column of tiles
         constexpr int TM = M / 16, CW = TN / 4;
-        f32x4 af[TM], bf[CW];
-#pragma unroll
-        for (int rr = 0; rr < TM; ++rr) af[rr] = frag_a(rr, ks);
+        f32x4 bf[CW];
 #pragma unroll
         for (int cc = 0; cc < CW; ++cc) bf[cc] = frag_b(wv + 4 * cc, ks);
 #pragma unroll
-        for (int rr = 0; rr < TM; ++rr)
+        for (int a = 0; a < NA; ++a) {
+          f32x4 af[TM];
 #pragma unroll
-          for (int cc = 0; cc < CW; ++cc)
-            c[rr * CW + cc] = mma_f32_k16(af[rr], bf[cc], c[rr * CW + cc]);
+          for (int rr = 0; rr < TM; ++rr) af[rr] = frag_a(a, rr, ks);
+#pragma unroll
+          for (int rr = 0; rr < TM; ++rr)
+#pragma unroll
+            for (int cc = 0; cc < CW; ++cc)
+              c[a][rr * CW + cc] = mma_f32_k16(af[rr], bf[cc], c[a][rr * CW + cc]);
+        }
       } else {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int q = 0; q < TPW; ++q) {
           const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
-          c[q] = mma_f32_k16(frag_a(t / TN, ks), frag_b(t % TN, ks), c[q]);
+          c[a][q] = mma_f32_k16(frag_a(a, t / TN, ks), frag_b(t % TN, ks), c[a][q]);
         }
       }
     }
     __syncthreads();
   }
+}
+
+// c[q] += the wave's tiles of A B (one left operand), as above.
+template <int M, int N, int K, bool TA, bool TB, int CAP>
+__device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
+                                              int ldb, float (&lds)[CAP]) {
+  f32x4 *const cs[1] = {c};
+  const float *const as[1] = {A};
+  mm_accumulate_n<M, N, K, TA, TB, 1>(cs, as, lda, B, ldb, lds);
 }
 
 // out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
@@ -281,6 +306,22 @@ __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, 
   mm_accumulate<M, N, K1, TA1, TB1>(c, A1, lda1, B1, ldb1, lds);
   mm_accumulate<M, N, K2, TA2, TB2>(c, A2, lda2, B2, ldb2, lds);
   mm_store<M, N>(out, ldo, nullptr, 1.f, c);
+}
+
+// out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
+// dimension), staging B once.
+template <int M, int N, int K, bool TA, bool TB, int CAP>
+__device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const float *A1,
+                                              const float *A2, int lda, const float *B, int ldb,
+                                              float (&lds)[CAP]) {
+  f32x4 c1[MmTiles<M, N>::TPW], c2[MmTiles<M, N>::TPW];
+#pragma unroll
+  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c1[q] = c2[q] = zero4();
+  f32x4 *const cs[2] = {c1, c2};
+  const float *const as[2] = {A1, A2};
+  mm_accumulate_n<M, N, K, TA, TB, 2>(cs, as, lda, B, ldb, lds);
+  mm_store<M, N>(out1, ldo, nullptr, 1.f, c1);
+  mm_store<M, N>(out2, ldo, nullptr, 1.f, c2);
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
@@ -369,7 +410,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
   constexpr int LA = C + 4;
   constexpr int YM = D < 64 ? D : 64;  // row block of Qt^T dO
-  constexpr int MM = cmax(cmax(mm_lds<C, C, D>(), mm_lds<C, D, C>()), mm_lds<YM, D, C>());
+  constexpr int MM_PAIR = 3 * C * ((D < 32 ? D : 32) + 4);  // Kt, Qt and Kh slices together
+  constexpr int MM = cmax(cmax(MM_PAIR, mm_lds<C, D, C>()), mm_lds<YM, D, C>());
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_mm[MM];
@@ -427,8 +469,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
   __syncthreads();
-  block_mm<C, C, D, false, true>(p.mm, C, p.kt, D, p.kh, D, 1.f, false, s_mm);  // M = Kt Kh^T
-  block_mm<C, C, D, false, true>(p.pm, C, p.qt, D, p.kh, D, 1.f, false, s_mm);  // Qt Kh^T
+  // M = Kt Kh^T and Qt Kh^T, staging Kh once
+  block_mm_pair<C, C, D, false, true>(p.mm, p.pm, C, p.kt, p.qt, D, p.kh, D, s_mm);
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, s = e % C;
     if (s > r) p.pm[e] = 0.f;  // P = lower incl. diagonal
