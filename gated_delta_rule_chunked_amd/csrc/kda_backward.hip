@@ -409,9 +409,10 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     const T *__restrict__ d_o, const float *__restrict__ g, const float *__restrict__ beta,
     const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
   constexpr int LA = C + 4;
-  constexpr int YM = D < 64 ? D : 64;  // row block of Qt^T dO
+  constexpr int YM = D < 64 ? D : 64;  // row block of dO^T Qt
   constexpr int MM_PAIR = 3 * C * ((D < 32 ? D : 32) + 4);  // Kt, Qt and Kh slices together
-  constexpr int MM = cmax(cmax(MM_PAIR, mm_lds<C, D, C>()), mm_lds<YM, D, C>());
+  constexpr int MM = cmax(cmax(MM_PAIR, mm_lds<C, D, C>()),
+                          cmax(mm_lds<YM, C, C>(), mm_lds<YM, D, C>()));
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_mm[MM];
@@ -465,6 +466,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     *reinterpret_cast<f32x4 *>(p.kh + e) = kv * emg;
     *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
     *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
+    if constexpr (sizeof(T) == 2) {  // the chains' copy of Ke
+      const f32x4 ke4 = kv * egn;
+      bf16x4 kb;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kb[u] = (bf16)ke4[u];
+      *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(tb + C * C) + C * D + e) = kb;
+    }
     *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
     *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
@@ -503,37 +511,89 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   __syncthreads();
   block_mm<C, D, C, false, false>(p.w, D, tb, C, p.kt, D, 1.f, false, s_mm);  // W = (T Diag(beta)) Kt
   block_mm<C, D, C, false, false>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
-  // the two terms of the state-gradient recursion that do not depend on it:
-  // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke
-  block_mm<C, D, C, true, false>(p.px, D, p.pm, C, s_do, D, 1.f, false, s_mm);
+  // the two terms of the state-gradient recursion that do not depend on it,
+  // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke.
+  // They are stored transposed (X^T = dO^T P, Y^T = dO^T Qt): a chain lane's
+  // four rows of one column are then one 16-byte load.
 #pragma unroll
-  for (int m0 = 0; m0 < D; m0 += YM)
-    block_mm<YM, D, C, true, false>(p.qy + m0 * D, D, p.qt + m0, D, s_do, D, 1.f, false, s_mm);
+  for (int n0 = 0; n0 < D; n0 += YM) {
+    block_mm<YM, C, C, true, false>(p.px + n0 * C, C, s_do + n0, D, p.pm, C, 1.f, false, s_mm);
+    block_mm<YM, D, C, true, false>(p.qy + n0 * D, D, s_do + n0, D, p.qt, D, 1.f, false, s_mm);
+  }
+  if constexpr (sizeof(T) == 2) {  // the chains' copy of W
+    __syncthreads();
+    bf16 *wb = reinterpret_cast<bf16 *>(tb + C * C);
+    for (int e4 = tid; e4 < C * D / 4; e4 += NT) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4 *>(p.w + 4 * e4);
+      bf16x4 b4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b4[u] = (bf16)w4[u];
+      *reinterpret_cast<bf16x4 *>(wb + 4 * e4) = b4;
+    }
+  }
 }
 
 // ---- chain helpers ----------------------------------------------------------
-// A chunk's [R][CO] fp32 matrix moved as float4 through registers into LDS
-// rows of stride CO + 4.
-template <int R, int CO>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// A chunk's [R][CO] matrix, stored as fp32 or bf16, moved in 16-byte pieces
+// through registers into fp32 LDS rows of stride CO + 4.  A bf16 piece holds
+// 8 elements, two to a dword (low half first); widening one is a shift.
+template <int R, int CO, typename WT>
 struct Stage {
-  static constexpr int N4 = R * CO / 4, P = (N4 + NT - 1) / NT;
-  f32x4 r[P];
-  __device__ __forceinline__ void load(const float *src) {
+  static constexpr int EV = 16 / (int)sizeof(WT);  // elements per piece
+  static constexpr int NV = R * CO / EV, P = (NV + NT - 1) / NT;
+  static_assert(CO % EV == 0, "a piece stays within one row");
+  u32x4 r[P];
+  __device__ __forceinline__ void load(const WT *src) {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
       const int e = threadIdx.x + NT * m;
-      if (N4 % NT == 0 || e < N4) r[m] = reinterpret_cast<const f32x4 *>(src)[e];
+      if (NV % NT == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
     }
   }
   __device__ __forceinline__ void store(float *dst) const {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
       const int e = threadIdx.x + NT * m;
-      if (N4 % NT == 0 || e < N4)
-        *reinterpret_cast<f32x4 *>(dst + (e / (CO / 4)) * (CO + 4) + 4 * (e % (CO / 4))) = r[m];
+      if (NV % NT == 0 || e < NV) {
+        float *at = dst + (e / (CO / EV)) * (CO + 4) + EV * (e % (CO / EV));
+        if constexpr (EV == 4) {
+          *reinterpret_cast<f32x4 *>(at) = __builtin_bit_cast(f32x4, r[m]);
+        } else {
+          f32x4 lo, hi;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            lo[2 * u] = __uint_as_float(r[m][u] << 16);
+            lo[2 * u + 1] = __uint_as_float(r[m][u] & 0xffff0000u);
+            hi[2 * u] = __uint_as_float(r[m][2 + u] << 16);
+            hi[2 * u + 1] = __uint_as_float(r[m][2 + u] & 0xffff0000u);
+          }
+          *reinterpret_cast<f32x4 *>(at) = lo;
+          *reinterpret_cast<f32x4 *>(at + 4) = hi;
+        }
+      }
     }
   }
 };
+
+// W and Ke as the two chains stream them.  For bf16 inputs they are the bf16
+// copies that the per-tile pass leaves in the tile's scratch, right after
+// T Diag(beta): half the bytes of each chain step, rounded as the forward's
+// own chain rounds them.  The gradient pass reuses that scratch afterwards.
+template <typename WT>
+__device__ __forceinline__ void chain_operands(const BwdLayout &L, char *ws, int64_t tile, int C,
+                                               int D, const WT **w, const WT **ke) {
+  if constexpr (sizeof(WT) == 4) {
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    *w = p.w;
+    *ke = p.ke;
+  } else {
+    const float *x = reinterpret_cast<const float *>(ws + L.scratch) + tile * L.scratch_per_tile;
+    *w = reinterpret_cast<const WT *>(x + C * C);
+    *ke = *w + C * D;
+  }
+}
 
 // The two chains run their per-chunk products on the fp32 matrix cores in
 // 16 x 16 output tiles (mma_f32_k16: lane l = 16 g + c supplies A[c][4g + i]
@@ -577,7 +637,7 @@ constexpr size_t dstate_lds_bytes() {
 // One block per (sequence, head, 16-column slice); each chunk's W and Ke are
 // staged whole in LDS, the next chunk's (and its U tile and gamma) being
 // loaded into registers while this one is computed.
-template <int D, int C>
+template <int D, int C, typename WT>
 __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, int N, int H,
                                             int seq_len, const float *__restrict__ s0,
                                             BwdLayout L, char *ws, float *sm) {
@@ -611,13 +671,16 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
   }
   // one chunk's operands: W and Ke whole, the wave's U tile, e^{G_n}
   struct Buf {
-    Stage<C, D> w, k;
+    Stage<C, D, WT> w, k;
     f32x4 u, g[CBW];
   };
   auto fetch = [&](Buf &B, int ci) {  // chunk min(ci, nch - 1): always in range
-    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + min(ci, nch - 1)) * H + h, C, D);
-    B.w.load(p.w);
-    B.k.load(p.ke);
+    const int64_t tile = (int64_t)(first + min(ci, nch - 1)) * H + h;
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    const WT *w, *ke;
+    chain_operands<WT>(L, ws, tile, C, D, &w, &ke);
+    B.w.load(w);
+    B.k.load(ke);
     B.u = zero4();
     if (has_rb) {
 #pragma unroll
@@ -693,7 +756,7 @@ __device__ __forceinline__ void state_chain(int b, const int *__restrict__ cu, i
 }
 
 // ---- 3. state gradients, chunks in reverse ---------------------------------
-template <int D, int C>
+template <int D, int C, typename WT>
 __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, int N, int H,
                                              int seq_len, const float *__restrict__ dsf,
                                              float *__restrict__ ds0, BwdLayout L, char *ws,
@@ -728,25 +791,24 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
   // one chunk's operands: W and Ke whole, the wave's tiles of X = P^T dO
   // (its token block) and of Y = Qt^T dO (its channel blocks), e^{G_n}
   struct Buf {
-    Stage<C, D> w, k;
+    Stage<C, D, WT> w, k;
     f32x4 x, y[CBW], g[CBW];
   };
   auto fetch = [&](Buf &B, int ci) {  // chunk max(ci, 0): always in range
-    const TilePtr p = tile_ptrs(L, ws, (int64_t)(first + max(ci, 0)) * H + h, C, D);
-    B.w.load(p.w);
-    B.k.load(p.ke);
+    const int64_t tile = (int64_t)(first + max(ci, 0)) * H + h;
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    const WT *w, *ke;
+    chain_operands<WT>(L, ws, tile, C, D, &w, &ke);
+    B.w.load(w);
+    B.k.load(ke);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = min(wv * CBW + j, NCB - 1);
       B.g[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) B.y[j][i] = p.qy[(16 * cb + 4 * lg + i) * D + col0 + lr];
+      B.y[j] = *reinterpret_cast<const f32x4 *>(p.qy + (col0 + lr) * D + 16 * cb + 4 * lg);
     }
     B.x = zero4();
-    if (has_rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) B.x[i] = p.px[(16 * wv + 4 * lg + i) * D + col0 + lr];
-    }
+    if (has_rb) B.x = *reinterpret_cast<const f32x4 *>(p.px + (col0 + lr) * C + 16 * wv + 4 * lg);
   };
   // Two buffers in turn, as in the state chain (here in reverse chunk order).
   auto step = [&](Buf &B, int ci) {
@@ -831,21 +893,21 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
 }
 
 // ---- chain launches ----------------------------------------------------------
-template <int D, int C>
+template <int D, int C, typename WT>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ cu, int N, int H,
                                                        int seq_len, const float *__restrict__ s0,
                                                        BwdLayout L, char *ws) {
   extern __shared__ __align__(16) float sm[];
-  state_chain<D, C>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
+  state_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
 }
 
-template <int D, int C>
+template <int D, int C, typename WT>
 __global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ cu, int N, int H,
                                                         int seq_len, const float *__restrict__ dsf,
                                                         float *__restrict__ ds0, BwdLayout L,
                                                         char *ws) {
   extern __shared__ __align__(16) float sm[];
-  dstate_chain<D, C>((int)blockIdx.x, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+  dstate_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
 }
 
 // The two chains are independent: the state-gradient recursion reads W, Ke
@@ -853,16 +915,16 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ 
 // one launch runs them side by side: workgroups below `split` walk the state
 // gradients backward, the others the states forward.  `split` is a multiple
 // of 8, so each part keeps a pair's slices on one XCD.
-template <int D, int C>
+template <int D, int C, typename WT>
 __global__ __launch_bounds__(NT) void bwd_chains_kernel(
     const int *__restrict__ cu, int N, int H, int seq_len, const float *__restrict__ s0,
     const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws, int split) {
   extern __shared__ __align__(16) float sm[];
   const int b = (int)blockIdx.x;
   if (b < split)
-    dstate_chain<D, C>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+    dstate_chain<D, C, WT>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
   else
-    state_chain<D, C>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
+    state_chain<D, C, WT>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
 }
 
 // ---- 4. per-tile gradients -------------------------------------------------
@@ -1003,11 +1065,11 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   constexpr size_t lds_chains = lds_state > lds_dstate ? lds_state : lds_dstate;
   // 80,384 bytes at the largest shape (d = 128, C = 64)
   static std::atomic<unsigned long long> raised1{0}, raised2{0}, raised3{0};
-  hipError_t e = raise_lds_limit((const void *)bwd_state_kernel<D, C>, (int)lds_state, raised1);
+  hipError_t e = raise_lds_limit((const void *)bwd_state_kernel<D, C, T>, (int)lds_state, raised1);
   if (e == hipSuccess)
-    e = raise_lds_limit((const void *)bwd_dstate_kernel<D, C>, (int)lds_dstate, raised2);
+    e = raise_lds_limit((const void *)bwd_dstate_kernel<D, C, T>, (int)lds_dstate, raised2);
   if (e == hipSuccess)
-    e = raise_lds_limit((const void *)bwd_chains_kernel<D, C>, (int)lds_chains, raised3);
+    e = raise_lds_limit((const void *)bwd_chains_kernel<D, C, T>, (int)lds_chains, raised3);
   if (e != hipSuccess) return e;
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
@@ -1015,13 +1077,13 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
                        a.lay, a.ws);
   const int cus = device_cus();
   if (cus > 0 && 2 * slices <= (unsigned)cus) {
-    hipLaunchKernelGGL((bwd_chains_kernel<D, C>), dim3(2 * slices), dim3(NT), lds_chains,
+    hipLaunchKernelGGL((bwd_chains_kernel<D, C, T>), dim3(2 * slices), dim3(NT), lds_chains,
                        a.stream, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.dsf,
                        a.ds0, a.lay, a.ws, (int)slices);
   } else {
-    hipLaunchKernelGGL((bwd_state_kernel<D, C>), dim3(slices), dim3(NT), lds_state, a.stream,
+    hipLaunchKernelGGL((bwd_state_kernel<D, C, T>), dim3(slices), dim3(NT), lds_state, a.stream,
                        a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
-    hipLaunchKernelGGL((bwd_dstate_kernel<D, C>), dim3(slices), dim3(NT), lds_dstate, a.stream,
+    hipLaunchKernelGGL((bwd_dstate_kernel<D, C, T>), dim3(slices), dim3(NT), lds_dstate, a.stream,
                        a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf, a.ds0, a.lay,
                        a.ws);
   }
