@@ -466,13 +466,6 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     *reinterpret_cast<f32x4 *>(p.kh + e) = kv * emg;
     *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
     *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
-    if constexpr (sizeof(T) == 2) {  // the chains' copy of Ke
-      const f32x4 ke4 = kv * egn;
-      bf16x4 kb;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kb[u] = (bf16)ke4[u];
-      *reinterpret_cast<bf16x4 *>(reinterpret_cast<bf16 *>(tb + C * C) + C * D + e) = kb;
-    }
     *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
     *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
@@ -520,15 +513,39 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     block_mm<YM, C, C, true, false>(p.px + n0 * C, C, s_do + n0, D, p.pm, C, 1.f, false, s_mm);
     block_mm<YM, D, C, true, false>(p.qy + n0 * D, D, s_do + n0, D, p.qt, D, 1.f, false, s_mm);
   }
-  if constexpr (sizeof(T) == 2) {  // the chains' copy of W
+  if constexpr (sizeof(T) == 2) {
+    // the chains' bf16 copies: W and Ke row-major and, for C >= 32, W^T and
+    // Ke^T.  A thread takes 8 rows x 4 channels of each, read as 16-byte rows,
+    // and writes them back as 4-wide rows and as four 8-token columns.
     __syncthreads();
     bf16 *wb = reinterpret_cast<bf16 *>(tb + C * C);
-    for (int e4 = tid; e4 < C * D / 4; e4 += NT) {
-      const f32x4 w4 = *reinterpret_cast<const f32x4 *>(p.w + 4 * e4);
-      bf16x4 b4;
+    for (int e = tid; e < C * D / 32; e += NT) {
+      const int c4 = 4 * (e % (D / 4)), r8 = 8 * (e / (D / 4));
 #pragma unroll
-      for (int u = 0; u < 4; ++u) b4[u] = (bf16)w4[u];
-      *reinterpret_cast<bf16x4 *>(wb + 4 * e4) = b4;
+      for (int mtx = 0; mtx < 2; ++mtx) {
+        const float *src = mtx == 0 ? p.w : p.ke;
+        bf16 *dst = wb + mtx * C * D;
+        f32x4 x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const f32x4 *>(src + (r8 + i) * D + c4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          bf16x4 b4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) b4[u] = (bf16)x[i][u];
+          *reinterpret_cast<bf16x4 *>(dst + (r8 + i) * D + c4) = b4;
+        }
+        if constexpr (C >= 32) {
+          bf16 *dt = wb + (2 + mtx) * C * D;  // [D][C]
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            bf16x8 t8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t8[i] = (bf16)x[i][u];
+            *reinterpret_cast<bf16x8 *>(dt + (c4 + u) * C + r8) = t8;
+          }
+        }
+      }
     }
   }
 }
@@ -581,6 +598,19 @@ struct Stage {
 // copies that the per-tile pass leaves in the tile's scratch, right after
 // T Diag(beta): half the bytes of each chain step, rounded as the forward's
 // own chain rounds them.  The gradient pass reuses that scratch afterwards.
+// For bf16 inputs and C >= 32 the chains also take W^T and Ke^T ([d][C]
+// bf16, the same rounded values), which follow the two copies in scratch.
+__device__ __forceinline__ void chain_operands_t(const BwdLayout &L, char *ws, int64_t tile, int C,
+                                                 int D, const bf16 **wt, const bf16 **ket) {
+  const float *x = reinterpret_cast<const float *>(ws + L.scratch) + tile * L.scratch_per_tile;
+  *wt = reinterpret_cast<const bf16 *>(x + C * C) + 2 * C * D;
+  *ket = *wt + C * D;
+}
+
+// Chains on the bf16 matrix cores: bf16 inputs with chunks of 32 or more.
+template <int C, typename WT>
+constexpr bool chain_bf16() { return sizeof(WT) == 2 && C >= 32; }
+
 template <typename WT>
 __device__ __forceinline__ void chain_operands(const BwdLayout &L, char *ws, int64_t tile, int C,
                                                int D, const WT **w, const WT **ke) {
@@ -623,14 +653,49 @@ __device__ __forceinline__ bool chain_block(int b, int pairs, int *slice, int *p
 }
 inline unsigned chain_grid(int pairs, int ns) { return 8u * (unsigned)((pairs + 7) / 8) * ns; }
 
-template <int D, int C>
+template <int D, int C, typename WT>
 constexpr size_t state_lds_bytes() {
   using Sh = ChainShape<D, C>;
-  return sizeof(float) * (2 * C * Sh::LD + 16 * Sh::LD + 16 * Sh::LU);
+  if constexpr (chain_bf16<C, WT>())  // bf16 [C][D + 8], [D][C + 8], [16][D + 8], [16][C + 8]
+    return sizeof(bf16) * ((C + 16) * (D + 8) + (D + 16) * (C + 8));
+  else
+    return sizeof(float) * (2 * C * Sh::LD + 16 * Sh::LD + 16 * Sh::LU);
 }
-template <int D, int C>
+template <int D, int C, typename WT>
 constexpr size_t dstate_lds_bytes() {
-  return state_lds_bytes<D, C>();  // W, Ke, the transposed dS_next and dUnew
+  return state_lds_bytes<D, C, WT>();  // W, Ke, the transposed dS_next and dUnew
+}
+
+// A chunk's [R][CO] bf16 matrix moved in 16-byte pieces through registers
+// into bf16 LDS rows of stride CO + 8 (rows 4 banks apart, so that the
+// 16-byte fragment reads of 8 consecutive rows hit distinct banks).
+template <int R, int CO>
+struct StageB {
+  static constexpr int NV = R * CO / 8, P = (NV + NT - 1) / NT;
+  static_assert(CO % 8 == 0, "a piece stays within one row");
+  u32x4 r[P];
+  __device__ __forceinline__ void load(const bf16 *src) {
+#pragma unroll
+    for (int m = 0; m < P; ++m) {
+      const int e = threadIdx.x + NT * m;
+      if (NV % NT == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
+    }
+  }
+  __device__ __forceinline__ void store(bf16 *dst) const {
+#pragma unroll
+    for (int m = 0; m < P; ++m) {
+      const int e = threadIdx.x + NT * m;
+      if (NV % NT == 0 || e < NV)
+        *reinterpret_cast<u32x4 *>(dst + (e / (CO / 8)) * (CO + 8) + 8 * (e % (CO / 8))) = r[m];
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
+  return r;
 }
 
 // ---- 2. chunk start states ------------------------------------------------
@@ -892,13 +957,289 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
   }
 }
 
+// ---- 2b/3b. the two chains on the bf16 matrix cores ------------------------
+// Same walks, grids and outputs as above, for bf16 inputs with C >= 32.  The
+// chains stage W (or Ke) row-major and Ke^T (or W^T) as bf16, and round the
+// state (or state gradient) and the Unew (or dUnew) tile to bf16 where they
+// enter a product, as the forward's chain rounds its state.  The state, its
+// gradient and every stored result stay fp32.  Each product is D / 32 or
+// C / 32 steps of v_mfma_f32_16x16x32_bf16 per 16 x 16 tile, where the fp32
+// form needs eight times as many fp32 instructions of twice the cycles.
+template <int D, int C>
+__device__ __forceinline__ void state_chain_bf(int b, const int *__restrict__ cu, int N, int H,
+                                               int seq_len, const float *__restrict__ s0,
+                                               BwdLayout L, char *ws, float *sm) {
+  using Sh = ChainShape<D, C>;
+  constexpr int NRB = Sh::NRB, NCB = Sh::NCB, CBW = Sh::CBW;
+  constexpr int LB = D + 8, LT = C + 8;
+  bf16 *sW = reinterpret_cast<bf16 *>(sm), *sKT = sW + C * LB;  // [C][LB], [D][LT]
+  bf16 *sSt = sKT + D * LT, *sUt = sSt + 16 * LB;                // S^T [16][LB], Unew^T [16][LT]
+  int slice, pair;
+  if (!chain_block<Sh::NS>(b, N * H, &slice, &pair)) return;
+  const int seq = pair / H, h = pair % H;
+  const int col0 = slice * 16;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_rb = wv < NRB;
+  int first, nch, len;
+  seq_chunks(seq, cu, seq_len, C, reinterpret_cast<const int *>(ws + L.seq_first), &first,
+             &nch, &len);
+  if (nch == 0) return;
+  // S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
+  f32x4 S[CBW];
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = wv * CBW + j;
+    S[j] = zero4();
+    if (s0 && cb < NCB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[j][i] = s0[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
+    }
+  }
+  struct Buf {
+    StageB<C, D> w;
+    StageB<D, C> k;
+    f32x4 u, g[CBW];
+  };
+  auto fetch = [&](Buf &B, int ci) {  // chunk min(ci, nch - 1): always in range
+    const int64_t tile = (int64_t)(first + min(ci, nch - 1)) * H + h;
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    const bf16 *w, *ke, *wt, *ket;
+    chain_operands<bf16>(L, ws, tile, C, D, &w, &ke);
+    chain_operands_t(L, ws, tile, C, D, &wt, &ket);
+    B.w.load(w);
+    B.k.load(ket);
+    B.u = zero4();
+    if (has_rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) B.u[i] = p.u[(16 * wv + 4 * lg + i) * D + col0 + lr];
+    }
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = min(wv * CBW + j, NCB - 1);
+      B.g[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+    }
+  };
+  auto step = [&](Buf &B, int ci) {
+    const int64_t tile = (int64_t)(first + ci) * H + h;
+    float *sc = reinterpret_cast<float *>(ws + L.sc) + tile * D * D;
+    __syncthreads();  // the previous chunk is done with the LDS operands
+    B.w.store(sW);
+    B.k.store(sKT);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+        *reinterpret_cast<bf16x4 *>(sSt + lr * LB + 16 * cb + 4 * lg) = to_bf16x4(S[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[(16 * cb + 4 * lg + i) * D + col0 + lr] = S[j][i];
+      }
+    }
+    const f32x4 u0 = B.u;
+    f32x4 gam[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) gam[j] = B.g[j];
+    __syncthreads();
+    fetch(B, ci + 2);
+    // Unew = U - W S for the wave's token block
+    if (has_rb) {
+      f32x4 a0 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sW + (16 * wv + lr) * LB + k0 + 8 * lg);
+        const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(sSt + lr * LB + k0 + 8 * lg);
+        a0 = mma_k32(a, bb, a0);
+      }
+      *reinterpret_cast<bf16x4 *>(sUt + lr * LT + 16 * wv + 4 * lg) = to_bf16x4(u0 - a0);
+    }
+    __syncthreads();
+    // S = Diag(gam) S + Ke^T Unew for the wave's channel blocks
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (NCB % 4 == 0 || cb < NCB) {
+        f32x4 acc = S[j] * gam[j];
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8 *>(sKT + (16 * cb + lr) * LT + k0 + 8 * lg);
+          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(sUt + lr * LT + k0 + 8 * lg);
+          acc = mma_k32(a, bb, acc);
+        }
+        S[j] = acc + 0.f;  // a real VALU read of the result, before any branch
+      }
+    }
+  };
+  Buf b0, b1;
+  fetch(b0, 0);
+  fetch(b1, 1);
+  for (int ci = 0; ci < nch; ci += 2) {
+    step(b0, ci);
+    if (ci + 1 < nch) step(b1, ci + 1);
+  }
+}
+
+template <int D, int C>
+__device__ __forceinline__ void dstate_chain_bf(int b, const int *__restrict__ cu, int N, int H,
+                                                int seq_len, const float *__restrict__ dsf,
+                                                float *__restrict__ ds0, BwdLayout L, char *ws,
+                                                float *sm) {
+  using Sh = ChainShape<D, C>;
+  constexpr int NRB = Sh::NRB, NCB = Sh::NCB, CBW = Sh::CBW;
+  constexpr int LB = D + 8, LT = C + 8;
+  bf16 *sK = reinterpret_cast<bf16 *>(sm), *sWT = sK + C * LB;  // [C][LB], [D][LT]
+  bf16 *sDt = sWT + D * LT, *sUt = sDt + 16 * LB;  // dS_next^T [16][LB], dUnew^T [16][LT]
+  int slice, pair;
+  if (!chain_block<Sh::NS>(b, N * H, &slice, &pair)) return;
+  const int seq = pair / H, h = pair % H;
+  const int col0 = slice * 16;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool has_rb = wv < NRB;
+  int first, nch, len;
+  seq_chunks(seq, cu, seq_len, C, reinterpret_cast<const int *>(ws + L.seq_first), &first,
+             &nch, &len);
+  // dS[j][i] = dS_next[16 cb + 4 lg + i][col0 + lr], cb = wv CBW + j
+  f32x4 dS[CBW];
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) {
+    const int cb = wv * CBW + j;
+    dS[j] = zero4();
+    if (dsf && cb < NCB) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dS[j][i] = dsf[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr];
+    }
+  }
+  struct Buf {
+    StageB<C, D> k;
+    StageB<D, C> w;
+    f32x4 x, y[CBW], g[CBW];
+  };
+  auto fetch = [&](Buf &B, int ci) {  // chunk max(ci, 0): always in range
+    const int64_t tile = (int64_t)(first + max(ci, 0)) * H + h;
+    const TilePtr p = tile_ptrs(L, ws, tile, C, D);
+    const bf16 *w, *ke, *wt, *ket;
+    chain_operands<bf16>(L, ws, tile, C, D, &w, &ke);
+    chain_operands_t(L, ws, tile, C, D, &wt, &ket);
+    B.k.load(ke);
+    B.w.load(wt);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = min(wv * CBW + j, NCB - 1);
+      B.g[j] = *reinterpret_cast<const f32x4 *>(p.gam + 16 * cb + 4 * lg);
+      B.y[j] = *reinterpret_cast<const f32x4 *>(p.qy + (col0 + lr) * D + 16 * cb + 4 * lg);
+    }
+    B.x = zero4();
+    if (has_rb) B.x = *reinterpret_cast<const f32x4 *>(p.px + (col0 + lr) * C + 16 * wv + 4 * lg);
+  };
+  auto step = [&](Buf &B, int ci) {
+    const int64_t tile = (int64_t)(first + ci) * H + h;
+    float *dse = reinterpret_cast<float *>(ws + L.dse) + tile * D * D;
+    float *dun = reinterpret_cast<float *>(ws + L.dun) + tile * C * D;
+    __syncthreads();  // the previous chunk is done with the LDS operands
+    B.k.store(sK);
+    B.w.store(sWT);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+        *reinterpret_cast<bf16x4 *>(sDt + lr * LB + 16 * cb + 4 * lg) = to_bf16x4(dS[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dse[(16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
+      }
+    }
+    const f32x4 x0 = B.x;
+    f32x4 gam[CBW], y0[CBW];
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      gam[j] = B.g[j];
+      y0[j] = B.y[j];
+    }
+    __syncthreads();
+    fetch(B, ci - 2);
+    // dUnew = P^T dO + Ke dS_next for the wave's token block
+    if (has_rb) {
+      f32x4 a0 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (16 * wv + lr) * LB + k0 + 8 * lg);
+        const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(sDt + lr * LB + k0 + 8 * lg);
+        a0 = mma_k32(a, bb, a0);
+      }
+      const f32x4 du = x0 + a0;
+      *reinterpret_cast<bf16x4 *>(sUt + lr * LT + 16 * wv + 4 * lg) = to_bf16x4(du);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dun[(16 * wv + 4 * lg + i) * D + col0 + lr] = du[i];
+    }
+    __syncthreads();
+    // dS = Diag(gam) dS_next + Qt^T dO - W^T dUnew for the wave's channel blocks
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (NCB % 4 == 0 || cb < NCB) {
+        f32x4 aw = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8 *>(sWT + (16 * cb + lr) * LT + k0 + 8 * lg);
+          const bf16x8 bb = *reinterpret_cast<const bf16x8 *>(sUt + lr * LT + k0 + 8 * lg);
+          aw = mma_k32(a, bb, aw);
+        }
+        dS[j] = dS[j] * gam[j] + (y0[j] - aw);
+      }
+    }
+  };
+  Buf b0, b1;
+  if (nch > 0) {  // an empty sequence has no tiles: only dS_0 = dS_final below
+    fetch(b0, nch - 1);
+    fetch(b1, nch - 2);
+  }
+  for (int ci = nch - 1; ci >= 0; ci -= 2) {
+    step(b0, ci);
+    if (ci > 0) step(b1, ci - 1);
+  }
+  if (ds0) {
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = wv * CBW + j;
+      if (cb < NCB) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ds0[((int64_t)pair * D + 16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
+      }
+    }
+  }
+}
+
+template <int D, int C, typename WT>
+__device__ __forceinline__ void run_state_chain(int b, const int *cu, int N, int H, int seq_len,
+                                                const float *s0, BwdLayout L, char *ws,
+                                                float *sm) {
+  if constexpr (chain_bf16<C, WT>())
+    state_chain_bf<D, C>(b, cu, N, H, seq_len, s0, L, ws, sm);
+  else
+    state_chain<D, C, WT>(b, cu, N, H, seq_len, s0, L, ws, sm);
+}
+
+template <int D, int C, typename WT>
+__device__ __forceinline__ void run_dstate_chain(int b, const int *cu, int N, int H, int seq_len,
+                                                 const float *dsf, float *ds0, BwdLayout L,
+                                                 char *ws, float *sm) {
+  if constexpr (chain_bf16<C, WT>())
+    dstate_chain_bf<D, C>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+  else
+    dstate_chain<D, C, WT>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+}
+
 // ---- chain launches ----------------------------------------------------------
 template <int D, int C, typename WT>
 __global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ cu, int N, int H,
                                                        int seq_len, const float *__restrict__ s0,
                                                        BwdLayout L, char *ws) {
   extern __shared__ __align__(16) float sm[];
-  state_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
+  run_state_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, s0, L, ws, sm);
 }
 
 template <int D, int C, typename WT>
@@ -907,7 +1248,7 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ 
                                                         float *__restrict__ ds0, BwdLayout L,
                                                         char *ws) {
   extern __shared__ __align__(16) float sm[];
-  dstate_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+  run_dstate_chain<D, C, WT>((int)blockIdx.x, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
 }
 
 // The two chains are independent: the state-gradient recursion reads W, Ke
@@ -922,9 +1263,9 @@ __global__ __launch_bounds__(NT) void bwd_chains_kernel(
   extern __shared__ __align__(16) float sm[];
   const int b = (int)blockIdx.x;
   if (b < split)
-    dstate_chain<D, C, WT>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
+    run_dstate_chain<D, C, WT>(b, cu, N, H, seq_len, dsf, ds0, L, ws, sm);
   else
-    state_chain<D, C, WT>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
+    run_state_chain<D, C, WT>(b - split, cu, N, H, seq_len, s0, L, ws, sm);
 }
 
 // ---- 4. per-tile gradients -------------------------------------------------
@@ -1061,7 +1402,7 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   const unsigned slices = chain_grid(a.num_seqs * a.num_heads, D / 16);
   const T *q = reinterpret_cast<const T *>(a.q), *k = reinterpret_cast<const T *>(a.k);
   const T *v = reinterpret_cast<const T *>(a.v), *d_o = reinterpret_cast<const T *>(a.d_o);
-  constexpr size_t lds_state = state_lds_bytes<D, C>(), lds_dstate = dstate_lds_bytes<D, C>();
+  constexpr size_t lds_state = state_lds_bytes<D, C, T>(), lds_dstate = dstate_lds_bytes<D, C, T>();
   constexpr size_t lds_chains = lds_state > lds_dstate ? lds_state : lds_dstate;
   // 80,384 bytes at the largest shape (d = 128, C = 64)
   static std::atomic<unsigned long long> raised1{0}, raised2{0}, raised3{0};
