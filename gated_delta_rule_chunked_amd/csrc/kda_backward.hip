@@ -93,10 +93,112 @@ constexpr int mm_lds() {
 // padding of 4 keeps both free of bank conflicts.  Ends with a barrier.
 // NA = 2: two left operands A[0], A[1] (same shape and leading dimension)
 // against one B, into c[0] and c[1], staging B once per slice.
-template <int M, int N, int K, bool TA, bool TB, int NA, int CAP>
+// The bf16 form (BF, for bf16 inputs) of a product whose operands are both
+// read along the contraction (A by rows, B transposed) with K a multiple of
+// 32: each K slice of 32 is rounded to bf16 as it is staged (rows of stride
+// 40, 4 banks apart over 8 rows), and a 16 x 16 tile takes one
+// v_mfma_f32_16x16x32_bf16 per slice.  Accumulation stays fp32.
+template <int M, int N, int K, int NA, int CAP>
+__device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *const *A, int lda,
+                                                 const float *B, int ldb, float (&lds)[CAP]) {
+  static_assert(K % 32 == 0, "contraction");
+  constexpr int KB = 32, LB = KB + 8;
+  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
+  constexpr int GA = M * KB / 4, GB = N * KB / 4;  // float4 per slice
+  constexpr int QA = (GA + NT - 1) / NT, QB = (GB + NT - 1) / NT;
+  constexpr int SA = M * LB, SB = N * LB;  // bf16 elements
+  static_assert(2 * (NA * SA + SB) <= 4 * CAP, "the caller's LDS buffer holds the staging");
+  bf16 *la = reinterpret_cast<bf16 *>(lds), *lb = la + NA * SA;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x4 ra[NA][QA], rb[QB];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int p = 0; p < QA; ++p) {
+      const int f = tid + NT * p;
+      if (GA % NT == 0 || f < GA)
+        ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + (f / 8) * lda + k0 + 4 * (f % 8));
+    }
+#pragma unroll
+    for (int p = 0; p < QB; ++p) {
+      const int f = tid + NT * p;
+      if (GB % NT == 0 || f < GB)
+        rb[p] = *reinterpret_cast<const f32x4 *>(B + (f / 8) * ldb + k0 + 4 * (f % 8));
+    }
+  };
+  auto cvt = [](f32x4 v) {
+    bf16x4 r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = (bf16)v[u];
+    return r;
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int p = 0; p < QA; ++p) {
+      const int f = tid + NT * p;
+      if (GA % NT == 0 || f < GA)
+        *reinterpret_cast<bf16x4 *>(la + a * SA + (f / 8) * LB + 4 * (f % 8)) = cvt(ra[a][p]);
+    }
+#pragma unroll
+    for (int p = 0; p < QB; ++p) {
+      const int f = tid + NT * p;
+      if (GB % NT == 0 || f < GB)
+        *reinterpret_cast<bf16x4 *>(lb + (f / 8) * LB + 4 * (f % 8)) = cvt(rb[p]);
+    }
+  };
+  auto frag_a = [&](int a, int rt) {
+    return *reinterpret_cast<const bf16x8 *>(la + a * SA + (16 * rt + lr) * LB + 8 * lg);
+  };
+  auto frag_b = [&](int ct) {
+    return *reinterpret_cast<const bf16x8 *>(lb + (16 * ct + lr) * LB + 8 * lg);
+  };
+  load(0);
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    store();
+    __syncthreads();
+    if (k0 + KB < K) load(k0 + KB);  // next slice in flight during this one
+    if constexpr (TN % 4 == 0) {
+      constexpr int TM = M / 16, CW = TN / 4;
+      bf16x8 bfr[CW];
+#pragma unroll
+      for (int cc = 0; cc < CW; ++cc) bfr[cc] = frag_b(wv + 4 * cc);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        bf16x8 afr[TM];
+#pragma unroll
+        for (int rr = 0; rr < TM; ++rr) afr[rr] = frag_a(a, rr);
+#pragma unroll
+        for (int rr = 0; rr < TM; ++rr)
+#pragma unroll
+          for (int cc = 0; cc < CW; ++cc)
+            c[a][rr * CW + cc] = mma_k32(afr[rr], bfr[cc], c[a][rr * CW + cc]);
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
+        c[a][q] = mma_k32(frag_a(a, t / TN), frag_b(t % TN), c[a][q]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int CAP>
 __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *const *A, int lda,
                                                 const float *B, int ldb, float (&lds)[CAP]) {
   static_assert(K % 16 == 0, "contraction");
+  if constexpr (BF && !TA && TB && K % 32 == 0) {
+    mm_accumulate_bf<M, N, K, NA>(c, A, lda, B, ldb, lds);
+    return;
+  }
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
   constexpr int LMA = M + 4, LNB = N + 4;           // row strides of the transposed layouts
   constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
@@ -237,12 +339,12 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
 }
 
 // c[q] += the wave's tiles of A B (one left operand), as above.
-template <int M, int N, int K, bool TA, bool TB, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
 __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
                                               int ldb, float (&lds)[CAP]) {
   f32x4 *const cs[1] = {c};
   const float *const as[1] = {A};
-  mm_accumulate_n<M, N, K, TA, TB, 1>(cs, as, lda, B, ldb, lds);
+  mm_accumulate_n<M, N, K, TA, TB, 1, BF>(cs, as, lda, B, ldb, lds);
 }
 
 // out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
@@ -272,45 +374,46 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
 
 // out = alpha A B (+ out when acc).  `lds` holds at least mm_lds<M, N, K>()
 // floats.
-template <int M, int N, int K, bool TA, bool TB, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
 __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
                                          const float *B, int ldb, float alpha, bool acc,
                                          float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K, TA, TB>(c, A, lda, B, ldb, lds);
+  mm_accumulate<M, N, K, TA, TB, BF>(c, A, lda, B, ldb, lds);
   mm_store<M, N>(out, ldo, acc ? out : nullptr, alpha, c);
 }
 
 // out = init + alpha A B (init has leading dimension ldo).
-template <int M, int N, int K, bool TA, bool TB, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
 __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
                                               const float *A, int lda, const float *B, int ldb,
                                               float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K, TA, TB>(c, A, lda, B, ldb, lds);
+  mm_accumulate<M, N, K, TA, TB, BF>(c, A, lda, B, ldb, lds);
   mm_store<M, N>(out, ldo, init, alpha, c);
 }
 
 // out = A1 B1 + A2 B2, both products accumulated in registers.
-template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2, int CAP>
+template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2, bool BF = false,
+          int CAP>
 __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, int lda1,
                                           const float *B1, int ldb1, const float *A2, int lda2,
                                           const float *B2, int ldb2, float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K1, TA1, TB1>(c, A1, lda1, B1, ldb1, lds);
-  mm_accumulate<M, N, K2, TA2, TB2>(c, A2, lda2, B2, ldb2, lds);
+  mm_accumulate<M, N, K1, TA1, TB1, BF>(c, A1, lda1, B1, ldb1, lds);
+  mm_accumulate<M, N, K2, TA2, TB2, BF>(c, A2, lda2, B2, ldb2, lds);
   mm_store<M, N>(out, ldo, nullptr, 1.f, c);
 }
 
 // out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
 // dimension), staging B once.
-template <int M, int N, int K, bool TA, bool TB, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
 __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const float *A1,
                                               const float *A2, int lda, const float *B, int ldb,
                                               float (&lds)[CAP]) {
@@ -319,7 +422,7 @@ __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo,
   for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c1[q] = c2[q] = zero4();
   f32x4 *const cs[2] = {c1, c2};
   const float *const as[2] = {A1, A2};
-  mm_accumulate_n<M, N, K, TA, TB, 2>(cs, as, lda, B, ldb, lds);
+  mm_accumulate_n<M, N, K, TA, TB, 2, BF>(cs, as, lda, B, ldb, lds);
   mm_store<M, N>(out1, ldo, nullptr, 1.f, c1);
   mm_store<M, N>(out2, ldo, nullptr, 1.f, c2);
 }
@@ -471,7 +574,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   }
   __syncthreads();
   // M = Kt Kh^T and Qt Kh^T, staging Kh once
-  block_mm_pair<C, C, D, false, true>(p.mm, p.pm, C, p.kt, p.qt, D, p.kh, D, s_mm);
+  constexpr bool BF = sizeof(T) == 2;  // bf16 matrix cores where both operands allow
+  block_mm_pair<C, C, D, false, true, BF>(p.mm, p.pm, C, p.kt, p.qt, D, p.kh, D, s_mm);
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, s = e % C;
     if (s > r) p.pm[e] = 0.f;  // P = lower incl. diagonal
@@ -1318,22 +1422,25 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
   __syncthreads();
   block_mm_init<C, D, D, false, false>(unew, D, p.u, -1.f, p.w, D, sc, D, s_mm);  // U - W S
   row_dots<D, D>(s_dgam, dse, sc, D, false);                   // dgam = rowsum(dS_next * S)
-  block_mm<C, C, D, false, true>(s_dp, C, dot, D, unew, D, 1.f, false, s_mm);  // dO Unew^T
+  constexpr bool BF = sizeof(T) == 2;  // bf16 matrix cores where both operands allow
+  block_mm<C, C, D, false, true, BF>(s_dp, C, dot, D, unew, D, 1.f, false, s_mm);  // dO Unew^T
   for (int e = tid; e < CC; e += NT)
     if (e % C > e / C) s_dp[e] = 0.f;  // dP: lower incl. diagonal
   __syncthreads();
   // dQt = dO S^T + dP Kh
-  block_mm2<C, D, D, false, true, C, false, false>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D, s_mm);
-  block_mm<C, D, D, false, true>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
-  block_mm<C, D, D, false, true>(dw, D, dun, D, sc, D, -1.f, false, s_mm);    // -dUnew S^T
+  block_mm2<C, D, D, false, true, C, false, false, BF>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D,
+                                                       s_mm);
+  block_mm<C, D, D, false, true, BF>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
+  block_mm<C, D, D, false, true, BF>(dw, D, dun, D, sc, D, -1.f, false, s_mm);  // -dUnew S^T
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
-  block_mm2<C, C, D, false, true, D, false, true>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D, s_mm);
+  block_mm2<C, C, D, false, true, D, false, true, BF>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D,
+                                                      s_mm);
   for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e % C];
   __syncthreads();
   block_mm<C, D, C, true, false>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);   // T^T dW
   block_mm<C, D, C, true, false>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);   // T^T dUnew
   block_mm<C, C, C, true, false>(s_xm, C, p.tm, C, s_dt, C, 1.f, false, s_mm);  // T^T dT
-  block_mm<C, C, C, false, true>(s_dt, C, s_xm, C, p.tm, C, -1.f, false, s_mm); // dA (pre-mask)
+  block_mm<C, C, C, false, true, BF>(s_dt, C, s_xm, C, p.tm, C, -1.f, false, s_mm);  // dA (pre-mask)
   for (int e = tid; e < CC; e += NT)
     if (e % C >= e / C) s_dt[e] = 0.f;  // dA strictly lower
   __syncthreads();
