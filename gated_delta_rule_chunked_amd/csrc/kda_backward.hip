@@ -51,11 +51,19 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 256;  // threads per workgroup, all kernels
+constexpr int NTC = 256;  // threads per workgroup of the chains
+
+// Threads per workgroup of the per-tile kernels: eight wavefronts where
+// every product has enough 16 x 16 tiles to share (d >= 64 and C = 64), so
+// that twice as many slice loads are in flight per tile; four otherwise.
+// With fewer tiles per wave the compiler places some accumulator reads
+// right behind the tile-bound branch, which the assembly scan rejects.
+template <int D, int C>
+constexpr int bwd_threads() { return D >= 64 && C >= 64 ? 512 : 256; }
 
 // Products of the backward, on the fp32 matrix cores.  An M x N output
 // (M <= 64, N <= 128, multiples of 16) is cut into 16 x 16 tiles, tile
-// t = (t / (N/16), t % (N/16)) computed by wavefront t % 4 with
+// t = (t / (N/16), t % (N/16)) computed by wavefront t % NW (NW wavefronts) with
 // mma_f32_k16.  Operands: A(i, k) = TA ? A[k][i] : A[i][k] and
 // B(k, j) = TB ? B[j][k] : B[k][j], row-major with leading dimensions a
 // multiple of 4, 16-byte aligned, in global memory or LDS.  K slices of 32
@@ -64,10 +72,11 @@ constexpr int NT = 256;  // threads per workgroup, all kernels
 // contiguous, so that each operand of a 16-deep step is one 16-byte read
 // per lane.  Waves past the last tile repeat it (no branch around the
 // matrix instructions) and store nothing.
-template <int M, int N>
+template <int M, int N, int NT = 256>
 struct MmTiles {
+  static constexpr int NW = NT / 64;
   static_assert(M % 16 == 0 && N % 16 == 0 && M <= 64 && N <= 128, "shape");
-  static constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + 3) / 4;
+  static constexpr int TN = N / 16, TT = (M / 16) * TN, TPW = (TT + NW - 1) / NW;
 };
 
 // LDS floats that a product with contraction K stages, for either layout
@@ -81,7 +90,7 @@ constexpr int mm_lds() {
   return (M + N + 8) * ((K < 32 ? K : 32) + 4);
 }
 
-// c[q] (MmTiles<M, N>::TPW accumulators) += the wave's tiles of A B
+// c[q] (MmTiles<M, N, NT>::TPW accumulators) += the wave's tiles of A B
 // (contraction K).  Each K slice is staged in LDS in the order its global
 // rows come in, so every staging store is one 16-byte write:
 //   A: sa[i][kk] = A(i, k0 + kk), row stride KS + 4, when A is read by rows
@@ -98,12 +107,13 @@ constexpr int mm_lds() {
 // 32: each K slice of 32 is rounded to bf16 as it is staged (rows of stride
 // 40, 4 banks apart over 8 rows), and a 16 x 16 tile takes one
 // v_mfma_f32_16x16x32_bf16 per slice.  Accumulation stays fp32.
-template <int M, int N, int K, int NA, int CAP>
+template <int M, int N, int K, int NA, int NT, int CAP>
 __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *const *A, int lda,
                                                  const float *B, int ldb, float (&lds)[CAP]) {
+  constexpr int NW = NT / 64;
   static_assert(K % 32 == 0, "contraction");
   constexpr int KB = 32, LB = KB + 8;
-  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
+  constexpr int TN = MmTiles<M, N, NT>::TN, TT = MmTiles<M, N, NT>::TT, TPW = MmTiles<M, N, NT>::TPW;
   constexpr int GA = M * KB / 4, GB = N * KB / 4;  // float4 per slice
   constexpr int QA = (GA + NT - 1) / NT, QB = (GB + NT - 1) / NT;
   constexpr int SA = M * LB, SB = N * LB;  // bf16 elements
@@ -162,11 +172,11 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *c
     store();
     __syncthreads();
     if (k0 + KB < K) load(k0 + KB);  // next slice in flight during this one
-    if constexpr (TN % 4 == 0) {
-      constexpr int TM = M / 16, CW = TN / 4;
+    if constexpr (TN % NW == 0) {
+      constexpr int TM = M / 16, CW = TN / NW;
       bf16x8 bfr[CW];
 #pragma unroll
-      for (int cc = 0; cc < CW; ++cc) bfr[cc] = frag_b(wv + 4 * cc);
+      for (int cc = 0; cc < CW; ++cc) bfr[cc] = frag_b(wv + NW * cc);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         bf16x8 afr[TM];
@@ -183,7 +193,7 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *c
       for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
+        const int t = TT % NW == 0 ? wv + NW * q : min(wv + NW * q, TT - 1);
         c[a][q] = mma_k32(frag_a(a, t / TN), frag_b(t % TN), c[a][q]);
       }
     }
@@ -191,17 +201,18 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *c
   }
 }
 
-template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int CAP>
+template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int NT = 256, int CAP>
 __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *const *A, int lda,
                                                 const float *B, int ldb, float (&lds)[CAP]) {
+  constexpr int NW = NT / 64;
   static_assert(K % 16 == 0, "contraction");
   if constexpr (BF && !TA && TB && K % 32 == 0) {
-    mm_accumulate_bf<M, N, K, NA>(c, A, lda, B, ldb, lds);
+    mm_accumulate_bf<M, N, K, NA, NT>(c, A, lda, B, ldb, lds);
     return;
   }
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
   constexpr int LMA = M + 4, LNB = N + 4;           // row strides of the transposed layouts
-  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
+  constexpr int TN = MmTiles<M, N, NT>::TN, TT = MmTiles<M, N, NT>::TT, TPW = MmTiles<M, N, NT>::TPW;
   constexpr int FA = M * KS / 4, FB = N * KS / 4;  // float4 per slice
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
   constexpr int SA = TA ? KS * LMA : M * LK, SB = TB ? N * LK : KS * LNB;
@@ -305,14 +316,14 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
     if (k0 + KS < K) load(k0 + KS);  // next slice in flight during this one
 #pragma unroll
     for (int ks = 0; ks < KS; ks += 16) {
-      if constexpr (TN % 4 == 0) {
+      if constexpr (TN % NW == 0) {
         // wave wv owns tile columns wv + 4 cc of every tile row (q = row * CW
         // + cc, the same tiles as t = wv + 4 q): each A and B fragment is read
         // from LDS once per step and used for a whole row or column of tiles
-        constexpr int TM = M / 16, CW = TN / 4;
+        constexpr int TM = M / 16, CW = TN / NW;
         f32x4 bf[CW];
 #pragma unroll
-        for (int cc = 0; cc < CW; ++cc) bf[cc] = frag_b(wv + 4 * cc, ks);
+        for (int cc = 0; cc < CW; ++cc) bf[cc] = frag_b(wv + NW * cc, ks);
 #pragma unroll
         for (int a = 0; a < NA; ++a) {
           f32x4 af[TM];
@@ -329,7 +340,7 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
         for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int q = 0; q < TPW; ++q) {
-          const int t = TT % 4 == 0 ? wv + 4 * q : min(wv + 4 * q, TT - 1);
+          const int t = TT % NW == 0 ? wv + NW * q : min(wv + NW * q, TT - 1);
           c[a][q] = mma_f32_k16(frag_a(a, t / TN, ks), frag_b(t % TN, ks), c[a][q]);
         }
       }
@@ -339,20 +350,21 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
 }
 
 // c[q] += the wave's tiles of A B (one left operand), as above.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
 __device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
                                               int ldb, float (&lds)[CAP]) {
   f32x4 *const cs[1] = {c};
   const float *const as[1] = {A};
-  mm_accumulate_n<M, N, K, TA, TB, 1, BF>(cs, as, lda, B, ldb, lds);
+  mm_accumulate_n<M, N, K, TA, TB, 1, BF, NT>(cs, as, lda, B, ldb, lds);
 }
 
 // out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
 // leading dimension ldo for both).  Ends with a barrier.
-template <int M, int N>
+template <int M, int N, int NT = 256>
 __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init, float alpha,
                                          f32x4 *c) {
-  constexpr int TN = MmTiles<M, N>::TN, TT = MmTiles<M, N>::TT, TPW = MmTiles<M, N>::TPW;
+  constexpr int NW = NT / 64;
+  constexpr int TN = MmTiles<M, N, NT>::TN, TT = MmTiles<M, N, NT>::TT, TPW = MmTiles<M, N, NT>::TPW;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the results reach ordinary registers here, in straight-line code, before
@@ -361,8 +373,8 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
   for (int q = 0; q < TPW; ++q) asm volatile("" : "+v"(c[q]));
 #pragma unroll
   for (int q = 0; q < TPW; ++q) {
-    const int t = wv + 4 * q;
-    if (TT % 4 == 0 || t < TT) {
+    const int t = wv + NW * q;
+    if (TT % NW == 0 || t < TT) {
       const int at = (16 * (t / TN) + 4 * lg) * ldo + 16 * (t % TN) + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -374,57 +386,57 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
 
 // out = alpha A B (+ out when acc).  `lds` holds at least mm_lds<M, N, K>()
 // floats.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
 __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
                                          const float *B, int ldb, float alpha, bool acc,
                                          float (&lds)[CAP]) {
-  f32x4 c[MmTiles<M, N>::TPW];
+  f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
-  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K, TA, TB, BF>(c, A, lda, B, ldb, lds);
-  mm_store<M, N>(out, ldo, acc ? out : nullptr, alpha, c);
+  for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K, TA, TB, BF, NT>(c, A, lda, B, ldb, lds);
+  mm_store<M, N, NT>(out, ldo, acc ? out : nullptr, alpha, c);
 }
 
 // out = init + alpha A B (init has leading dimension ldo).
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
 __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
                                               const float *A, int lda, const float *B, int ldb,
                                               float (&lds)[CAP]) {
-  f32x4 c[MmTiles<M, N>::TPW];
+  f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
-  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K, TA, TB, BF>(c, A, lda, B, ldb, lds);
-  mm_store<M, N>(out, ldo, init, alpha, c);
+  for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K, TA, TB, BF, NT>(c, A, lda, B, ldb, lds);
+  mm_store<M, N, NT>(out, ldo, init, alpha, c);
 }
 
 // out = A1 B1 + A2 B2, both products accumulated in registers.
 template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2, bool BF = false,
-          int CAP>
+          int NT = 256, int CAP>
 __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, int lda1,
                                           const float *B1, int ldb1, const float *A2, int lda2,
                                           const float *B2, int ldb2, float (&lds)[CAP]) {
-  f32x4 c[MmTiles<M, N>::TPW];
+  f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
-  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c[q] = zero4();
-  mm_accumulate<M, N, K1, TA1, TB1, BF>(c, A1, lda1, B1, ldb1, lds);
-  mm_accumulate<M, N, K2, TA2, TB2, BF>(c, A2, lda2, B2, ldb2, lds);
-  mm_store<M, N>(out, ldo, nullptr, 1.f, c);
+  for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c[q] = zero4();
+  mm_accumulate<M, N, K1, TA1, TB1, BF, NT>(c, A1, lda1, B1, ldb1, lds);
+  mm_accumulate<M, N, K2, TA2, TB2, BF, NT>(c, A2, lda2, B2, ldb2, lds);
+  mm_store<M, N, NT>(out, ldo, nullptr, 1.f, c);
 }
 
 // out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
 // dimension), staging B once.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
 __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const float *A1,
                                               const float *A2, int lda, const float *B, int ldb,
                                               float (&lds)[CAP]) {
-  f32x4 c1[MmTiles<M, N>::TPW], c2[MmTiles<M, N>::TPW];
+  f32x4 c1[MmTiles<M, N, NT>::TPW], c2[MmTiles<M, N, NT>::TPW];
 #pragma unroll
-  for (int q = 0; q < MmTiles<M, N>::TPW; ++q) c1[q] = c2[q] = zero4();
+  for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c1[q] = c2[q] = zero4();
   f32x4 *const cs[2] = {c1, c2};
   const float *const as[2] = {A1, A2};
-  mm_accumulate_n<M, N, K, TA, TB, 2, BF>(cs, as, lda, B, ldb, lds);
-  mm_store<M, N>(out1, ldo, nullptr, 1.f, c1);
-  mm_store<M, N>(out2, ldo, nullptr, 1.f, c2);
+  mm_accumulate_n<M, N, K, TA, TB, 2, BF, NT>(cs, as, lda, B, ldb, lds);
+  mm_store<M, N, NT>(out1, ldo, nullptr, 1.f, c1);
+  mm_store<M, N, NT>(out2, ldo, nullptr, 1.f, c2);
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
@@ -432,7 +444,7 @@ __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo,
 // TPR consecutive threads share a row, each reading float4s part, part +
 // TPR, ...; a thread's rows are r0, r0 + NT / TPR, ..., all loaded before
 // any of the sums is reduced.  Ends with a barrier.
-template <int R, int L>
+template <int R, int L, int NT = 256>
 __device__ __forceinline__ void row_dots(float *out, const float *X, const float *Y, int ld,
                                          bool acc) {
   constexpr int TPR = L / 4 < 16 ? L / 4 : 16;  // threads per row
@@ -507,10 +519,11 @@ __device__ void seq_chunks(int seq, const int *cu, int seq_len, int C, const int
 
 // ---- 1. per-tile recompute ------------------------------------------------
 template <typename T, int D, int C>
-__global__ __launch_bounds__(NT) void bwd_prep_kernel(
+__global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ d_o, const float *__restrict__ g, const float *__restrict__ beta,
     const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
+  constexpr int NT = bwd_threads<D, C>();
   constexpr int LA = C + 4;
   constexpr int YM = D < 64 ? D : 64;  // row block of dO^T Qt
   constexpr int MM_PAIR = 3 * C * ((D < 32 ? D : 32) + 4);  // Kt, Qt and Kh slices together
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
   __syncthreads();
   // M = Kt Kh^T and Qt Kh^T, staging Kh once
   constexpr bool BF = sizeof(T) == 2;  // bf16 matrix cores where both operands allow
-  block_mm_pair<C, C, D, false, true, BF>(p.mm, p.pm, C, p.kt, p.qt, D, p.kh, D, s_mm);
+  block_mm_pair<C, C, D, false, true, BF, NT>(p.mm, p.pm, C, p.kt, p.qt, D, p.kh, D, s_mm);
   for (int e = tid; e < C * C; e += NT) {
     const int r = e / C, s = e % C;
     if (s > r) p.pm[e] = 0.f;  // P = lower incl. diagonal
@@ -606,16 +619,16 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(
     }
   }
   __syncthreads();
-  block_mm<C, D, C, false, false>(p.w, D, tb, C, p.kt, D, 1.f, false, s_mm);  // W = (T Diag(beta)) Kt
-  block_mm<C, D, C, false, false>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
+  block_mm<C, D, C, false, false, false, NT>(p.w, D, tb, C, p.kt, D, 1.f, false, s_mm);  // W = (T Diag(beta)) Kt
+  block_mm<C, D, C, false, false, false, NT>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
   // the two terms of the state-gradient recursion that do not depend on it,
   // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke.
   // They are stored transposed (X^T = dO^T P, Y^T = dO^T Qt): a chain lane's
   // four rows of one column are then one 16-byte load.
 #pragma unroll
   for (int n0 = 0; n0 < D; n0 += YM) {
-    block_mm<YM, C, C, true, false>(p.px + n0 * C, C, s_do + n0, D, p.pm, C, 1.f, false, s_mm);
-    block_mm<YM, D, C, true, false>(p.qy + n0 * D, D, s_do + n0, D, p.qt, D, 1.f, false, s_mm);
+    block_mm<YM, C, C, true, false, false, NT>(p.px + n0 * C, C, s_do + n0, D, p.pm, C, 1.f, false, s_mm);
+    block_mm<YM, D, C, true, false, false, NT>(p.qy + n0 * D, D, s_do + n0, D, p.qt, D, 1.f, false, s_mm);
   }
   if constexpr (sizeof(T) == 2) {
     // the chains' bf16 copies: W and Ke row-major and, for C >= 32, W^T and
@@ -663,21 +676,21 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <int R, int CO, typename WT>
 struct Stage {
   static constexpr int EV = 16 / (int)sizeof(WT);  // elements per piece
-  static constexpr int NV = R * CO / EV, P = (NV + NT - 1) / NT;
+  static constexpr int NV = R * CO / EV, P = (NV + NTC - 1) / NTC;
   static_assert(CO % EV == 0, "a piece stays within one row");
   u32x4 r[P];
   __device__ __forceinline__ void load(const WT *src) {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int e = threadIdx.x + NT * m;
-      if (NV % NT == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
+      const int e = threadIdx.x + NTC * m;
+      if (NV % NTC == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
     }
   }
   __device__ __forceinline__ void store(float *dst) const {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int e = threadIdx.x + NT * m;
-      if (NV % NT == 0 || e < NV) {
+      const int e = threadIdx.x + NTC * m;
+      if (NV % NTC == 0 || e < NV) {
         float *at = dst + (e / (CO / EV)) * (CO + 4) + EV * (e % (CO / EV));
         if constexpr (EV == 4) {
           *reinterpret_cast<f32x4 *>(at) = __builtin_bit_cast(f32x4, r[m]);
@@ -775,21 +788,21 @@ constexpr size_t dstate_lds_bytes() {
 // 16-byte fragment reads of 8 consecutive rows hit distinct banks).
 template <int R, int CO>
 struct StageB {
-  static constexpr int NV = R * CO / 8, P = (NV + NT - 1) / NT;
+  static constexpr int NV = R * CO / 8, P = (NV + NTC - 1) / NTC;
   static_assert(CO % 8 == 0, "a piece stays within one row");
   u32x4 r[P];
   __device__ __forceinline__ void load(const bf16 *src) {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int e = threadIdx.x + NT * m;
-      if (NV % NT == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
+      const int e = threadIdx.x + NTC * m;
+      if (NV % NTC == 0 || e < NV) r[m] = reinterpret_cast<const u32x4 *>(src)[e];
     }
   }
   __device__ __forceinline__ void store(bf16 *dst) const {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int e = threadIdx.x + NT * m;
-      if (NV % NT == 0 || e < NV)
+      const int e = threadIdx.x + NTC * m;
+      if (NV % NTC == 0 || e < NV)
         *reinterpret_cast<u32x4 *>(dst + (e / (CO / 8)) * (CO + 8) + 8 * (e % (CO / 8))) = r[m];
     }
   }
@@ -1339,7 +1352,7 @@ __device__ __forceinline__ void run_dstate_chain(int b, const int *cu, int N, in
 
 // ---- chain launches ----------------------------------------------------------
 template <int D, int C, typename WT>
-__global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ cu, int N, int H,
+__global__ __launch_bounds__(NTC) void bwd_state_kernel(const int *__restrict__ cu, int N, int H,
                                                        int seq_len, const float *__restrict__ s0,
                                                        BwdLayout L, char *ws) {
   extern __shared__ __align__(16) float sm[];
@@ -1347,7 +1360,7 @@ __global__ __launch_bounds__(NT) void bwd_state_kernel(const int *__restrict__ c
 }
 
 template <int D, int C, typename WT>
-__global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ cu, int N, int H,
+__global__ __launch_bounds__(NTC) void bwd_dstate_kernel(const int *__restrict__ cu, int N, int H,
                                                         int seq_len, const float *__restrict__ dsf,
                                                         float *__restrict__ ds0, BwdLayout L,
                                                         char *ws) {
@@ -1361,7 +1374,7 @@ __global__ __launch_bounds__(NT) void bwd_dstate_kernel(const int *__restrict__ 
 // gradients backward, the others the states forward.  `split` is a multiple
 // of 8, so each part keeps a pair's slices on one XCD.
 template <int D, int C, typename WT>
-__global__ __launch_bounds__(NT) void bwd_chains_kernel(
+__global__ __launch_bounds__(NTC) void bwd_chains_kernel(
     const int *__restrict__ cu, int N, int H, int seq_len, const float *__restrict__ s0,
     const float *__restrict__ dsf, float *__restrict__ ds0, BwdLayout L, char *ws, int split) {
   extern __shared__ __align__(16) float sm[];
@@ -1380,11 +1393,12 @@ __global__ __launch_bounds__(NT) void bwd_chains_kernel(
 // q dQt e^G (= dKt Kt - dKh Kh + dQt Qt - dKe Ke), kept in LDS for the
 // reverse cumulative sum that gives dg.
 template <typename T, int D, int C>
-__global__ __launch_bounds__(NT) void bwd_grad_kernel(
+__global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
     T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
+  constexpr int NT = bwd_threads<D, C>();
   constexpr int MM = cmax(cmax(mm_lds<C, D, D>(), mm_lds<C, C, D>()),
                           cmax(mm_lds<C, D, C>(), mm_lds<C, C, C>()));
   constexpr int CC = C * C, CD = C * D;
@@ -1420,36 +1434,36 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(
         load4_f32<T>(d_o + (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i) * live;
   }
   __syncthreads();
-  block_mm_init<C, D, D, false, false>(unew, D, p.u, -1.f, p.w, D, sc, D, s_mm);  // U - W S
-  row_dots<D, D>(s_dgam, dse, sc, D, false);                   // dgam = rowsum(dS_next * S)
+  block_mm_init<C, D, D, false, false, false, NT>(unew, D, p.u, -1.f, p.w, D, sc, D, s_mm);  // U - W S
+  row_dots<D, D, NT>(s_dgam, dse, sc, D, false);                   // dgam = rowsum(dS_next * S)
   constexpr bool BF = sizeof(T) == 2;  // bf16 matrix cores where both operands allow
-  block_mm<C, C, D, false, true, BF>(s_dp, C, dot, D, unew, D, 1.f, false, s_mm);  // dO Unew^T
+  block_mm<C, C, D, false, true, BF, NT>(s_dp, C, dot, D, unew, D, 1.f, false, s_mm);  // dO Unew^T
   for (int e = tid; e < CC; e += NT)
     if (e % C > e / C) s_dp[e] = 0.f;  // dP: lower incl. diagonal
   __syncthreads();
   // dQt = dO S^T + dP Kh
-  block_mm2<C, D, D, false, true, C, false, false, BF>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D,
+  block_mm2<C, D, D, false, true, C, false, false, BF, NT>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D,
                                                        s_mm);
-  block_mm<C, D, D, false, true, BF>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
-  block_mm<C, D, D, false, true, BF>(dw, D, dun, D, sc, D, -1.f, false, s_mm);  // -dUnew S^T
+  block_mm<C, D, D, false, true, BF, NT>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
+  block_mm<C, D, D, false, true, BF, NT>(dw, D, dun, D, sc, D, -1.f, false, s_mm);  // -dUnew S^T
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
-  block_mm2<C, C, D, false, true, D, false, true, BF>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D,
+  block_mm2<C, C, D, false, true, D, false, true, BF, NT>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D,
                                                       s_mm);
   for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e % C];
   __syncthreads();
-  block_mm<C, D, C, true, false>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);   // T^T dW
-  block_mm<C, D, C, true, false>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);   // T^T dUnew
-  block_mm<C, C, C, true, false>(s_xm, C, p.tm, C, s_dt, C, 1.f, false, s_mm);  // T^T dT
-  block_mm<C, C, C, false, true, BF>(s_dt, C, s_xm, C, p.tm, C, -1.f, false, s_mm);  // dA (pre-mask)
+  block_mm<C, D, C, true, false, false, NT>(dbkt, D, p.tm, C, dw, D, 1.f, false, s_mm);   // T^T dW
+  block_mm<C, D, C, true, false, false, NT>(dbv, D, p.tm, C, dun, D, 1.f, false, s_mm);   // T^T dUnew
+  block_mm<C, C, C, true, false, false, NT>(s_xm, C, p.tm, C, s_dt, C, 1.f, false, s_mm);  // T^T dT
+  block_mm<C, C, C, false, true, BF, NT>(s_dt, C, s_xm, C, p.tm, C, -1.f, false, s_mm);  // dA (pre-mask)
   for (int e = tid; e < CC; e += NT)
     if (e % C >= e / C) s_dt[e] = 0.f;  // dA strictly lower
   __syncthreads();
-  row_dots<C, C>(s_dbr, s_dt, p.mm, C, false);  // rowsum(dA * M), before dA becomes dM
+  row_dots<C, C, NT>(s_dbr, s_dt, p.mm, C, false);  // rowsum(dA * M), before dA becomes dM
   for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e / C];  // dM = Diag(beta) dA
   __syncthreads();
   // dKt (without Diag(beta) dBKt) = dM Kh; dKh = dM^T Kt + dP^T Qt
-  block_mm<C, D, C, false, false>(dkt, D, s_dt, C, p.kh, D, 1.f, false, s_mm);
-  block_mm2<C, D, C, true, false, C, true, false>(dkh, D, s_dt, C, p.kt, D, s_dp, C, p.qt, D,
+  block_mm<C, D, C, false, false, false, NT>(dkt, D, s_dt, C, p.kh, D, 1.f, false, s_mm);
+  block_mm2<C, D, C, true, false, C, true, false, false, NT>(dkh, D, s_dt, C, p.kt, D, s_dp, C, p.qt, D,
                                                   s_mm);
   // last pass: dq, dk, dv, dbeta, dG (LDS) and colsum(dKe Ke) (LDS)
   for (int i = tid; i < D; i += NT) s_cs[i] = 0.f;
@@ -1520,23 +1534,23 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
     e = raise_lds_limit((const void *)bwd_chains_kernel<D, C, T>, (int)lds_chains, raised3);
   if (e != hipSuccess) return e;
   if (tiles > 0)
-    hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k, v,
+    hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(bwd_threads<D, C>()), 0, a.stream, q, k, v,
                        d_o, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
                        a.lay, a.ws);
   const int cus = device_cus();
   if (cus > 0 && 2 * slices <= (unsigned)cus) {
-    hipLaunchKernelGGL((bwd_chains_kernel<D, C, T>), dim3(2 * slices), dim3(NT), lds_chains,
+    hipLaunchKernelGGL((bwd_chains_kernel<D, C, T>), dim3(2 * slices), dim3(NTC), lds_chains,
                        a.stream, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.dsf,
                        a.ds0, a.lay, a.ws, (int)slices);
   } else {
-    hipLaunchKernelGGL((bwd_state_kernel<D, C, T>), dim3(slices), dim3(NT), lds_state, a.stream,
+    hipLaunchKernelGGL((bwd_state_kernel<D, C, T>), dim3(slices), dim3(NTC), lds_state, a.stream,
                        a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.s0, a.lay, a.ws);
-    hipLaunchKernelGGL((bwd_dstate_kernel<D, C, T>), dim3(slices), dim3(NT), lds_dstate, a.stream,
+    hipLaunchKernelGGL((bwd_dstate_kernel<D, C, T>), dim3(slices), dim3(NTC), lds_dstate, a.stream,
                        a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len, a.dsf, a.ds0, a.lay,
                        a.ws);
   }
   if (tiles > 0)
-    hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(NT), 0, a.stream, q, k,
+    hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(bwd_threads<D, C>()), 0, a.stream, q, k,
                        v, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
                        reinterpret_cast<T *>(a.dq), reinterpret_cast<T *>(a.dk),
                        reinterpret_cast<T *>(a.dv), a.dg, a.dbeta, a.lay, a.ws);
