@@ -307,7 +307,8 @@ def time_backward(torch, kda, w, steps, warmup, d, E):
                 roofline_frac=tf / FP32_MFMA_PEAK_TFLOPS,
                 roofline=dict(bound="mfma", achieved=tf, peak=FP32_MFMA_PEAK_TFLOPS,
                               unit="TFLOP/s", frac=tf / FP32_MFMA_PEAK_TFLOPS, traffic=None,
-                              kernel="kda_bwd_chunked (4 kernels, fp32 matrix cores)",
+                              kernel="kda_bwd_chunked (3 or 4 kernels, fp32 and bf16 matrix cores; "
+                                     "priced at the fp32 peak)",
                               flops_per_launch=flops, avg_launch_us=ms * 1e3))
 
 
