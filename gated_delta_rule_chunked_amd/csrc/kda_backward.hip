@@ -1469,6 +1469,8 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   for (int i = tid; i < D; i += NT) s_cs[i] = 0.f;
   __syncthreads();
   constexpr int RT = D / 4;  // threads per row
+  static_assert(NT % RT == 0, "a thread keeps the same four channels on every row");
+  f32x4 cs = zero4();  // this thread's share of colsum(dKe Ke)
   for (int e4 = tid; e4 < CD / 4; e4 += NT) {
     const int r = e4 / RT, i = 4 * (e4 % RT), e = 4 * e4;
     const bool live = r < n;
@@ -1495,7 +1497,7 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
       ok[u] = tk + th + te;
       dG[u] = kv[u] * (tk - th - te) + qv[u] * oq[u];
       rowp += vbk[u] * kv[u] * eg + vbv[u] * vv[u];  // (dBKt * Kt) + (dBV * V)
-      atomicAdd(s_cs + i + u, te * kv[u]);           // dKe * Ke, summed over rows
+      cs[u] += te * kv[u];                           // dKe * Ke, summed over rows
     }
     rowp = group_sum<RT>(rowp);
     if (live) {
@@ -1505,6 +1507,10 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
       *reinterpret_cast<f32x4 *>(s_dG + e) = dG;
       if (e4 % RT == 0) dbeta[(int64_t)(t0 + r) * H + h] = s_dbr[r] + rowp;
     }
+  }
+  if (tid < CD / 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) atomicAdd(s_cs + 4 * (tid % RT) + u, cs[u]);
   }
   __syncthreads();
   // dg: reverse cumulative sum of dG over the chunk plus dG_n, per channel
