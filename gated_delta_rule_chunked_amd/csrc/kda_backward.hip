@@ -1402,9 +1402,12 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   constexpr int MM = cmax(cmax(mm_lds<C, D, D>(), mm_lds<C, C, D>()),
                           cmax(mm_lds<C, D, C>(), mm_lds<C, C, C>()));
   constexpr int CC = C * C, CD = C * D;
-  // dG [C][D] and colsum(dKe Ke) [D] reuse the staging and dP / dM space
-  // once the last product is done; T^T dT's space then holds rowsum(dA M)
-  static_assert(CD + D <= MM + 2 * CC, "LDS reuse at the end");
+  // dG [C][D] and the per-row-group partials of colsum(dKe Ke) [CSR][D]
+  // reuse the staging and dP / dM space once the last product is done;
+  // T^T dT's space then holds rowsum(dA M)
+  constexpr int RT = D / 4;                                 // threads per row (last pass)
+  constexpr int CSR = (NT < CD / 4 ? NT : CD / 4) / RT;     // row groups of the last pass
+  static_assert(CD + CSR * D <= MM + 2 * CC, "LDS reuse at the end");
   __shared__ int s_loc[4];
   __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_big[MM + 3 * CC];
@@ -1465,10 +1468,9 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   block_mm<C, D, C, false, false, false, NT>(dkt, D, s_dt, C, p.kh, D, 1.f, false, s_mm);
   block_mm2<C, D, C, true, false, C, true, false, false, NT>(dkh, D, s_dt, C, p.kt, D, s_dp, C, p.qt, D,
                                                   s_mm);
-  // last pass: dq, dk, dv, dbeta, dG (LDS) and colsum(dKe Ke) (LDS)
-  for (int i = tid; i < D; i += NT) s_cs[i] = 0.f;
-  __syncthreads();
-  constexpr int RT = D / 4;  // threads per row
+  // last pass: dq, dk, dv, dbeta, dG (LDS) and colsum(dKe Ke): each thread
+  // sums its channels over its rows, the row groups' partials meet in LDS and
+  // are added in a fixed order, so dg is the same bits on every run
   static_assert(NT % RT == 0, "a thread keeps the same four channels on every row");
   f32x4 cs = zero4();  // this thread's share of colsum(dKe Ke)
   for (int e4 = tid; e4 < CD / 4; e4 += NT) {
@@ -1508,14 +1510,14 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
       if (e4 % RT == 0) dbeta[(int64_t)(t0 + r) * H + h] = s_dbr[r] + rowp;
     }
   }
-  if (tid < CD / 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) atomicAdd(s_cs + 4 * (tid % RT) + u, cs[u]);
-  }
+  if (tid < CD / 4)
+    *reinterpret_cast<f32x4 *>(s_cs + (tid / RT) * D + 4 * (tid % RT)) = cs;
   __syncthreads();
   // dg: reverse cumulative sum of dG over the chunk plus dG_n, per channel
   for (int i = tid; i < D; i += NT) {
-    float run = s_dgam[i] * p.gam[i] + s_cs[i];
+    float csum = 0.f;
+    for (int g = 0; g < CSR; ++g) csum += s_cs[g * D + i];
+    float run = s_dgam[i] * p.gam[i] + csum;
     for (int r = n - 1; r >= 0; --r) {
       run += s_dG[r * D + i];
       dg[(int64_t)(t0 + r) * rs + (int64_t)h * D + i] = run;

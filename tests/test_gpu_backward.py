@@ -130,3 +130,24 @@ def test_backward_headline_size_sampled_pairs():
               flush=True)
         for key, e in errs.items():
             assert e <= TOL[w.dtype], f"pair ({seq}, {h}) {key} error {e:.3e}"
+
+
+@pytest.mark.parametrize("case", ["headline", "ragged"])
+def test_backward_deterministic(case):
+    """No atomics on any accumulation: two runs on the same inputs give the
+    same bits for every gradient, at the headline size (B=2, H=8, T=2048,
+    d=128, C=64, with a final-state gradient) and on ragged packed sequences
+    with initial states (d=64, C=32)."""
+    print(f"[backward] bitwise run-to-run, {case}", flush=True)
+    if case == "headline":
+        w = kin.workload(1)
+        d, chunk = 128, 64
+    else:
+        w = kin.make_prefill(611, H=3, d=64, dtype=kin.BF16, chunk_size=32,
+                             lengths=[95, 0, 1, 130, 33], s0_std=0.05)
+        d, chunk = 64, 32
+    do, dsf = kin.backward_inputs(612, w.total_tokens, w.num_heads, d, w.num_seqs, w.dtype)
+    a = _run(w, do, dsf, chunk)
+    b = _run(w, do, dsf, chunk)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "ds0"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
