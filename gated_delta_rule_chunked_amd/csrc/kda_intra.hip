@@ -241,8 +241,9 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
     const f32x4 etot = {__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
     if (rg == 0) {
       *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
-      // precondition of the chunk-start reference: summed log-decay > -80
-      if (in.flags && (tot[0] <= -80.f || tot[1] <= -80.f || tot[2] <= -80.f || tot[3] <= -80.f))
+      // precondition of the chunk-start reference: summed log-decay >= -80
+      // (e^80 is finite in fp32 and bf16)
+      if (in.flags && (tot[0] < -80.f || tot[1] < -80.f || tot[2] < -80.f || tot[3] < -80.f))
         atomicOr(in.flags, KDA_FLAG_DECAY_RANGE);
     }
     // e^-G = 1 / e^G and e^(G_n - G) = e^G_n / e^G: in range for G > -80

@@ -105,3 +105,28 @@ def test_check_inputs_rejects_bad_offsets_and_computes_nothing(cu):
     torch.cuda.synchronize()
     assert int(f.item()) & kda.FLAG_BAD_CU_SEQLENS
     assert bool(torch.all(o == 7.0)) and bool(torch.all(fs == 3.0))
+
+
+def test_bounded_gate_at_its_limit_keeps_the_flag_clear():
+    """K3's bounded gate g = g_min sigmoid(z) with g_min = -5 and z = 30:
+    sigmoid rounds to 1 in fp32, so every token decays by exactly -5 and a
+    16-token chunk sums to exactly -80, the bound itself (e^80 is finite in
+    fp32 and bf16).  The flag stays clear and the outputs match the oracle."""
+    print("[diagnostics] sigmoid gate at g_min = -5, z = 30, C = 16", flush=True)
+    kda = _kda()
+    T, H, d = 96, 2, 64
+    w = kin.make_prefill(904, B=1, T=T, H=H, d=d, dtype=kin.BF16, chunk_size=16)
+    dd = upload_prefill(w)
+    z = torch.full((T, H, d), 30.0, dtype=torch.bfloat16, device="cuda")
+    f = _flags()
+    o, s = kda.fwd_chunked(dd["q"], dd["k"], dd["v"], z, dd["beta"], chunk_size=16,
+                           gate="sigmoid", gate_min=-5.0, flags=f)
+    torch.cuda.synchronize()
+    assert int(f.item()) == 0, int(f.item())
+    q, k, v, _, b, _ = w.f64()
+    q, k, g, b = oracle.prepare_inputs(q, k, np.full((T, H, d), 30.0), b, gate="sigmoid",
+                                       gate_min=-5.0)
+    ro, rs = oracle.recurrent(q, k, v, g, b)
+    eo, es = relerr(from_device(o), ro), relerr(from_device(s), rs)
+    print(f"  relerr o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
