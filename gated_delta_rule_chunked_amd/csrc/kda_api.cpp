@@ -90,6 +90,7 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
     case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
     case KDA_ERROR_LAUNCH_FAILED: return "KDA_ERROR_LAUNCH_FAILED";
+    case KDA_ERROR_SCRATCH_TOO_SMALL: return "KDA_ERROR_SCRATCH_TOO_SMALL";
   }
   return "KDA_UNKNOWN_STATUS";
 }

@@ -74,6 +74,9 @@ def library():
     lib.kda_bwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32,
                                     ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     sz, vp]
+    lib.kda_fwd_chunked_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32,
+                                            i32, ctypes.c_int, vp, vp, vp, vp]
     pin = ctypes.POINTER(KdaOptions)
     lib.kda_fwd_chunked_ex.restype = ctypes.c_int
     lib.kda_fwd_chunked_ex.argtypes = [pin, ctypes.c_uint32] + lib.kda_fwd_chunked.argtypes
@@ -292,6 +295,46 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     else:
         _check(library().kda_fwd_chunked_stage(STAGES[stage], *args),
                f"kda_fwd_chunked_stage({stage})")
+    return o, fs
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDA_NOALLOC_SCRATCH_BYTES (include/kda.h)
+
+
+def fwd_chunked_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        log_alpha: torch.Tensor, beta: torch.Tensor,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        num_seqs: Optional[int] = None,
+                        initial_state: Optional[torch.Tensor] = None,
+                        chunk_size: int = 64, out: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_fwd_chunked_noalloc: the prefill of fwd_chunked with the
+    workspace taken from the library's per-GPU device array (no workspace
+    argument, no allocation by the library).  Pass `out` and `final_state`
+    to allocate nothing here either.  Calls that overlap on one GPU race."""
+    T, H, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, (T, H, d))
+    _need(log_alpha, "log_alpha", torch.float32, (T, H, d))
+    _need(beta, "beta", torch.float32, (T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n = cu_seqlens.numel() - 1
+    else:
+        n = 1 if num_seqs is None else int(num_seqs)
+    dev = q.device
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, d, d))
+    o = out if out is not None else torch.empty((T, H, d), dtype=v.dtype, device=dev)
+    _need(o, "out", v.dtype, (T, H, d))
+    fs = final_state if final_state is not None else torch.empty(
+        (n, H, d, d), dtype=torch.float32, device=dev)
+    _need(fs, "final_state", torch.float32, (n, H, d, d))
+    _check(library().kda_fwd_chunked_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(cu_seqlens), n, T, H, d,
+        d, chunk_size, _dtype_code(q.dtype), _ptr(initial_state), _ptr(fs), _ptr(o),
+        _stream(dev)), "kda_fwd_chunked_noalloc")
     return o, fs
 
 

@@ -56,7 +56,9 @@ typedef enum {
   KDA_SUCCESS = 0,
   KDA_ERROR_INVALID_VALUE = 1, /* null/misaligned pointer, bad size, small workspace */
   KDA_ERROR_NOT_SUPPORTED = 2, /* valid request the library has no kernel for */
-  KDA_ERROR_LAUNCH_FAILED = 3  /* the HIP runtime refused a kernel launch */
+  KDA_ERROR_LAUNCH_FAILED = 3, /* the HIP runtime refused a kernel launch */
+  KDA_ERROR_SCRATCH_TOO_SMALL = 4 /* kda_fwd_chunked_noalloc: the call needs more
+                                     workspace than KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
@@ -294,6 +296,40 @@ kda_status kda_decode_step_ex(const kda_options *options, const void *q, const v
                               const void *v, const void *gate, const float *beta,
                               float *state, void *o, int32_t batch, int32_t num_heads,
                               int32_t d_k, int32_t d_v, kda_dtype dtype, void *stream);
+
+/*
+ * ---- Prefill without any allocation -------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * kda_fwd_chunked_noalloc is kda_fwd_chunked (same arguments and kernels,
+ * same results bit for bit) with the workspace taken from a device array
+ * that the library holds on every GPU it runs on, until the process ends:
+ * KDA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  It allocates nothing and calls
+ * no allocating routine.  The first call on a device, with that device
+ * current, looks up the array's device address (hipGetSymbolAddress); the
+ * stream must belong to the current device.
+ *
+ *   Returns KDA_ERROR_SCRATCH_TOO_SMALL, with nothing enqueued, when
+ *   kda_fwd_chunked_workspace_size() for the arguments exceeds
+ *   KDA_NOALLOC_SCRATCH_BYTES (bf16, d = 128, C = 64 needs about 72.5 KiB
+ *   per (chunk, head) tile: e.g. B=2 x T=2048 x H=8 takes 36.8 MiB), and
+ *   KDA_ERROR_LAUNCH_FAILED if the array's address cannot be found.  Other
+ *   errors are kda_fwd_chunked's.
+ *   Calls on one GPU share its array: calls that overlap on one GPU (several
+ *   streams or host threads at once) race and must be serialised by the
+ *   caller.  Each call writes every workspace byte it reads, so nothing
+ *   left by an earlier call is used.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+kda_status kda_fwd_chunked_noalloc(const void *q, const void *k, const void *v,
+                                   const float *log_alpha, const float *beta,
+                                   const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                   int32_t d_v, int32_t chunk_size, kda_dtype dtype,
+                                   const float *initial_state, float *final_state, void *o,
+                                   void *stream);
 
 /*
  * ---- Backward (training) ----------------------------------------------------

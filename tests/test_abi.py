@@ -44,6 +44,7 @@ def test_status_strings(lib):
     assert lib.kda_status_string(1) == b"KDA_ERROR_INVALID_VALUE"
     assert lib.kda_status_string(2) == b"KDA_ERROR_NOT_SUPPORTED"
     assert lib.kda_status_string(3) == b"KDA_ERROR_LAUNCH_FAILED"
+    assert lib.kda_status_string(4) == b"KDA_ERROR_SCRATCH_TOO_SMALL"
     assert lib.kda_status_string(77) == b"KDA_UNKNOWN_STATUS"
     assert lib.kda_version() >= 100
 
@@ -225,3 +226,21 @@ def test_bwd_rejects_bad_arguments_on_host(lib):
     assert bwd(T=255) == 1
     assert lib.kda_bwd_chunked_workspace_size(4096, 2, 8, 128, 128, 64, 1) > 0
     assert lib.kda_bwd_chunked_workspace_size(4096, 2, 8, 96, 96, 64, 1) == 0
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_on_the_host(lib):
+    """kda_fwd_chunked_noalloc refuses, before any HIP call, a prefill whose
+    workspace exceeds KDA_NOALLOC_SCRATCH_BYTES (here B=1 x T=32768 x H=32,
+    1.16 GiB), and returns the size errors of kda_fwd_chunked for invalid
+    or unsupported sizes.  Device pointers are never dereferenced on the
+    host, so aligned dummy addresses stand in for them."""
+    p = [ctypes.c_void_p(0x100000 + 0x1000 * i) for i in range(8)]
+    f = lib.kda_fwd_chunked_noalloc
+    big = lib.kda_fwd_chunked_workspace_size(32768, 1, 32, 128, 128, 64, 1)
+    assert big > 64 << 20
+    assert f(p[0], p[1], p[2], p[3], p[4], None, 1, 32768, 32, 128, 128, 64, 1, None, p[5],
+             p[6], None) == 4
+    assert f(p[0], p[1], p[2], p[3], p[4], None, 1, 4096, 8, 96, 96, 64, 1, None, p[5], p[6],
+             None) == 2  # unsupported head size
+    assert f(p[0], p[1], p[2], p[3], p[4], None, 0, 4096, 8, 128, 128, 64, 1, None, p[5], p[6],
+             None) == 1  # no sequences
