@@ -150,6 +150,9 @@ kda_status fwd_run(unsigned mask, const kda_options *options, const void *q, con
   a.beta = beta;
   a.in = in;
   a.cu_seqlens = cu_seqlens;
+  a.chunk_tab = cu_seqlens ? reinterpret_cast<const int4 *>(reinterpret_cast<char *>(workspace) +
+                                                            lay.chunk_tab)
+                           : nullptr;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.d = d_k;
@@ -169,6 +172,12 @@ kda_status fwd_run(unsigned mask, const kda_options *options, const void *q, con
 
   if (in.check && cu_seqlens &&
       launch_check_cu(cu_seqlens, num_seqs, total_tokens, in.flags, a.stream) != hipSuccess)
+    return KDA_ERROR_LAUNCH_FAILED;
+  if ((mask & 1u) && cu_seqlens &&
+      launch_chunk_table(cu_seqlens, num_seqs, total_tokens, chunk_size, lay.max_chunks,
+                         reinterpret_cast<int4 *>(a.ws + lay.chunk_tab),
+                         reinterpret_cast<int *>(a.ws + lay.seq_first), in,
+                         a.stream) != hipSuccess)
     return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 1u) && launch_intra(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   if ((mask & 2u) && launch_inter(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
@@ -269,6 +278,9 @@ kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
   a.s0 = initial_state;
   a.dsf = d_final_state;
   a.cu_seqlens = cu_seqlens;
+  a.chunk_tab = cu_seqlens ? reinterpret_cast<const int4 *>(reinterpret_cast<char *>(workspace) +
+                                                            lay.chunk_tab)
+                           : nullptr;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.d = d_k;
@@ -285,6 +297,12 @@ kda_status kda_bwd_chunked(const void *q, const void *k, const void *v,
   a.ws = reinterpret_cast<char *>(workspace);
   a.lay = lay;
   a.stream = reinterpret_cast<hipStream_t>(stream);
+  if (cu_seqlens &&
+      launch_chunk_table(cu_seqlens, num_seqs, total_tokens, chunk_size, lay.max_chunks,
+                         reinterpret_cast<int4 *>(a.ws + lay.chunk_tab),
+                         reinterpret_cast<int *>(a.ws + lay.seq_first), OptArgs(),
+                         a.stream) != hipSuccess)
+    return KDA_ERROR_LAUNCH_FAILED;
   if (launch_bwd(a, dtype) != hipSuccess) return KDA_ERROR_LAUNCH_FAILED;
   return KDA_SUCCESS;
 }

@@ -522,22 +522,19 @@ template <typename T, int D, int C>
 __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ d_o, const float *__restrict__ g, const float *__restrict__ beta,
-    const int *__restrict__ cu, int N, int H, int seq_len, BwdLayout L, char *ws) {
+    const int4 *__restrict__ tab, int N, int H, int seq_len, BwdLayout L, char *ws) {
   constexpr int NT = bwd_threads<D, C>();
   constexpr int LA = C + 4;
   constexpr int YM = D < 64 ? D : 64;  // row block of dO^T Qt
   constexpr int MM_PAIR = 3 * C * ((D < 32 ? D : 32) + 4);  // Kt, Qt and Kh slices together
   constexpr int MM = cmax(cmax(MM_PAIR, mm_lds<C, D, C>()),
                           cmax(mm_lds<YM, C, C>(), mm_lds<YM, D, C>()));
-  __shared__ int s_loc[4];
-  __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_mm[MM];
   __shared__ __align__(16) float s_a[C * LA];  // A = strict_lower(beta M), for the substitution
   __shared__ __align__(16) float s_do[C * D];  // dO, zero past the chunk's end
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
-  int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
-  locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
-  const int t0 = s_loc[1], n = s_loc[2];
+  const ChunkLoc loc = chunk_loc(c, tab, N, seq_len, C);
+  const int t0 = loc.t0, n = loc.n;
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
@@ -1395,7 +1392,7 @@ __global__ __launch_bounds__(NTC) void bwd_chains_kernel(
 template <typename T, int D, int C>
 __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const T *__restrict__ d_o, const int *__restrict__ cu, int N, int H, int seq_len,
+    const T *__restrict__ d_o, const int4 *__restrict__ tab, int N, int H, int seq_len,
     T *__restrict__ dq, T *__restrict__ dk, T *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta, BwdLayout L, char *ws) {
   constexpr int NT = bwd_threads<D, C>();
@@ -1408,17 +1405,14 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   constexpr int RT = D / 4;                                 // threads per row (last pass)
   constexpr int CSR = (NT < CD / 4 ? NT : CD / 4) / RT;     // row groups of the last pass
   static_assert(CD + CSR * D <= MM + 2 * CC, "LDS reuse at the end");
-  __shared__ int s_loc[4];
-  __shared__ int s_scan[NT];
   __shared__ __align__(16) float s_big[MM + 3 * CC];
   __shared__ float s_dgam[D];
   float(&s_mm)[MM] = *reinterpret_cast<float(*)[MM]>(s_big);  // product staging
   float *s_dp = s_big + MM, *s_dt = s_dp + CC, *s_xm = s_dt + CC;
   float *s_dG = s_big, *s_cs = s_big + CD, *s_dbr = s_xm;
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
-  int *seq_first = reinterpret_cast<int *>(ws + L.seq_first);
-  locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
-  const int t0 = s_loc[1], n = s_loc[2];
+  const ChunkLoc loc = chunk_loc(c, tab, N, seq_len, C);
+  const int t0 = loc.t0, n = loc.n;
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
@@ -1543,7 +1537,7 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   if (e != hipSuccess) return e;
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_prep_kernel<T, D, C>), dim3(tiles), dim3(bwd_threads<D, C>()), 0, a.stream, q, k, v,
-                       d_o, a.g, a.beta, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
+                       d_o, a.g, a.beta, a.chunk_tab, a.num_seqs, a.num_heads, a.seq_len,
                        a.lay, a.ws);
   const int cus = device_cus();
   if (cus > 0 && 2 * slices <= (unsigned)cus) {
@@ -1559,7 +1553,7 @@ static hipError_t launch_bwd_dc(const BwdArgs &a) {
   }
   if (tiles > 0)
     hipLaunchKernelGGL((bwd_grad_kernel<T, D, C>), dim3(tiles), dim3(bwd_threads<D, C>()), 0, a.stream, q, k,
-                       v, d_o, a.cu_seqlens, a.num_seqs, a.num_heads, a.seq_len,
+                       v, d_o, a.chunk_tab, a.num_seqs, a.num_heads, a.seq_len,
                        reinterpret_cast<T *>(a.dq), reinterpret_cast<T *>(a.dk),
                        reinterpret_cast<T *>(a.dv), a.dg, a.dbeta, a.lay, a.ws);
   return hipGetLastError();

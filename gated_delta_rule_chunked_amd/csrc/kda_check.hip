@@ -1,4 +1,5 @@
-// kda_check.hip -- on-device validation of cu_seqlens for the prefill.
+// kda_check.hip -- on-device handling of cu_seqlens: its validation for the
+// prefill, and the chunk table of packed sequences.
 //
 // The sequence offsets are device data, so the host cannot check them
 // without a synchronisation.  With kda_options.check_inputs this kernel runs
@@ -18,6 +19,61 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int *__restrict__ c
   for (int s = threadIdx.x; s < N; s += blockDim.x) bad |= cu[s + 1] < cu[s];
   if (threadIdx.x == 0) bad |= cu[0] != 0 || (int64_t)cu[N] != total;
   if (__syncthreads_or(bad) && threadIdx.x == 0) atomicOr(flags, KDA_FLAG_BAD_CU_SEQLENS);
+}
+
+// The chunk table of packed sequences: chunk id -> (sequence, first token,
+// rows), ids enumerating the chunks of sequence 0, then 1, ... (chunks never
+// straddle sequences; a sequence's last chunk holds the tail).  One
+// workgroup walks the sequences 1,024 at a time: chunk counts, a block scan
+// for the first id of each sequence, then each thread writes its sequence's
+// entries.  Entries past the last chunk get rows = 0, so the tiles launched
+// for the bound max_chunks that no chunk fills have nothing to do.  Lengths
+// that break the rules (negative, or a range outside [0, total)) count as
+// empty and ids at or past max_chunks are not written.
+constexpr int kTabThreads = 1024;
+
+__global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(
+    const int *__restrict__ cu, int N, int64_t total, int C, int64_t max_chunks,
+    int4 *__restrict__ tab, int *__restrict__ seq_first, const OptArgs in) {
+  if (inputs_rejected(in)) return;
+  __shared__ long long s_scan[kTabThreads];
+  const int tid = threadIdx.x;
+  long long base = 0;
+  for (int s0 = 0; s0 < N; s0 += kTabThreads) {
+    const int s = s0 + tid;
+    int start = 0, len = 0;
+    if (s < N) {
+      start = cu[s];
+      len = cu[s + 1] - start;
+      if (start < 0 || len < 0 || (int64_t)start + len > total) len = 0;
+    }
+    const long long nc = (len + C - 1) / C;
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < kTabThreads; off <<= 1) {
+      const long long add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const long long first = base + s_scan[tid] - nc;
+    if (s < N) {
+      seq_first[s] = (int)(first < max_chunks ? first : max_chunks);
+      for (long long i = 0; i < nc && first + i < max_chunks; ++i)
+        tab[first + i] = make_int4(s, start + (int)i * C, min(C, len - (int)i * C), 0);
+    }
+    base += s_scan[kTabThreads - 1];
+    __syncthreads();
+  }
+  for (long long c = base + tid; c < max_chunks; c += kTabThreads) tab[c] = make_int4(N, 0, 0, 0);
+}
+
+hipError_t launch_chunk_table(const int *cu, int N, int64_t total, int C, int64_t max_chunks,
+                              int4 *tab, int *seq_first, const OptArgs &in, hipStream_t stream) {
+  if (max_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(kTabThreads), 0, stream, cu, N, total, C,
+                     max_chunks, tab, seq_first, in);
+  return hipGetLastError();
 }
 
 hipError_t launch_check_cu(const int *cu, int N, int64_t total, int *flags,

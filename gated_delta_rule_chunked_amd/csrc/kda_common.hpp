@@ -283,61 +283,33 @@ __device__ __forceinline__ float l2_inv_norm(f32x4 x) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// ---- chunk location (prefill kernels) -----------------------------------
-// Locates chunk id `c` among the sequences: s_loc = (sequence, first token,
-// rows), rows = 0 when c lies past the last chunk.  The workgroup of head 0
-// that owns the first chunk of a sequence records it in seq_first.
-__device__ inline void locate_chunk(int c, int h, const int *cu, int N, int seq_len, int C,
-                             int *s_loc, int *s_scan, int *seq_first) {
-  const int tid = threadIdx.x;
-  if (cu == nullptr) {
-    if (tid == 0) {
-      const int per = (seq_len + C - 1) / C;
-      const int s = c / per, i = c % per;
-      s_loc[0] = s;
-      s_loc[1] = s * seq_len + i * C;
-      s_loc[2] = (s < N) ? min(C, seq_len - i * C) : 0;
-      if (h == 0 && i == 0 && s < N) seq_first[s] = c;
-    }
-    __syncthreads();
-    return;
+// ---- chunk location -------------------------------------------------------
+// Sequence, first token and rows of chunk id c (rows = 0 past the last
+// chunk).  Packed sequences read the chunk table built once per call
+// (chunk_table_kernel); equal-length sequences compute it.  c is uniform
+// over the workgroup, so the results are moved to scalar registers.
+struct ChunkLoc {
+  int seq, t0, n;
+};
+__device__ __forceinline__ ChunkLoc chunk_loc(int c, const int4 *tab, int N, int seq_len,
+                                              int C) {
+  ChunkLoc l;
+  if (tab != nullptr) {
+    const int4 e = tab[c];
+    l.seq = e.x;
+    l.t0 = e.y;
+    l.n = e.z;
+  } else {
+    const int per = max((seq_len + C - 1) / C, 1);
+    l.seq = c / per;
+    const int i = c - l.seq * per;
+    l.t0 = l.seq * seq_len + i * C;
+    l.n = l.seq < N ? min(C, seq_len - i * C) : 0;
   }
-  if (tid == 0) { s_loc[0] = 0; s_loc[1] = 0; s_loc[2] = 0; s_loc[3] = 0; }
-  int base = 0;
-  for (int s0 = 0; s0 < N; s0 += blockDim.x) {
-    const int s = s0 + tid;
-    int len = 0, start = 0;
-    if (s < N) {
-      start = cu[s];
-      len = cu[s + 1] - start;
-    }
-    const int nc = (len + C - 1) / C;
-    __syncthreads();
-    s_scan[tid] = nc;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-      const int add = (tid >= off) ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
-    }
-    const int incl = base + s_scan[tid];
-    const int excl = incl - nc;
-    if (s < N && nc > 0) {
-      if (c >= excl && c < incl) {
-        const int i = c - excl;
-        s_loc[0] = s;
-        s_loc[1] = start + i * C;
-        s_loc[2] = min(C, len - i * C);
-        s_loc[3] = 1;
-      }
-      if (h == 0 && c == excl) seq_first[s] = c;
-    }
-    base += s_scan[blockDim.x - 1];
-    __syncthreads();
-    if (s_loc[3]) break;
-  }
-  __syncthreads();
+  l.seq = __builtin_amdgcn_readfirstlane(l.seq);
+  l.t0 = __builtin_amdgcn_readfirstlane(l.t0);
+  l.n = __builtin_amdgcn_readfirstlane(l.n);
+  return l;
 }
 
 }  // namespace kda

@@ -14,7 +14,10 @@ namespace kda {
 // Prefill workspace layout.  Per-chunk products are stored per (chunk, head)
 // tile, tile index = chunk * H + head, so that every tile is one contiguous
 // block; chunk ids enumerate the chunks of sequence 0, then sequence 1, ...
-//   seq_first   int  [num_seqs]      first chunk id of each non-empty sequence
+//   seq_first   int  [num_seqs]      first chunk id of each sequence
+//   chunk_tab   int4 [max_chunks]    (sequence, first token, rows, 0) per chunk
+//                                    id, rows = 0 past the last chunk (packed
+//                                    sequences; built once per call)
 //   qt          elem [tiles][C][D]   Q * exp(G)
 //   w           elem [tiles][C][D]   WY factor W = T Diag(beta) (K * exp(G))
 //   ut          elem [tiles][D][C]   WY factor U = T Diag(beta) V, transposed
@@ -31,7 +34,8 @@ namespace kda {
 struct FwdLayout {
   int64_t max_chunks = 0;
   int64_t tiles = 0;
-  size_t seq_first = 0, qt = 0, w = 0, ut = 0, ket = 0, p = 0, gam = 0, total = 0;
+  size_t seq_first = 0, chunk_tab = 0, qt = 0, w = 0, ut = 0, ket = 0, p = 0, gam = 0,
+         total = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -51,6 +55,7 @@ inline FwdLayout fwd_layout(int64_t T, int64_t N, int64_t H, int64_t D,
     return at;
   };
   L.seq_first = take(sizeof(int) * (size_t)N);
+  L.chunk_tab = take(16 * (size_t)L.max_chunks);
   L.qt = take(elem * (size_t)(L.tiles * C * D));
   L.w = take(elem * (size_t)(L.tiles * C * D));
   L.ut = take(elem * (size_t)(L.tiles * D * C));
@@ -94,6 +99,7 @@ struct FwdArgs {
   const float *beta;
   OptArgs in;
   const int *cu_seqlens;  // device, or nullptr for equal lengths
+  const int4 *chunk_tab;  // in the workspace when cu_seqlens is set, else nullptr
   int num_seqs, num_heads, d, chunk;
   int64_t total_tokens;
   int seq_len;            // equal-length sequences: tokens per sequence
@@ -114,14 +120,17 @@ struct FwdArgs {
 struct BwdLayout {
   int64_t tiles = 0;
   int64_t scratch_per_tile = 0;  // floats
-  size_t seq_first = 0, kt = 0, kh = 0, qt = 0, ke = 0, w = 0, u = 0, vr = 0, gc = 0,
+  int64_t max_chunks = 0;
+  size_t seq_first = 0, chunk_tab = 0, kt = 0, kh = 0, qt = 0, ke = 0, w = 0, u = 0, vr = 0,
+         gc = 0,
          tm = 0, pm = 0, mm = 0, gam = 0, bt = 0, px = 0, qy = 0, sc = 0, dse = 0, dun = 0,
          scratch = 0, total = 0;
 };
 
 inline BwdLayout bwd_layout(int64_t T, int64_t N, int64_t H, int64_t D, int64_t C) {
   BwdLayout L;
-  L.tiles = ((T + N * (C - 1)) / C) * H;
+  L.max_chunks = (T + N * (C - 1)) / C;
+  L.tiles = L.max_chunks * H;
   L.scratch_per_tile = 9 * C * D + 4 * C * C + D;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -131,6 +140,7 @@ inline BwdLayout bwd_layout(int64_t T, int64_t N, int64_t H, int64_t D, int64_t 
   };
   const size_t f = sizeof(float), t = (size_t)L.tiles;
   L.seq_first = take(sizeof(int) * (size_t)N);
+  L.chunk_tab = take(16 * (size_t)L.max_chunks);
   L.kt = take(f * t * C * D);
   L.kh = take(f * t * C * D);
   L.qt = take(f * t * C * D);
@@ -158,6 +168,7 @@ struct BwdArgs {
   const void *q, *k, *v, *d_o;
   const float *g, *beta, *s0, *dsf;
   const int *cu_seqlens;
+  const int4 *chunk_tab;  // in the workspace when cu_seqlens is set, else nullptr
   int num_seqs, num_heads, d, chunk, seq_len;
   int64_t grid_chunks;
   void *dq, *dk, *dv;
@@ -186,6 +197,13 @@ inline hipError_t raise_lds_limit(const void *kernel, int bytes,
   return e;
 }
 hipError_t launch_intra(const FwdArgs &a, kda_dtype dt);
+// Builds the chunk table and seq_first of packed sequences from cu [N + 1]
+// (one workgroup).  Offsets that break the rules cannot make it write past
+// the table or describe chunks outside [0, total); the call's other kernels
+// then compute garbage but stay in bounds.  Returns at once when check_inputs
+// has flagged cu (in.check).
+hipError_t launch_chunk_table(const int *cu, int N, int64_t total, int C, int64_t max_chunks,
+                              int4 *tab, int *seq_first, const OptArgs &in, hipStream_t stream);
 // Validates cu_seqlens [N + 1] (cu[0] = 0, non-decreasing, cu[N] = total) and
 // ORs KDA_FLAG_BAD_CU_SEQLENS into *flags when it fails.
 hipError_t launch_check_cu(const int *cu, int N, int64_t total, int *flags, hipStream_t stream);

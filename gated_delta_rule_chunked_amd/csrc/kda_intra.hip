@@ -99,32 +99,19 @@ __device__ __forceinline__ void copy_run(T *dst, const T *row32) {
   *reinterpret_cast<typename Frag<T>::type *>(dst) = join4(load4<T>(row32), load4<T>(row32 + 16));
 }
 
-// L consecutive elements of one type, in 16- or 8-byte pieces when they fill
-// them (p is aligned to the piece size).
+// A thread's run of L consecutive elements of one channel (L = 1, 2, 4, 8
+// tokens), kept as one vector so that 16-bit elements share registers in
+// pairs, and stored to LDS in one piece (the destination is aligned to it).
 template <typename T, int L>
-__device__ __forceinline__ void store_elems(T *p, const T *x) {
-  constexpr int V = 16 / (int)sizeof(T);
-  if constexpr (sizeof(T) == 2 && L % V != 0 && L % 4 == 0) {
-#pragma unroll
-    for (int j = 0; j < L; j += 4)
-      *reinterpret_cast<typename Vec4<T>::type *>(p + j) =
-          typename Vec4<T>::type{x[j], x[j + 1], x[j + 2], x[j + 3]};
-  } else if constexpr (L % V == 0) {
-#pragma unroll
-    for (int j = 0; j < L; j += V) {
-      typename Frag<T>::type r;  // 8 elements for bf16; 8 fp32 = two pieces
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = x[j + i];
-        *reinterpret_cast<typename Frag<T>::type *>(p + j) = r;
-      } else {
-        *reinterpret_cast<f32x4 *>(p + j) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < L; ++i) p[i] = x[i];
-  }
+struct Run {
+  typedef T type __attribute__((ext_vector_type(L < 2 ? 2 : L)));
+};
+template <typename T, int L>
+__device__ __forceinline__ void store_run(T *p, const typename Run<T, L>::type &x) {
+  if constexpr (L == 1)
+    *p = x[0];
+  else
+    *reinterpret_cast<typename Run<T, L>::type *>(p) = x;
 }
 
 // RAW: the gate input is z in the operand type and in.gate selects the gate
@@ -133,7 +120,7 @@ template <typename T, int D, int C, bool RAW>
 __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const void *__restrict__ gate, const float *__restrict__ beta, const OptArgs in,
-    const int *__restrict__ cu, int N, int H, int seq_len, int *__restrict__ seq_first,
+    const int4 *__restrict__ tab, int N, int H, int seq_len,
     T *__restrict__ qt_out, T *__restrict__ w_out, T *__restrict__ ut_out,
     T *__restrict__ ket_out, T *__restrict__ p_out, float *__restrict__ gam_out) {
   using Cfg = IntraCfg<T, D, C>;
@@ -153,16 +140,13 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   float *sA = reinterpret_cast<float *>(smem + Cfg::BYTES_X);    // [C][LDA] (phase 2+)
   f32x4 *sTot = reinterpret_cast<f32x4 *>(smem + Cfg::BYTES_X);  // [RG][CG] (phase 1)
   float *sBeta = reinterpret_cast<float *>(smem + Cfg::BYTES_X + Cfg::BYTES_Y);
-  __shared__ int s_loc[4];
-  __shared__ int s_scan[NT];
 
   // heads vary fastest over the grid: the tiles resident together then read
   // whole token rows of the [T, H, d] inputs instead of one head's slice
   if (inputs_rejected(in)) return;
   const int h = (int)(blockIdx.x % (unsigned)H), c = (int)(blockIdx.x / (unsigned)H);
-  locate_chunk(c, h, cu, N, seq_len, C, s_loc, s_scan, seq_first);
-  const int t0 = __builtin_amdgcn_readfirstlane(s_loc[1]);
-  const int n = __builtin_amdgcn_readfirstlane(s_loc[2]);
+  const ChunkLoc loc = chunk_loc(c, tab, N, seq_len, C);
+  const int t0 = loc.t0, n = loc.n;
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const int tid = threadIdx.x, lane = lane_id();
@@ -215,7 +199,7 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
 
   // Per channel of this thread's token run: Diag(beta) Kt, Diag(beta) V and
   // Ke, staged transposed in phase 3.
-  T bk[4][RPT], bv[4][RPT], ke[4][RPT];
+  typename Run<T, RPT>::type bk[4], bv[4], ke[4];
   // Full chunks (every tile but a sequence's last) skip the row masks.
   auto scaled_rows = [&](auto tail) {
     constexpr bool TAIL = decltype(tail)::value;
@@ -342,9 +326,9 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   if (r0 < C) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      store_elems<T, RPT>(sBKt + (ch0 + e) * LDT + r0, bk[e]);
-      store_elems<T, RPT>(sBVt + (ch0 + e) * LDT + r0, bv[e]);
-      store_elems<T, RPT>(sKeT + (ch0 + e) * LDT + r0, ke[e]);
+      store_run<T, RPT>(sBKt + (ch0 + e) * LDT + r0, bk[e]);
+      store_run<T, RPT>(sBVt + (ch0 + e) * LDT + r0, bv[e]);
+      store_run<T, RPT>(sKeT + (ch0 + e) * LDT + r0, ke[e]);
     }
   }
   if (CK > C) {  // padding tokens are zero
@@ -445,8 +429,8 @@ static hipError_t launch_intra_t(const FwdArgs &a) {
   char *ws = a.ws;
   hipLaunchKernelGGL(kern, grid, dim3(Cfg::NT), Cfg::LDS_BYTES, a.stream,
                      reinterpret_cast<const T *>(a.q), reinterpret_cast<const T *>(a.k),
-                     reinterpret_cast<const T *>(a.v), a.gate, a.beta, a.in, a.cu_seqlens, a.num_seqs,
-                     a.num_heads, a.seq_len, reinterpret_cast<int *>(ws + a.lay.seq_first),
+                     reinterpret_cast<const T *>(a.v), a.gate, a.beta, a.in, a.chunk_tab,
+                     a.num_seqs, a.num_heads, a.seq_len,
                      reinterpret_cast<T *>(ws + a.lay.qt), reinterpret_cast<T *>(ws + a.lay.w),
                      reinterpret_cast<T *>(ws + a.lay.ut), reinterpret_cast<T *>(ws + a.lay.ket),
                      reinterpret_cast<T *>(ws + a.lay.p), reinterpret_cast<float *>(ws + a.lay.gam));

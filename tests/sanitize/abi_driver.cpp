@@ -18,7 +18,9 @@
 
 namespace {
 struct Record {
-  int intra = 0, inter = 0, epilogue = 0, check_cu = 0, decode = 0, bwd = 0;
+  int intra = 0, inter = 0, epilogue = 0, check_cu = 0, decode = 0, bwd = 0, table = 0;
+  int64_t table_entries = 0;
+  const int4 *tab = nullptr;
   kda::FwdArgs fwd{};
   kda::BwdArgs bwdargs{};
   int64_t epi_rows = 0;
@@ -36,7 +38,9 @@ void check(bool ok, const char *what, int line) {
 }
 #define CHECK(x) check((x), #x, __LINE__)
 
-int launches() { return rec.intra + rec.inter + rec.epilogue + rec.check_cu + rec.decode + rec.bwd; }
+int launches() {
+  return rec.intra + rec.inter + rec.epilogue + rec.check_cu + rec.decode + rec.bwd + rec.table;
+}
 void reset() { rec = Record(); launch_result = hipSuccess; }
 
 void *dev(uintptr_t i) { return reinterpret_cast<void *>((uintptr_t)0x100000 + 0x1000 * i); }
@@ -48,6 +52,13 @@ hipError_t launch_intra(const FwdArgs &a, kda_dtype) { ++rec.intra; rec.fwd = a;
 hipError_t launch_inter(const FwdArgs &a, kda_dtype) { ++rec.inter; rec.fwd = a; return launch_result; }
 hipError_t launch_check_cu(const int *, int, int64_t, int *, hipStream_t) {
   ++rec.check_cu;
+  return launch_result;
+}
+hipError_t launch_chunk_table(const int *, int, int64_t, int, int64_t max_chunks, int4 *tab,
+                              int *, const OptArgs &, hipStream_t) {
+  ++rec.table;
+  rec.table_entries = max_chunks;
+  rec.tab = tab;
   return launch_result;
 }
 hipError_t launch_bwd(const BwdArgs &a, kda_dtype) { ++rec.bwd; rec.bwdargs = a; return launch_result; }
@@ -93,13 +104,13 @@ struct Fwd {
 void layout_fits(const kda::FwdArgs &a, size_t ws_bytes) {
   const kda::FwdLayout &L = a.lay;
   CHECK(L.total <= ws_bytes);
-  const size_t offs[] = {L.seq_first, L.qt, L.w, L.ut, L.ket, L.p, L.gam};
+  const size_t offs[] = {L.seq_first, L.chunk_tab, L.qt, L.w, L.ut, L.ket, L.p, L.gam};
   for (size_t off : offs) {
     CHECK(off % 256 == 0);
     CHECK(off < L.total || (off == L.total && a.total_tokens == 0));
   }
-  CHECK(L.seq_first < L.qt && L.qt < L.w && L.w < L.ut && L.ut < L.ket && L.ket < L.p &&
-        L.p < L.gam);
+  CHECK(L.seq_first < L.chunk_tab && L.chunk_tab < L.qt && L.qt < L.w && L.w < L.ut &&
+        L.ut < L.ket && L.ket < L.p && L.p < L.gam);
   CHECK(a.grid_chunks >= 0 && a.grid_chunks <= L.max_chunks);
 }
 
@@ -139,7 +150,14 @@ void fwd_cases() {
           CHECK(f.run() == KDA_SUCCESS);
           CHECK(rec.intra == 1 && rec.inter == 1);
           layout_fits(rec.fwd, f.ws_bytes);
-          if (varlen) CHECK(rec.fwd.grid_chunks == rec.fwd.lay.max_chunks);
+          if (varlen) {
+            CHECK(rec.fwd.grid_chunks == rec.fwd.lay.max_chunks);
+            CHECK(rec.table == 1 && rec.table_entries == rec.fwd.lay.max_chunks);
+            CHECK(reinterpret_cast<const char *>(rec.tab) ==
+                  static_cast<const char *>(f.ws) + rec.fwd.lay.chunk_tab);
+          } else {
+            CHECK(rec.table == 0 && rec.fwd.chunk_tab == nullptr);
+          }
         }
   // stages one at a time
   {

@@ -330,3 +330,17 @@ def test_many_pairs_every_slice_width(dtype, d, n_seqs):
                          len_range=(1, 150), s0_std=0.05)
     o, s = _run_gpu(w)
     _check(w, o, s)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [(kin.BF16, 128, 64), (kin.BF16, 64, 32),
+                                           (kin.F32, 32, 16)])
+def test_many_short_packed_sequences(dtype, d, chunk):
+    """1,100 packed sequences of 1 to 100 tokens (some chunks straddle no
+    boundary, many sequences are a single partial chunk), 2 heads, initial
+    states: the chunk table built once per call locates every chunk; all
+    outputs and final states against the oracle."""
+    print(f"[parity] 1100 short sequences dtype={dtype} d={d} C={chunk}", flush=True)
+    w = kin.make_prefill(1100 + d + chunk, B=1100, H=2, d=d, dtype=dtype, chunk_size=chunk,
+                         len_range=(1, 100), s0_std=0.05)
+    o, s = _run_gpu(w)
+    _check(w, o, s)
