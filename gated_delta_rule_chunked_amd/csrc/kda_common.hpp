@@ -243,7 +243,8 @@ __device__ __forceinline__ f32x4 gate_softplus(f32x4 z, float eA) {
                gate_softplus(z[3], eA)};
 }
 
-// The bounded gate g = g_min sigmoid(z), in (g_min, 0).
+// The bounded gate g = g_min sigmoid(z): in (g_min, 0) mathematically; in
+// fp32 sigmoid rounds to 1 for z above about 17, so g can equal g_min.
 __device__ __forceinline__ float gate_sigmoid(float z, float gmin) { return gmin * sigmoid(z); }
 __device__ __forceinline__ f32x4 gate_sigmoid(f32x4 z, float gmin) {
   return f32x4{gmin * sigmoid(z[0]), gmin * sigmoid(z[1]), gmin * sigmoid(z[2]),

@@ -20,8 +20,15 @@
 //
 // (* = per-channel product.)  The inter-chunk kernel then uses U - W S,
 // Qt S + P (U - W S) and e^(G_n) S + Ke^T (U - W S).  The chunk-start
-// reference of Kh needs G_n > -80 per channel (e^80 is far inside fp32 and
-// bf16 range), the bound quoted in the same section of mkdocs.reaper.mx.
+// reference of Kh needs G_n >= -80 per channel (e^80 is far inside fp32 and
+// bf16 range), the bound quoted in the same section of mkdocs.reaper.mx for
+// a 16-token tile.  A chunk that decays further in some channel takes a
+// second form of A and P (tile-uniform branch): each 16-token block b is
+// referenced to R_b, the cumulative decay before it, so that
+//   A[i][j] = beta_i sum_e (K_i e^(G_i - R_bi)) e^(R_bi - R_bj) (K_j e^(R_bj - G_j))
+// with the first two factors <= 1 and the third bounded by the decay inside
+// block bj; P likewise with Q.  The bound then applies to 16-token blocks
+// only; Ke takes e^(G_n - G) directly.
 //
 // One workgroup of 4 wavefronts per tile:
 //  1. Thread t owns 4 channels x RPT consecutive tokens.  It loads its g, q,
@@ -77,7 +84,8 @@ struct IntraCfg {
   static constexpr int BYTES_A = C * LDA * 4;
   static constexpr int BYTES_TOT = RG * CG * 16;   // phase-1 token-group totals (alias A)
   static constexpr int BYTES_Y = BYTES_A > BYTES_TOT ? BYTES_A : BYTES_TOT;
-  static constexpr int LDS_BYTES = BYTES_X + BYTES_Y + C * 4;
+  static constexpr int BYTES_REF = NRB * D * 4;     // per-block decay references
+  static constexpr int LDS_BYTES = BYTES_X + BYTES_Y + C * 4 + BYTES_REF;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(C % 16 == 0 && D % 32 == 0 && RPT * RG >= C, "tile shape");
   static_assert(RPT == 1 || RPT == 2 || RPT % 4 == 0, "token runs per thread");
@@ -140,6 +148,7 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   float *sA = reinterpret_cast<float *>(smem + Cfg::BYTES_X);    // [C][LDA] (phase 2+)
   f32x4 *sTot = reinterpret_cast<f32x4 *>(smem + Cfg::BYTES_X);  // [RG][CG] (phase 1)
   float *sBeta = reinterpret_cast<float *>(smem + Cfg::BYTES_X + Cfg::BYTES_Y);
+  float *sRef = reinterpret_cast<float *>(smem + Cfg::BYTES_X + Cfg::BYTES_Y + C * 4);  // [NRB][D]
 
   // heads vary fastest over the grid: the tiles resident together then read
   // whole token rows of the [T, H, d] inputs instead of one head's slice
@@ -200,6 +209,11 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   // Per channel of this thread's token run: Diag(beta) Kt, Diag(beta) V and
   // Ke, staged transposed in phase 3.
   typename Run<T, RPT>::type bk[4], bv[4], ke[4];
+  T *qt_tile = qt_out + tile * (C * D);
+  // Whether some channel of the chunk decays by more than the bound of the
+  // chunk-start reference (uniform over the workgroup).
+  bool far = false;
+  f32x4 far_pre = zero4(), far_tot = zero4();
   // Full chunks (every tile but a sequence's last) skip the row masks.
   auto scaled_rows = [&](auto tail) {
     constexpr bool TAIL = decltype(tail)::value;
@@ -223,14 +237,20 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       tot += x;
     }
     const f32x4 etot = {__expf(tot[0]), __expf(tot[1]), __expf(tot[2]), __expf(tot[3])};
-    if (rg == 0) {
-      *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
-      // precondition of the chunk-start reference: summed log-decay >= -80
-      // (e^80 is finite in fp32 and bf16)
-      if (in.flags && (tot[0] < -80.f || tot[1] < -80.f || tot[2] < -80.f || tot[3] < -80.f))
-        atomicOr(in.flags, KDA_FLAG_DECAY_RANGE);
+    if (rg == 0) *reinterpret_cast<f32x4 *>(gam_out + tile * D + ch0) = etot;
+    // The chunk-start reference holds while the summed log-decay is >= -80
+    // in every channel (e^80 is finite in fp32 and bf16).  Every wavefront's
+    // 64 threads cover all CG channel groups (CG <= 64 divides 64) and read
+    // the same totals from LDS, so a wavefront vote gives every wave the same
+    // answer without a workgroup barrier.
+    static_assert(64 % CG == 0, "each wavefront covers every channel group");
+    far = __any(tot[0] < -80.f || tot[1] < -80.f || tot[2] < -80.f || tot[3] < -80.f) != 0;
+    if (__builtin_expect(far, 0)) {  // the block-referenced rows are formed by far_rows
+      far_pre = pre;
+      far_tot = tot;
+      return;
     }
-    // e^-G = 1 / e^G and e^(G_n - G) = e^G_n / e^G: in range for G > -80
+    // e^-G = 1 / e^G and e^(G_n - G) = e^G_n / e^G: in range for G >= -80
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int r = r0 + j;
@@ -264,19 +284,85 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       }
     }
   };
+  // Block-referenced rows of a chunk past the bound (rare: one masked form).
+  auto far_rows = [&](const f32x4 pre, const f32x4 tot) {
+    constexpr bool TAIL = true;
+    // R_b = G of the row before block b (0 for block 0), written by the
+    // thread that owns that row
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j;
+      if (r < C - 1 && (r & 15) == 15)
+        *reinterpret_cast<f32x4 *>(sRef + ((r + 1) >> 4) * D + ch0) = Gv[j] + pre;
+    }
+    if (rg == 0) *reinterpret_cast<f32x4 *>(sRef + ch0) = zero4();
+    __syncthreads();
+    // the remaining bound: every 16-token block's summed log-decay >= -80
+    if (rg == 0 && in.flags) {
+      bool bad = false;
+#pragma unroll
+      for (int b = 0; b < NRB; ++b) {
+        const f32x4 lo = b + 1 < NRB ? *reinterpret_cast<const f32x4 *>(sRef + (b + 1) * D + ch0)
+                                     : tot;
+        const f32x4 d = lo - *reinterpret_cast<const f32x4 *>(sRef + b * D + ch0);
+        bad |= d[0] < -80.f || d[1] < -80.f || d[2] < -80.f || d[3] < -80.f;
+      }
+      if (bad) atomicOr(in.flags, KDA_FLAG_DECAY_RANGE);
+    }
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int r = r0 + j;
+      if (r < C) {
+        const bool live = !TAIL || r < n;
+        f32x4 qv = live ? to_f32x4(qr[j]) : zero4();
+        f32x4 kv = live ? to_f32x4(kr[j]) : zero4();
+        const f32x4 vv = live ? to_f32x4(vr[j]) : zero4();
+        if (in.l2norm_qk) {
+          qv *= l2_inv_norm<CG>(qv);
+          kv *= l2_inv_norm<CG>(kv);
+        }
+        const float br = live ? (in.beta_logits ? sigmoid(brr[j]) : brr[j]) : 0.f;
+        if (cg == 0) sBeta[r] = br;
+        const f32x4 G = Gv[j] + pre;
+        const f32x4 R = *reinterpret_cast<const f32x4 *>(sRef + (r >> 4) * D + ch0);
+        f32x4 qt, kt, ktl, qtl, khl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float eg = __expf(G[e]);
+          const float el = __expf(G[e] - R[e]);  // <= 1; >= e^-80 inside a block
+          const float eh = __builtin_amdgcn_rcpf(el);
+          qt[e] = qv[e] * eg;
+          kt[e] = kv[e] * eg;
+          ktl[e] = kv[e] * el;
+          qtl[e] = qv[e] * el;
+          khl[e] = kv[e] * eh;
+          ke[e][j] = from_f32<T>(kv[e] * __expf(tot[e] - G[e]));
+          bk[e][j] = from_f32<T>(br * kt[e]);
+          bv[e][j] = from_f32<T>(br * vv[e]);
+        }
+        // Qt goes out here: sQt holds the block-referenced rows
+        store4_f32<T>(qt_tile + frag_off(r, kperm_pos(ch0), D), qt);
+        store4_f32<T>(sKt + r * LDR + ch0, ktl);
+        store4_f32<T>(sKh + r * LDR + ch0, khl);
+        store4_f32<T>(sQt + r * LDR + ch0, qtl);
+      }
+    }
+  };
   if (n == C)
     scaled_rows(Flag<false>{});
   else
     scaled_rows(Flag<true>{});
+  if (__builtin_expect(far, 0)) far_rows(far_pre, far_tot);
   __syncthreads();
 
   // ---------------- phase 2: Qt out; A and P on the matrix cores ------------
   // Qt leaves from LDS one contiguous 16 x 32 fragment block per wavefront
   // store (rows past the chunk end are zero).
-  T *qt_tile = qt_out + tile * (C * D);
-  for (int b = wv; b < Cfg::NQB; b += NW) {
-    const int rb = b / KD, ks = b % KD;
-    copy_run<T>(qt_tile + b * 512 + lane * 8, sQt + (16 * rb + lr) * LDR + 32 * ks + 4 * lg);
+  if (!far) {
+    for (int b = wv; b < Cfg::NQB; b += NW) {
+      const int rb = b / KD, ks = b % KD;
+      copy_run<T>(qt_tile + b * 512 + lane * 8, sQt + (16 * rb + lr) * LDR + 32 * ks + 4 * lg);
+    }
   }
   // Each wave takes a token block and a pair of key blocks 2m, 2m + 1, whose
   // P columns are adjacent kperm positions: one 16-byte store per lane.
@@ -286,7 +372,12 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   // return a stale register on gfx950, so results are only ever read in
   // straight-line code after the instructions that produce them.
   T *p_tile = p_out + tile * (C * CK);
-#pragma unroll
+  // FAR: the row operands are scaled by e^(R_rb - R_kb) per channel for key
+  // block kb (1 on and above the diagonal blocks, which are masked anyway).
+  auto ap_tiles = [&](auto far_form) {
+  constexpr bool FAR = decltype(far_form)::value;
+  // (the rare FAR form is kept compact: its loops are not unrolled)
+#pragma unroll FAR ? 1 : 2
   for (int it = 0; it < (Cfg::NP + NW - 1) / NW; ++it) {
     const int idx = wv + NW * it;
     if (idx >= Cfg::NP) break;
@@ -300,10 +391,30 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       const F fq = load8<T>(sQt + (16 * rb + lr) * LDR + kk);
       const F fh0 = load8<T>(sKh + hrow0 * LDR + kk);
       const F fh1 = load8<T>(sKh + hrow1 * LDR + kk);
-      accA0 = mma_k32(fk, fh0, accA0);  // A[16 rb + 4 lg + i][32 m + lr]
-      accA1 = mma_k32(fk, fh1, accA1);  // A[16 rb + 4 lg + i][32 m + 16 + lr]
-      accP0 = mma_k32(fh0, fq, accP0);  // P[16 rb + lr][32 m + 4 lg + i]
-      accP1 = mma_k32(fh1, fq, accP1);  // P[16 rb + lr][32 m + 16 + 4 lg + i]
+      if constexpr (FAR) {
+        const float *rr = sRef + rb * D + kk;
+        const float *r0p = sRef + min(2 * m, NRB - 1) * D + kk;
+        const float *r1p = sRef + min(2 * m + 1, NRB - 1) * D + kk;
+        F fk0, fk1, fq0, fq1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float s0 = __expf(fminf(rr[e] - r0p[e], 0.f));
+          const float s1 = __expf(fminf(rr[e] - r1p[e], 0.f));
+          fk0[e] = from_f32<T>(to_f32(fk[e]) * s0);
+          fk1[e] = from_f32<T>(to_f32(fk[e]) * s1);
+          fq0[e] = from_f32<T>(to_f32(fq[e]) * s0);
+          fq1[e] = from_f32<T>(to_f32(fq[e]) * s1);
+        }
+        accA0 = mma_k32(fk0, fh0, accA0);
+        accA1 = mma_k32(fk1, fh1, accA1);
+        accP0 = mma_k32(fh0, fq0, accP0);
+        accP1 = mma_k32(fh1, fq1, accP1);
+      } else {
+        accA0 = mma_k32(fk, fh0, accA0);  // A[16 rb + 4 lg + i][32 m + lr]
+        accA1 = mma_k32(fk, fh1, accA1);  // A[16 rb + 4 lg + i][32 m + 16 + lr]
+        accP0 = mma_k32(fh0, fq, accP0);  // P[16 rb + lr][32 m + 4 lg + i]
+        accP1 = mma_k32(fh1, fq, accP1);  // P[16 rb + lr][32 m + 16 + 4 lg + i]
+      }
     }
     f32x4 bta;
 #pragma unroll
@@ -319,6 +430,15 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       accP1[i] = (32 * m + 16 + 4 * lg + i <= prow) ? accP1[i] : 0.f;
     }
     store8_f32<T>(p_tile + frag_off(prow, 32 * m + 8 * lg, CK), accP0, accP1);
+  }
+  };
+  if constexpr (NRB > 1) {
+    if (__builtin_expect(far, 0))
+      ap_tiles(Flag<true>{});
+    else
+      ap_tiles(Flag<false>{});
+  } else {  // one block per chunk: the block reference is the chunk start
+    ap_tiles(Flag<false>{});
   }
   __syncthreads();
 

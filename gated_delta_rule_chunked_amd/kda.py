@@ -272,8 +272,8 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     sigmoid(out_gate) (out_gate [T, H, d] in v's dtype, or None).
 
     Diagnostics: `flags` (int32 [1] device tensor, zeroed by the caller)
-    collects FLAG_DECAY_RANGE (a chunk's summed log-decay reached -80, the
-    precondition of the chunk algorithm) and, with check_inputs,
+    collects FLAG_DECAY_RANGE (a 16-token block's summed log-decay fell
+    below -80, the precondition of the chunk algorithm) and, with check_inputs,
     FLAG_BAD_CU_SEQLENS (cu_seqlens failed validation on the device; nothing
     was computed).  Read it after synchronising.
     """

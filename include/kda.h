@@ -114,12 +114,16 @@ size_t kda_fwd_chunked_workspace_size(int64_t total_tokens, int32_t num_seqs,
  *               ordered (same stream or synchronised).
  *   stream      hipStream_t or NULL.
  *
- * Precondition of the chunk algorithm (mkdocs.reaper.mx, section "Le piege
- * numerique de la decroissance cumulee"): inside any chunk the summed
- * log-decay of every channel must stay above -80, so that exp(-G) stays in
- * fp32/bf16 range.  Larger decays give inf/NaN outputs; use a smaller
- * chunk_size for such inputs.  kda_fwd_chunked_ex reports a breach in
- * kda_options.flags (KDA_FLAG_DECAY_RANGE).
+ * Decay range (mkdocs.reaper.mx, section "Le piege numerique de la
+ * decroissance cumulee": the chunk form divides by the cumulative decay, and
+ * the page bounds it over a 16-token tile).  Chunks whose summed log-decay
+ * stays >= -80 in every channel are referenced to the chunk start; a chunk
+ * that decays further is referenced per 16-token block, which is exact for
+ * any decay as long as every 16-token block's summed log-decay is >= -80 per
+ * channel (e^80 is finite in fp32 and bf16).  That block bound is the only
+ * precondition: past it outputs may be inf/NaN, and kda_fwd_chunked_ex
+ * reports the breach in kda_options.flags (KDA_FLAG_DECAY_RANGE).  Per-token
+ * log-decays >= -5 always meet it.
  *
  * q, k, v, o and the states must be 16-byte aligned; log_alpha 16-byte;
  * beta and cu_seqlens 4-byte.  chunk_size must be 16, 32 or 64.
@@ -228,11 +232,11 @@ typedef struct {
 } kda_options;
 
 /* Bits of kda_options.flags. */
-#define KDA_FLAG_DECAY_RANGE 1    /* some chunk's summed log-decay reached -80
-                                     in a channel: outside the precondition of
-                                     the chunk algorithm (see kda_fwd_chunked);
-                                     that chunk's outputs may be inf/NaN.  Set
-                                     by the intra-chunk kernel.               */
+#define KDA_FLAG_DECAY_RANGE 1    /* some 16-token block's summed log-decay fell
+                                     below -80 in a channel: outside the
+                                     precondition of the chunk algorithm (see
+                                     kda_fwd_chunked); that chunk's outputs may
+                                     be inf/NaN.  Set by the intra-chunk kernel. */
 #define KDA_FLAG_BAD_CU_SEQLENS 2 /* check_inputs: cu_seqlens failed
                                      validation; nothing was computed.        */
 
@@ -251,8 +255,8 @@ typedef struct {
  *   beta     [total_tokens, H] fp32: beta, or its logits.
  * Every other argument is as for kda_fwd_chunked, and so is the decay
  * precondition, which now applies to the g the gate function produces.
- * KDA_GATE_SIGMOID with gate_min >= -5 meets it for any z when
- * chunk_size = 16 (16 x 5 = 80, the tile bound of the section cited above).
+ * KDA_GATE_SIGMOID with gate_min >= -5 meets it for any z and any chunk size
+ * (16 x 5 = 80, the tile bound of the section cited above).
  */
 kda_status kda_fwd_chunked_ex(const kda_options *options, uint32_t stages, const void *q,
                               const void *k, const void *v, const void *gate,
