@@ -39,6 +39,11 @@
 
 namespace kda {
 
+template <bool B>
+struct StepKind {
+  static constexpr bool value = B;
+};
+
 template <typename T, int D, int C, int CT>
 struct InterOps {
   using F = typename Frag<T>::type;
@@ -189,10 +194,13 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     load_kg(B, ci);
   };
 
-  auto step = [&](Buf &B, int ci) {
+  // FULL: a chunk of C rows (every chunk but a sequence's last), whose o
+  // stores need no row mask.
+  auto step = [&](Buf &B, int ci, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     const int nxt = min(ci + PF, nch - 1);
     const int tc = t0 + ci * C;
-    const int rows = min(C, len - ci * C);
+    const int rows = FULL ? C : min(C, len - ci * C);
 
     // S entering the chunk, as K-step operands over channels, per column tile
     F sb[CT][KD];
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
         ov[t] = vec4_from_f32<T>(oc + 0.f);
       }
       T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
-      if (rows == C) {
+      if (FULL || rows == C) {
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
@@ -289,11 +297,22 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     load_all(B1, min(1, nch - 1));
     load_all(B2, min(2, nch - 1));
   }
-  for (int ci = 0; ci < nch; ci += 3) {
-    step(B0, ci);
-    if (ci + 1 < nch) step(B1, ci + 1);
-    if (ci + 2 < nch) step(B2, ci + 2);
+  // Full chunks three at a time with nothing conditional in the loop body:
+  // every pass issues the same loads and stores, so the waits the compiler
+  // places for a buffer's loads leave the other two chunks' loads in flight
+  // (conditional steps inside the loop made one step in three wait for the
+  // next chunk's loads as well).  The last one to three chunks, the partial
+  // one included, follow the loop.
+  const int nfull = len / C;
+  int ci = 0;
+  for (; ci + 3 <= nfull; ci += 3) {
+    step(B0, ci, StepKind<true>{});
+    step(B1, ci + 1, StepKind<true>{});
+    step(B2, ci + 2, StepKind<true>{});
   }
+  if (ci < nch) step(B0, ci, StepKind<false>{});
+  if (ci + 1 < nch) step(B1, ci + 1, StepKind<false>{});
+  if (ci + 2 < nch) step(B2, ci + 2, StepKind<false>{});
 
   if (s_final && has_state) {
 #pragma unroll
