@@ -117,7 +117,7 @@ def backward_bytes_per_token_head(d, E):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "gated_delta_rule_chunked_amd", "csrc")
 KERNEL_SOURCES = {"intra": ("kda_intra.hip",), "inter": ("kda_inter.hip", "kda_epilogue.hip"),
-                  "decode_kernel": ("kda_decode.hip",)}
+                  "decode_kernel": ("kda_decode.hip",), "bwd": ("kda_backward.hip",)}
 
 
 def kernel_source_sha(kernel):
@@ -402,13 +402,15 @@ def time_backward(torch, kda, w, steps, warmup, d, E):
     hbm_bound = t_hbm >= t_mma
     ach = (byts / sec / 1e9) if hbm_bound else (flops / sec / 1e12)
     peak = HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS
+    traffic = measured_traffic("backward", "bwd")  # the call's three or four kernels
     return dict(tokens_per_s=w.total_tokens / sec, ms_per_step=ms,
                 algorithmic_bytes=byts, algorithmic_flops=flops,
                 roofline_frac=max(t_hbm, t_mma) / sec,
                 mfma_frac_bf16=flops / sec / 1e12 / BF16_PEAK_TFLOPS,
                 roofline=dict(bound="hbm" if hbm_bound else "mfma", achieved=ach, peak=peak,
                               unit="GB/s" if hbm_bound else "TFLOP/s",
-                              frac=max(t_hbm, t_mma) / sec, traffic=None,
+                              frac=max(t_hbm, t_mma) / sec, traffic=traffic,
+                              traffic_over_algorithmic=None if traffic is None else traffic / byts,
                               scope="whole kda_bwd_chunked call (3 or 4 kernels); bytes: q, k, v, "
                                     "d_o, dq, dk, dv in bf16, g and dg in fp32, beta and dbeta; "
                                     "flops: the method's, triangles once, priced at the bf16 peak",
