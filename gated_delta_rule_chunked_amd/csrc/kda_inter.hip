@@ -61,6 +61,7 @@ struct InterOps {
     V4 uv[CT];      // U of the wave's token block, one output tile per column tile
     F kA[CBW][KC];  // Ke^T rows of the wave's channel blocks (K = tokens)
     f32x4 gv[CBW];  // e^{G_n} of the wave's channel rows
+    int warm;       // L2 warm-up load of a later chunk (WARM only)
   };
 };
 
@@ -68,7 +69,19 @@ struct InterOps {
 // share every W, Qt, P and Ke^T fragment a wave loads, so wider slices halve
 // the operand bytes per column but lengthen each serial step; the launch
 // takes them only where they cut the rounds of workgroups on the GPU.
-template <typename T, int D, int C, int PF, int CT>
+//
+// WARM: L2 warm-up loads.  Every slice of a (sequence, head) reads the same
+// W, Qt, Ke^T and P lines, and the first to ask for a line waits for HBM.
+// With WARM each workgroup also reads one dword from each of its 1/NS share
+// of those lines, WARM_AHEAD chunks beyond its register ring, so that the
+// ring's own loads find the lines in the XCD's L2.  The value read only
+// feeds an empty asm statement at the end.  It pays on long chains of
+// 16-column slices (measured on MI355X: the B=1 H=32 T=32768 prefill's chain
+// 549 -> 522 us) and costs time on short chains and wide slices, so the
+// launch enables it only there.
+constexpr int WARM_AHEAD = 3;
+
+template <typename T, int D, int C, int PF, int CT, bool WARM>
 __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const T *__restrict__ qt, const T *__restrict__ w, const T *__restrict__ ut,
     const T *__restrict__ ket, const T *__restrict__ pm,
@@ -193,6 +206,28 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     load_qp(B, ci);
     load_kg(B, ci);
   };
+  // warm-up line of this lane: line li of the tile's W, Qt, Ke^T and P lines
+  // taken in that order (lanes past the workgroup's share repeat its last
+  // line; the loads of one instruction to one line merge)
+  constexpr int LQ = C * D * (int)sizeof(T) / 128, LK = D * CK * (int)sizeof(T) / 128,
+                LP = C * CK * (int)sizeof(T) / 128, NL = 2 * LQ + LK + LP;
+  constexpr int NLW = (NL + NS - 1) / NS, NLV = (NLW + 3) / 4;
+  static_assert(!WARM || NLV <= 64, "one warm-up load per wave and chunk");
+  const int wli = min(slice * NLW + wv * NLV + min(lane, NLV - 1), NL - 1);
+  auto warm_load = [&](int ci) -> int {
+    const int64_t tile = tile_of(ci);
+    const char *p;
+    if (wli < LQ)
+      p = reinterpret_cast<const char *>(w + tile * (C * D)) + wli * 128;
+    else if (wli < 2 * LQ)
+      p = reinterpret_cast<const char *>(qt + tile * (C * D)) + (wli - LQ) * 128;
+    else if (wli < 2 * LQ + LK)
+      p = reinterpret_cast<const char *>(ket + tile * (D * CK)) + (wli - 2 * LQ) * 128;
+    else
+      p = reinterpret_cast<const char *>(pm + tile * (C * CK)) + (wli - 2 * LQ - LK) * 128;
+    return *reinterpret_cast<const int *>(p);
+  };
+  int warm_sink = 0;
 
   // FULL: a chunk of C rows (every chunk but a sequence's last), whose o
   // stores need no row mask.
@@ -286,16 +321,26 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     load_qp(B, nxt);
+    if constexpr (WARM) {  // the warm-up load issued PF steps ago has landed
+      warm_sink ^= B.warm;
+      B.warm = warm_load(min(ci + PF + WARM_AHEAD, nch - 1));
+    }
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
   };
 
   static_assert(PF == 3, "the chunk loop below is unrolled for three buffers");
   Buf B0, B1, B2;
+  B0.warm = B1.warm = B2.warm = 0;
   if (nch > 0) {
     load_all(B0, 0);
     load_all(B1, min(1, nch - 1));
     load_all(B2, min(2, nch - 1));
+    if constexpr (WARM) {
+      B0.warm = warm_load(min(PF, nch - 1));
+      B1.warm = warm_load(min(PF + 1, nch - 1));
+      B2.warm = warm_load(min(PF + 2, nch - 1));
+    }
   }
   // Full chunks three at a time with nothing conditional in the loop body:
   // every pass issues the same loads and stores, so the waits the compiler
@@ -313,6 +358,11 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   if (ci < nch) step(B0, ci, StepKind<false>{});
   if (ci + 1 < nch) step(B1, ci + 1, StepKind<false>{});
   if (ci + 2 < nch) step(B2, ci + 2, StepKind<false>{});
+
+  if constexpr (WARM) {
+    warm_sink ^= B0.warm ^ B1.warm ^ B2.warm;
+    asm volatile("" ::"v"(warm_sink));
+  }
 
   if (s_final && has_state) {
 #pragma unroll
@@ -342,14 +392,14 @@ int device_cus() {
   return n;
 }
 
-template <typename T, int D, int C, int CT>
+template <typename T, int D, int C, int CT, bool WARM>
 static hipError_t launch_inter_ct(const FwdArgs &a) {
   constexpr int NS = D / (16 * CT);
   const int pairs = a.num_seqs * a.num_heads;
   const int units = (pairs + 7) / 8;
   const dim3 grid((unsigned)(8 * units * NS));
   char *ws = a.ws;
-  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3, CT>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3, CT, WARM>), grid, dim3(256), 0, a.stream,
                      reinterpret_cast<const T *>(ws + a.lay.qt),
                      reinterpret_cast<const T *>(ws + a.lay.w),
                      reinterpret_cast<const T *>(ws + a.lay.ut),
@@ -376,12 +426,17 @@ static hipError_t launch_inter_c(const FwdArgs &a) {
   for (int c = 2; c <= MAX_CT; c *= 2)
     if (rounds(c) < rounds(ct)) ct = c;
   if constexpr (MAX_CT >= 4) {
-    if (ct == 4) return launch_inter_ct<T, D, C, 4>(a);
+    if (ct == 4) return launch_inter_ct<T, D, C, 4, false>(a);
   }
   if constexpr (MAX_CT >= 2) {
-    if (ct == 2) return launch_inter_ct<T, D, C, 2>(a);
+    if (ct == 2) return launch_inter_ct<T, D, C, 2, false>(a);
   }
-  return launch_inter_ct<T, D, C, 1>(a);
+  // L2 warm-up loads on 16-column slices of long chains (mean sequence
+  // length of at least WARM_MIN_CHUNKS chunks)
+  constexpr int64_t WARM_MIN_CHUNKS = 128;
+  if (a.total_tokens >= WARM_MIN_CHUNKS * C * (int64_t)a.num_seqs)
+    return launch_inter_ct<T, D, C, 1, true>(a);
+  return launch_inter_ct<T, D, C, 1, false>(a);
 }
 
 template <typename T, int D>

@@ -344,3 +344,21 @@ def test_many_short_packed_sequences(dtype, d, chunk):
                          len_range=(1, 100), s0_std=0.05)
     o, s = _run_gpu(w)
     _check(w, o, s)
+
+
+@pytest.mark.parametrize("dtype,d,chunk,shape", [
+    (kin.BF16, 128, 64, dict(B=1, T=8229, H=3)),
+    (kin.F32, 64, 32, dict(lengths=[4150, 4303], H=2)),
+    (kin.BF16, 32, 16, dict(B=2, T=2085, H=2)),
+])
+def test_long_chains_with_l2_warmup(dtype, d, chunk, shape):
+    """Few (sequence, head) pairs with at least 128 chunks each: the
+    inter-chunk launch takes 16-column slices with L2 warm-up loads, equal
+    lengths with a partial last chunk and packed sequences, initial states;
+    all outputs and final states against the oracle."""
+    print(f"[parity] long chains dtype={dtype} d={d} C={chunk} {shape}", flush=True)
+    w = kin.make_prefill(2000 + d + chunk, d=d, dtype=dtype, chunk_size=chunk, s0_std=0.05,
+                         **shape)
+    assert w.total_tokens >= 128 * chunk * w.num_seqs
+    o, s = _run_gpu(w)
+    _check(w, o, s)
