@@ -60,7 +60,7 @@ struct InterOps {
     F pA[KC];       // P rows of the wave's token block (K = tokens)
     V4 uv[CT];      // U of the wave's token block, one output tile per column tile
     F kA[CBW][KC];  // Ke^T rows of the wave's channel blocks (K = tokens)
-    f32x4 gv[CBW];  // e^{G_n} of the wave's channel rows
+    float gl;       // e^{G_n}: lane 16 j + r holds channel 16 cb_j + r (cb_j = wave's jth block)
     int warm;       // L2 warm-up load of a later chunk (WARM only)
   };
 };
@@ -198,7 +198,15 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
       const T *kk = ket + tile * (D * CK) + (cb * KC * 64 + lane) * 8;
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) B.kA[j][ks] = load8<T>(kk + ks * 512);
-      B.gv[j] = *reinterpret_cast<const f32x4 *>(gam + tile * D + 16 * cb + 4 * lg);
+    }
+    // e^{G_n} of the wave's CBW channel blocks, one dword per lane (lanes past
+    // them repeat the last block); the step gathers each lane's 4 rows with
+    // lane permutes.  A 16-byte load per lane, 16 lanes to an address, would
+    // return 16x the bytes through the vector-memory path.
+    {
+      const int jl = min(lane >> 4, CBW - 1);
+      const int cbl = ALL_CB ? wv * CBW + jl : min(wv * CBW + jl, NCB - 1);
+      B.gl = gam[tile * D + 16 * cbl + (lane & 15)];
     }
   };
   auto load_all = [&](Buf &B, int ci) {
@@ -276,9 +284,14 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
       if (ALL_CB || cb < NCB) {
+        f32x4 gj;  // e^{G_n} of rows 16 cb + 4 lg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gj[i] = __int_as_float(
+              __builtin_amdgcn_ds_bpermute((16 * j + 4 * lg + i) * 4, __float_as_int(B.gl)));
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
-          f32x4 acc = S[j][t] * B.gv[j];
+          f32x4 acc = S[j][t] * gj;
 #pragma unroll
           for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[t][ks], acc);
           S[j][t] = acc;
