@@ -181,6 +181,10 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
   f32x4 Gv[RPT];
   typename Vec4<T>::type qr[RPT], kr[RPT], vr[RPT], zr[RAW ? RPT : 1];
   float brr[RPT];
+  // The gate rows go first: the cumulative sum and its LDS exchange need
+  // only them, and the wait counter counts loads in issue order, so they run
+  // while q, k, v and beta are still arriving (the compiler otherwise issues
+  // most gate loads last; measured 6% off the kernel on long sequences).
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const unsigned r = (unsigned)min(r0 + j, n - 1);
@@ -189,6 +193,12 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       zr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(gb + off * GSZ);
     else
       Gv[j] = *reinterpret_cast<const f32x4 *>(gb + off * GSZ);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const unsigned r = (unsigned)min(r0 + j, n - 1);
+    const unsigned off = r * (unsigned)rs + (unsigned)ch0;
     qr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(qb + off * (unsigned)sizeof(T));
     kr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(kb + off * (unsigned)sizeof(T));
     vr[j] = *reinterpret_cast<const typename Vec4<T>::type *>(vb + off * (unsigned)sizeof(T));
