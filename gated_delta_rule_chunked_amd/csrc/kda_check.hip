@@ -24,23 +24,27 @@ __global__ __launch_bounds__(256) void check_cu_kernel(const int *__restrict__ c
 // The chunk table of packed sequences: chunk id -> (sequence, first token,
 // rows), ids enumerating the chunks of sequence 0, then 1, ... (chunks never
 // straddle sequences; a sequence's last chunk holds the tail).  One
-// workgroup walks the sequences 1,024 at a time: chunk counts, a block scan
-// for the first id of each sequence, then each thread writes its sequence's
-// entries.  Entries past the last chunk get rows = 0, so the tiles launched
-// for the bound max_chunks that no chunk fills have nothing to do.  Lengths
-// that break the rules (negative, or a range outside [0, total)) count as
-// empty and ids at or past max_chunks are not written.
+// workgroup walks the sequences 1,024 at a time: chunk counts and a block
+// scan give each sequence's first id; then every thread strides over the
+// pass's chunk ids and finds its sequence by binary search in the scan, so a
+// long sequence's entries are written by all threads at once.  Entries past
+// the last chunk get rows = 0, so the tiles launched for the bound
+// max_chunks that no chunk fills have nothing to do.  Lengths that break the
+// rules (negative, or a range outside [0, total)) count as empty and ids at
+// or past max_chunks are not written.
 constexpr int kTabThreads = 1024;
 
 __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(
     const int *__restrict__ cu, int N, int64_t total, int C, int64_t max_chunks,
     int4 *__restrict__ tab, int *__restrict__ seq_first, const OptArgs in) {
   if (inputs_rejected(in)) return;
-  __shared__ long long s_scan[kTabThreads];
+  __shared__ long long s_scan[kTabThreads];  // inclusive chunk-count scan of the pass
+  __shared__ int s_start[kTabThreads], s_len[kTabThreads];
   const int tid = threadIdx.x;
   long long base = 0;
   for (int s0 = 0; s0 < N; s0 += kTabThreads) {
     const int s = s0 + tid;
+    const int ns = min(kTabThreads, N - s0);  // sequences in this pass
     int start = 0, len = 0;
     if (s < N) {
       start = cu[s];
@@ -49,6 +53,8 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(
     }
     const long long nc = (len + C - 1) / C;
     s_scan[tid] = nc;
+    s_start[tid] = start;
+    s_len[tid] = len;
     __syncthreads();
     for (int off = 1; off < kTabThreads; off <<= 1) {
       const long long add = tid >= off ? s_scan[tid - off] : 0;
@@ -56,13 +62,24 @@ __global__ __launch_bounds__(kTabThreads) void chunk_table_kernel(
       s_scan[tid] += add;
       __syncthreads();
     }
-    const long long first = base + s_scan[tid] - nc;
     if (s < N) {
+      const long long first = base + s_scan[tid] - nc;
       seq_first[s] = (int)(first < max_chunks ? first : max_chunks);
-      for (long long i = 0; i < nc && first + i < max_chunks; ++i)
-        tab[first + i] = make_int4(s, start + (int)i * C, min(C, len - (int)i * C), 0);
     }
-    base += s_scan[kTabThreads - 1];
+    const long long pass_chunks = s_scan[kTabThreads - 1];
+    for (long long e = tid; e < pass_chunks && base + e < max_chunks; e += kTabThreads) {
+      // the sequence slot holding chunk e of the pass: the first slot whose
+      // inclusive count exceeds e (empty sequences never qualify)
+      int lo = 0, hi = ns - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_scan[mid] > e) hi = mid;
+        else lo = mid + 1;
+      }
+      const int i = (int)(e - (lo > 0 ? s_scan[lo - 1] : 0));  // chunk index in its sequence
+      tab[base + e] = make_int4(s0 + lo, s_start[lo] + i * C, min(C, s_len[lo] - i * C), 0);
+    }
+    base += pass_chunks;
     __syncthreads();
   }
   for (long long c = base + tid; c < max_chunks; c += kTabThreads) tab[c] = make_int4(N, 0, 0, 0);
