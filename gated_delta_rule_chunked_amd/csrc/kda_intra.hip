@@ -49,6 +49,8 @@
 // Every workspace tensor is written in the fragment-major, kperm-ordered
 // layout the inter-chunk kernel loads (kda_common.hpp), together with
 // exp(G_n) per channel.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -469,45 +471,81 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       sKeT[ch * LDT + r] = from_f32<T>(0.f);
     }
   }
-  // diagonal 16 x 16 blocks: lane j of wave b computes column j of T_bb
+  // diagonal 16 x 16 blocks: lane j of wave b computes column j of T_bb by
+  // forward substitution, right-looking: once T[m][j] is known it is added
+  // into every later row's sum, so a step waits on one multiply-add (the
+  // sums take their terms in the same order as a row-by-row substitution)
   if (wv < NRB && lane < 16) {
     const int b0 = 16 * wv, jcol = lane;
-    float tcol[16];
+    float acc[16], tcol[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) tcol[m] = (m == jcol) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      float s = 0.f;
+    for (int m = 0; m < 16; ++m) {
+      tcol[m] = jcol < m ? -acc[m] : (m == jcol ? 1.f : 0.f);
 #pragma unroll
-      for (int m = 0; m < r; ++m) s += sA[(b0 + r) * LDA + b0 + m] * tcol[m];
-      if (jcol < r) tcol[r] = -s;
+      for (int r = m + 1; r < 16; ++r) acc[r] += sA[(b0 + r) * LDA + b0 + m] * tcol[m];
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) sA[(b0 + m) * LDA + b0 + jcol] = tcol[m];
   }
   __syncthreads();
-  // blocks below the diagonal: T_ij = -T_ii X, X = sum_{m=j}^{i-1} A_im T_mj
+  // blocks below the diagonal: T_ij = -T_ii X, X = sum_{m=j}^{i-1} A_im T_mj.
+  // Block column j needs only T blocks of column j, so wave j walks its
+  // column down alone, with no barrier between block rows.  T_ij overwrites
+  // A_ij, which the walks of the columns left of j still read: each wave
+  // first copies the A and T_ii fragments of its walk into registers, and
+  // one barrier separates those reads from every write.  Each column is its
+  // own fully unrolled code, so matrix-core results are read in straight-line
+  // code; the products take their terms in block-row order as before.
+  static_assert(NRB <= NW, "one wave per block column");
+  constexpr int NPAIR = NRB * (NRB - 1) / 2;  // (i, m) pairs of column 0
+  f32x4 aF[NPAIR > 0 ? NPAIR : 1], tF[NRB > 1 ? NRB - 1 : 1];
+  auto col_load = [&](auto col) {
+    constexpr int bj = decltype(col)::value;
+    int q = 0;
 #pragma unroll
-  for (int bi = 1; bi < NRB; ++bi) {
-    f32x4 X = zero4();
-    const int bj = wv;
-    if (bj < bi) {
-      for (int m = bj; m < bi; ++m) {
-        const f32x4 af =
-            *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
+    for (int bi = bj + 1; bi < NRB; ++bi) {
+      tF[bi - bj - 1] =
+          *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
+#pragma unroll
+      for (int m = bj; m < bi; ++m, ++q)
+        aF[q] = *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * m + 4 * lg);
+    }
+  };
+  auto col_walk = [&](auto col) {
+    constexpr int bj = decltype(col)::value;
+    int q = 0;
+#pragma unroll
+    for (int bi = bj + 1; bi < NRB; ++bi) {
+      f32x4 X = zero4();
+#pragma unroll
+      for (int m = bj; m < bi; ++m, ++q) {
         f32x4 bf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) bf[i] = sA[(16 * m + 4 * lg + i) * LDA + 16 * bj + lr];
-        X = mma_f32_k16(af, bf, X);
+        X = mma_f32_k16(aF[q], bf, X);
       }
-    }
-    __syncthreads();
-    if (bj < bi) {
-      const f32x4 af =
-          *reinterpret_cast<const f32x4 *>(sA + (16 * bi + lr) * LDA + 16 * bi + 4 * lg);
-      const f32x4 Y = mma_f32_k16(af, X, zero4());
+      const f32x4 Y = mma_f32_k16(tF[bi - bj - 1], X, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) sA[(16 * bi + 4 * lg + i) * LDA + 16 * bj + lr] = -Y[i];
+    }
+  };
+  if constexpr (NRB > 1) {
+    if (wv == 0) col_load(std::integral_constant<int, 0>{});
+    if constexpr (NRB > 2) {
+      if (wv == 1) col_load(std::integral_constant<int, 1>{});
+    }
+    if constexpr (NRB > 3) {
+      if (wv == 2) col_load(std::integral_constant<int, 2>{});
+    }
+    __syncthreads();
+    if (wv == 0) col_walk(std::integral_constant<int, 0>{});
+    if constexpr (NRB > 2) {
+      if (wv == 1) col_walk(std::integral_constant<int, 1>{});
+    }
+    if constexpr (NRB > 3) {
+      if (wv == 2) col_walk(std::integral_constant<int, 2>{});
     }
     __syncthreads();
   }

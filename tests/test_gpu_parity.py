@@ -362,3 +362,15 @@ def test_long_chains_with_l2_warmup(dtype, d, chunk, shape):
     assert w.total_tokens >= 128 * chunk * w.num_seqs
     o, s = _run_gpu(w)
     _check(w, o, s)
+
+
+def test_one_long_packed_sequence_among_short_ones():
+    """A packed batch whose first sequence spans 1,094 chunks (more chunk-table
+    entries than the table kernel has threads), then a 5-token and a
+    3,000-token sequence, with initial states: every entry of the chunk table
+    and every output against the oracle."""
+    print("[parity] packed lengths 70000, 5, 3000, H=1, d=64, C=64", flush=True)
+    w = kin.make_prefill(4321, lengths=[70000, 5, 3000], H=1, d=64, dtype=kin.BF16,
+                         chunk_size=64, s0_std=0.05)
+    o, s = _run_gpu(w)
+    _check(w, o, s)
