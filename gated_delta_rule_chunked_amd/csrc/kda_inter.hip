@@ -27,9 +27,10 @@
 //
 // The intra-chunk kernel stores all of these operands fragment-major
 // (frag_off / tile_off), so every load below is one contiguous run per wave.
-// Loads are the bottleneck of a serial chain: each wave keeps PF chunks of
-// its operands in flight (a ring of register buffers, the loop unrolled by
-// PF), requesting chunk c + PF right after the last use of chunk c's group.
+// Loads are the bottleneck of a serial chain: each wave keeps PF = 3 chunks
+// of its operands in flight (a ring of register buffers, the loop unrolled
+// by 3), requesting chunk c + 3 right after the last use of chunk c's group.
+// Short sequences take PF = 1, one buffer (see the launch).
 // The requests are unconditional (chunks past the end re-read the last one)
 // and fenced with scheduling barriers so the compiler keeps them in place.
 // Workgroups of one (sequence, head) share blockIdx % 8 and therefore one
@@ -342,39 +343,54 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     lds_barrier();
   };
 
-  static_assert(PF == 3, "the chunk loop below is unrolled for three buffers");
-  Buf B0, B1, B2;
-  B0.warm = B1.warm = B2.warm = 0;
-  if (nch > 0) {
-    load_all(B0, 0);
-    load_all(B1, min(1, nch - 1));
-    load_all(B2, min(2, nch - 1));
-    if constexpr (WARM) {
-      B0.warm = warm_load(min(PF, nch - 1));
-      B1.warm = warm_load(min(PF + 1, nch - 1));
-      B2.warm = warm_load(min(PF + 2, nch - 1));
+  static_assert(PF == 1 || PF == 3, "one operand buffer, or a ring of three");
+  static_assert(!WARM || PF == 3, "warm-up loads ride on the ring");
+  if constexpr (PF == 1) {
+    // One buffer: each group of the next chunk's operands is requested right
+    // after its last use in this chunk.  About 130 registers fewer per lane
+    // than the ring, so more workgroups share a CU: for sequences of a few
+    // chunks, where no ring fills, that overlap is what counts.
+    Buf B0;
+    B0.warm = 0;
+    if (nch > 0) load_all(B0, 0);
+    const int nfull = len / C;
+    int ci = 0;
+    for (; ci < nfull; ++ci) step(B0, ci, StepKind<true>{});
+    if (ci < nch) step(B0, ci, StepKind<false>{});
+  } else {
+    Buf B0, B1, B2;
+    B0.warm = B1.warm = B2.warm = 0;
+    if (nch > 0) {
+      load_all(B0, 0);
+      load_all(B1, min(1, nch - 1));
+      load_all(B2, min(2, nch - 1));
+      if constexpr (WARM) {
+        B0.warm = warm_load(min(PF, nch - 1));
+        B1.warm = warm_load(min(PF + 1, nch - 1));
+        B2.warm = warm_load(min(PF + 2, nch - 1));
+      }
     }
-  }
-  // Full chunks three at a time with nothing conditional in the loop body:
-  // every pass issues the same loads and stores, so the waits the compiler
-  // places for a buffer's loads leave the other two chunks' loads in flight
-  // (conditional steps inside the loop made one step in three wait for the
-  // next chunk's loads as well).  The last one to three chunks, the partial
-  // one included, follow the loop.
-  const int nfull = len / C;
-  int ci = 0;
-  for (; ci + 3 <= nfull; ci += 3) {
-    step(B0, ci, StepKind<true>{});
-    step(B1, ci + 1, StepKind<true>{});
-    step(B2, ci + 2, StepKind<true>{});
-  }
-  if (ci < nch) step(B0, ci, StepKind<false>{});
-  if (ci + 1 < nch) step(B1, ci + 1, StepKind<false>{});
-  if (ci + 2 < nch) step(B2, ci + 2, StepKind<false>{});
+    // Full chunks three at a time with nothing conditional in the loop body:
+    // every pass issues the same loads and stores, so the waits the compiler
+    // places for a buffer's loads leave the other two chunks' loads in flight
+    // (conditional steps inside the loop made one step in three wait for the
+    // next chunk's loads as well).  The last one to three chunks, the partial
+    // one included, follow the loop.
+    const int nfull = len / C;
+    int ci = 0;
+    for (; ci + 3 <= nfull; ci += 3) {
+      step(B0, ci, StepKind<true>{});
+      step(B1, ci + 1, StepKind<true>{});
+      step(B2, ci + 2, StepKind<true>{});
+    }
+    if (ci < nch) step(B0, ci, StepKind<false>{});
+    if (ci + 1 < nch) step(B1, ci + 1, StepKind<false>{});
+    if (ci + 2 < nch) step(B2, ci + 2, StepKind<false>{});
 
-  if constexpr (WARM) {
-    warm_sink ^= B0.warm ^ B1.warm ^ B2.warm;
-    asm volatile("" ::"v"(warm_sink));
+    if constexpr (WARM) {
+      warm_sink ^= B0.warm ^ B1.warm ^ B2.warm;
+      asm volatile("" ::"v"(warm_sink));
+    }
   }
 
   if (s_final && has_state) {
@@ -405,14 +421,14 @@ int device_cus() {
   return n;
 }
 
-template <typename T, int D, int C, int CT, bool WARM>
+template <typename T, int D, int C, int CT, int PF, bool WARM>
 static hipError_t launch_inter_ct(const FwdArgs &a) {
   constexpr int NS = D / (16 * CT);
   const int pairs = a.num_seqs * a.num_heads;
   const int units = (pairs + 7) / 8;
   const dim3 grid((unsigned)(8 * units * NS));
   char *ws = a.ws;
-  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, 3, CT, WARM>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, PF, CT, WARM>), grid, dim3(256), 0, a.stream,
                      reinterpret_cast<const T *>(ws + a.lay.qt),
                      reinterpret_cast<const T *>(ws + a.lay.w),
                      reinterpret_cast<const T *>(ws + a.lay.ut),
@@ -429,27 +445,42 @@ static hipError_t launch_inter_ct(const FwdArgs &a) {
 // the narrowest slice among equals (shortest dependent chain per chunk).
 // fp32 operands at d = 128 keep 16-column slices: the wider slices' fp32
 // fragments do not fit the registers.
+//
+// Sequences of at most two chunks on average (many short prompts) take the
+// one-buffer form: no operand ring fills on them, and its lower register
+// count runs two or three workgroups per CU where the ring allows one.  Their
+// slices stay at most 32 columns wide, since 64-column slices keep one
+// workgroup per CU in either form.  Measured on 1,100 packed sequences of
+// 1-100 tokens, 16 heads: 1,310 -> 986 us; on longer chains the ring wins.
 template <typename T, int D, int C>
 static hipError_t launch_inter_c(const FwdArgs &a) {
   constexpr int MAX_CT = (sizeof(T) == 4 && D == 128) ? 1 : (D >= 64 ? 4 : 2);
+  const bool short_seqs = a.total_tokens <= 2 * (int64_t)C * a.num_seqs;
+  const int max_ct = short_seqs && MAX_CT > 2 ? 2 : MAX_CT;
   const int64_t units = ((int64_t)a.num_seqs * a.num_heads + 7) / 8;
   const int64_t cus = device_cus();
   auto rounds = [&](int ct) { return cus > 0 ? (8 * units * (D / (16 * ct)) + cus - 1) / cus : 1; };
   int ct = 1;
-  for (int c = 2; c <= MAX_CT; c *= 2)
+  for (int c = 2; c <= max_ct; c *= 2)
     if (rounds(c) < rounds(ct)) ct = c;
+  if (short_seqs) {
+    if constexpr (MAX_CT >= 2) {
+      if (ct == 2) return launch_inter_ct<T, D, C, 2, 1, false>(a);
+    }
+    return launch_inter_ct<T, D, C, 1, 1, false>(a);
+  }
   if constexpr (MAX_CT >= 4) {
-    if (ct == 4) return launch_inter_ct<T, D, C, 4, false>(a);
+    if (ct == 4) return launch_inter_ct<T, D, C, 4, 3, false>(a);
   }
   if constexpr (MAX_CT >= 2) {
-    if (ct == 2) return launch_inter_ct<T, D, C, 2, false>(a);
+    if (ct == 2) return launch_inter_ct<T, D, C, 2, 3, false>(a);
   }
   // L2 warm-up loads on 16-column slices of long chains (mean sequence
   // length of at least WARM_MIN_CHUNKS chunks)
   constexpr int64_t WARM_MIN_CHUNKS = 128;
   if (a.total_tokens >= WARM_MIN_CHUNKS * C * (int64_t)a.num_seqs)
-    return launch_inter_ct<T, D, C, 1, true>(a);
-  return launch_inter_ct<T, D, C, 1, false>(a);
+    return launch_inter_ct<T, D, C, 1, 3, true>(a);
+  return launch_inter_ct<T, D, C, 1, 3, false>(a);
 }
 
 template <typename T, int D>

@@ -374,3 +374,23 @@ def test_one_long_packed_sequence_among_short_ones():
                          chunk_size=64, s0_std=0.05)
     o, s = _run_gpu(w)
     _check(w, o, s)
+
+
+@pytest.mark.parametrize("dtype,d,chunk,shape", [
+    (kin.BF16, 128, 64, dict(B=16, len_range=(1, 100), H=2)),
+    (kin.BF16, 128, 64, dict(B=600, len_range=(1, 100), H=2)),
+    (kin.F32, 64, 32, dict(B=300, len_range=(1, 60), H=2)),
+    (kin.BF16, 32, 16, dict(B=64, T=30, H=3)),
+    (kin.F32, 128, 64, dict(B=100, T=100, H=2)),
+])
+def test_short_sequences_one_buffer_chain(dtype, d, chunk, shape):
+    """Sequences of at most two chunks on average: the inter-chunk launch takes
+    its one-buffer form, with 16- or 32-column slices (packed and equal
+    lengths, initial states); all outputs and final states against the
+    oracle."""
+    print(f"[parity] short sequences dtype={dtype} d={d} C={chunk} {shape}", flush=True)
+    w = kin.make_prefill(3000 + d + chunk, d=d, dtype=dtype, chunk_size=chunk, s0_std=0.05,
+                         **shape)
+    assert w.total_tokens <= 2 * chunk * w.num_seqs
+    o, s = _run_gpu(w)
+    _check(w, o, s)
