@@ -31,19 +31,20 @@
 // only; Ke takes e^(G_n - G) directly.
 //
 // One workgroup of 4 wavefronts per tile:
-//  1. Thread t owns 4 channels x RPT consecutive tokens.  It loads its g, q,
-//     k, v (coalesced along channels), sums g down its tokens, adds the
-//     totals of the token groups above it (LDS), forms the scaled rows in
-//     fp32, stores Qt and Ke^T straight to the workspace and stages Kt, Kh,
-//     Qt row-major in LDS.
-//  2. A and P^T tiles on the matrix cores (K = d); A (masked, beta-scaled)
-//     goes to LDS in fp32, P is produced as P^T tiles so that each lane
-//     stores 4 consecutive positions of one P row.
-//  3. Diag(beta) Kt and Diag(beta) V are staged transposed (each thread
+//  1. Thread t owns 4 channels x RPT consecutive tokens.  It loads its g
+//     rows, then q, k, v and beta (coalesced along channels), sums g down its
+//     tokens, adds the totals of the token groups above it (LDS), forms the
+//     scaled rows in fp32 and stages Kt, Kh, Qt row-major in LDS; Ke,
+//     Diag(beta) Kt and Diag(beta) V stay in registers.
+//  2. Qt leaves LDS for the workspace.  A and P^T tiles on the matrix cores
+//     (K = d); A (masked, beta-scaled) goes to LDS in fp32, P is produced as
+//     P^T tiles so that each lane stores 4 consecutive positions of one P row.
+//  3. Diag(beta) Kt, Diag(beta) V and Ke are staged transposed (each thread
 //     writes its token run of a channel at once); T = (I + A)^-1 in fp32 LDS:
 //     16 x 16 diagonal blocks by forward substitution, then the blocks below
-//     them block-row by block-row on fp32 matrix cores.
-//  4. W^T = (Diag(beta) Kt)^T T^T and U = T Diag(beta) V on the matrix cores,
+//     them on fp32 matrix cores, one block column per wave.
+//  4. Ke^T leaves LDS for the workspace.  W^T = (Diag(beta) Kt)^T T^T and
+//     U = T Diag(beta) V on the matrix cores,
 //     T rounded to the operand type; each wave reuses its T fragments for
 //     all of its tiles.
 // Every workspace tensor is written in the fragment-major, kperm-ordered
