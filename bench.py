@@ -176,6 +176,28 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+# Milliseconds of untimed whole calls that precede a workload's warmup steps.
+# After the host-side input set-up the GPU has been idle, and its clocks take
+# tens of ms of sustained load to settle: the first ~25 calls of the long
+# prefill after an idle pause run 5-20% slower than the later ones, so a
+# short warmup would time part of that ramp instead of the sustained rate.
+SETTLE_MS = 100.0
+
+
+def settle(torch, fn, ms):
+    """Runs fn() untimed until `ms` of wall time has passed, synchronizing
+    every few calls so that the wall time is GPU time; returns the count."""
+    n = 0
+    t = time.perf_counter()
+    while (time.perf_counter() - t) * 1e3 < ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def upload_prefill(torch, w):
     """Seeded host arrays -> device tensors (exact bits, no torch compute)."""
     def op(a):
@@ -214,7 +236,7 @@ def upload_prefill_raw(torch, w):
                 cu_seqlens=None, num_seqs=w.num_seqs, initial_state=None, options=opt)
 
 
-def time_prefill(torch, kda, w, steps, warmup, per_kernel=True):
+def time_prefill(torch, kda, w, steps, warmup, per_kernel=True, settle_ms=SETTLE_MS):
     """Times `steps` whole prefill calls, then each kernel separately.  The
     outputs of the last call stay in res["o"], res["final_state"]."""
     raw = isinstance(w, kin.RawPrefill)
@@ -224,6 +246,7 @@ def time_prefill(torch, kda, w, steps, warmup, per_kernel=True):
         cu_seqlens=d_in["cu_seqlens"], num_seqs=d_in["num_seqs"],
         initial_state=d_in["initial_state"], chunk_size=w.chunk_size,
         **d_in.get("options", {}))
+    settled = settle(torch, call, settle_ms)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -236,7 +259,7 @@ def time_prefill(torch, kda, w, steps, warmup, per_kernel=True):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / steps
-    res = dict(ms_per_step=ms, wall_ms_per_step=1e3 * t_wall / steps)
+    res = dict(ms_per_step=ms, wall_ms_per_step=1e3 * t_wall / steps, settle_calls=settled)
     if per_kernel:
         # the two kernels of the same call, each bracketed by events on
         # the launch stream, over the same number of passes
@@ -288,6 +311,7 @@ def prefill_report(w, res, d, E, C):
                mfma_frac_algorithmic=flops / sec / (BF16_PEAK_TFLOPS * 1e12))
     if "kernel_us" in res:
         out["kernel_us"] = res["kernel_us"]
+    out["settle_calls"] = res.get("settle_calls", 0)
     return out
 
 
@@ -371,7 +395,7 @@ def prefill_parity(w, res, ref=None):
     return out
 
 
-def time_backward(torch, kda, w, steps, warmup, d, E):
+def time_backward(torch, kda, w, steps, warmup, d, E, settle_ms=SETTLE_MS):
     """Times `steps` kda_bwd_chunked calls on workload w with d_o ~ N(0, 1)."""
     d_in = upload_prefill(torch, w)
     do, _ = kin.backward_inputs(7, w.total_tokens, w.num_heads, d, w.num_seqs, w.dtype)
@@ -380,6 +404,7 @@ def time_backward(torch, kda, w, steps, warmup, d, E):
                                d_in["beta"], d_o, cu_seqlens=d_in["cu_seqlens"],
                                num_seqs=d_in["num_seqs"], initial_state=d_in["initial_state"],
                                chunk_size=w.chunk_size)
+    settle(torch, call, settle_ms)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -483,7 +508,7 @@ def decode_sample(B, H, n=64):
             np.array([(7 * i + 3) % H for i in range(n)]))
 
 
-def time_decode(torch, kda, cfg, n_steps, warmup):
+def time_decode(torch, kda, cfg, n_steps, warmup, settle_ms=SETTLE_MS):
     B, H, d = cfg["batch"], cfg["H"], cfg["d"]
     t = time.perf_counter()
     sample = decode_sample(B, H)
@@ -495,6 +520,12 @@ def time_decode(torch, kda, cfg, n_steps, warmup):
     o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda")
     calls = [kda.bind_decode(q[s], k[s], v[s], g[s], be[s], state, out=o)[0]
              for s in range(n_steps)]
+    nxt = [0]
+
+    def one_step():  # the steps in turn; the state is reset below
+        calls[nxt[0] % n_steps]()
+        nxt[0] += 1
+    settle(torch, one_step, settle_ms)
     for s in range(min(warmup, n_steps)):
         calls[s]()
     state.copy_(st0)
@@ -647,6 +678,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed whole calls for this many ms before each workload's "
+                         "warmup steps, so that the GPU clocks have settled under load")
     ap.add_argument("--extra", default="prefill,varlen,raw,bwd,decode",
                     help="comma list of workloads besides the headline (prefill, varlen, raw, "
                          "bwd, decode) or 'none'")
@@ -692,7 +726,7 @@ def main():
             w = kin.raw_prefill_workload() if idx == "raw" else kin.workload(idx)
             steps = args.steps if name in ("long", "prefill", "raw") else min(args.steps, 20)
             log(f"  {args.warmup} warmup + {steps} timed calls")
-            r = time_prefill(torch, kda, w, steps, args.warmup)
+            r = time_prefill(torch, kda, w, steps, args.warmup, settle_ms=args.settle_ms)
             rep = prefill_report(w, r, d, E, C)
             rep["roofline"] = call_roofline(rname, w, r, d, E, C)
             if name == "varlen":
@@ -714,7 +748,7 @@ def main():
             log("backward of the B=2 H=8 T=2048 prefill")
             w = kin.workload(1)
             rep, got, do = time_backward(torch, kda, w, min(args.steps, 20),
-                                         min(args.warmup, 3), d, E)
+                                         min(args.warmup, 3), d, E, settle_ms=args.settle_ms)
             workloads["backward"] = rep
             if not args.no_cpu:
                 parity["backward"] = backward_parity(w, got, do)
@@ -725,7 +759,7 @@ def main():
             cfg4 = kin.WORKLOADS[4]
             log(f"decode batch 256 H=32: {args.decode_steps} steps")
             rep, got, host, st_smp = time_decode(torch, kda, cfg4, args.decode_steps,
-                                                 min(args.warmup, 50))
+                                                 min(args.warmup, 50), settle_ms=args.settle_ms)
             workloads["decode"] = rep
             log(f"  {rep['steps_per_s']:.0f} steps/s, {rep['roofline']['achieved']:.0f} GB/s")
             if not args.no_cpu:
@@ -764,6 +798,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
