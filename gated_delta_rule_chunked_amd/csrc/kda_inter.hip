@@ -99,6 +99,16 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 
   __shared__ V4 sS[CT][NCB][64];     // S (operand type), one output tile per channel block
   __shared__ V4 sU[CT][2 * KC][64];  // Unew (operand type), one tile per token block
+  // Wide output stores (WIDE_O): each wave turns its 16 output rows into
+  // 16-byte row pieces through LDS.  The direct form stores 4 CT narrow
+  // pieces per lane and step, and every store counts against the wave's
+  // 63 outstanding vector-memory operations, which the operand ring needs:
+  // at 64-column slices a step would hold 35 of them.  16-column slices of
+  // the ring (4 stores per step) keep the direct form, measured no slower.
+  constexpr bool WIDE_O = CT >= 2 || PF == 1;
+  constexpr int OW = 16 * CT, PE = 16 / (int)sizeof(T), LDO = OW + PE;
+  constexpr int PPR = OW / PE, WP = 16 * PPR, WPL = (WP + 63) / 64;
+  __shared__ __align__(16) T sO[WIDE_O ? C : 1][LDO];
 
   if (inputs_rejected(in)) return;
   const int b = blockIdx.x;
@@ -319,18 +329,38 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
         // "+ 0" makes it a real VALU read also when T is fp32
         ov[t] = vec4_from_f32<T>(oc + 0.f);
       }
-      T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
-      if (FULL || rows == C) {
+      if constexpr (WIDE_O) {
+        // the wave's rows only, so no other wave takes part: LDS operations
+        // of one wave complete in order
 #pragma unroll
         for (int t = 0; t < CT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) op[i * rs + 16 * t] = ov[t][i];
+          for (int i = 0; i < 4; ++i) sO[16 * rb + 4 * lg + i][16 * t + lr] = ov[t][i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < WPL; ++p) {
+          const int e = lane + 64 * p;
+          if (WP % 64 == 0 || e < WP) {
+            const int row = 16 * rb + e / PPR, c = (e % PPR) * PE;
+            if (FULL || row < rows)
+              *reinterpret_cast<uint4 *>(o + (int64_t)(tc + row) * rs + (int64_t)h * D + col0 +
+                                         c) = *reinterpret_cast<const uint4 *>(&sO[row][c]);
+          }
+        }
       } else {
+        T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
+        if (FULL || rows == C) {
 #pragma unroll
-        for (int t = 0; t < CT; ++t)
+          for (int t = 0; t < CT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * rb + 4 * lg + i < rows) op[i * rs + 16 * t] = ov[t][i];
+            for (int i = 0; i < 4; ++i) op[i * rs + 16 * t] = ov[t][i];
+        } else {
+#pragma unroll
+          for (int t = 0; t < CT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * rb + 4 * lg + i < rows) op[i * rs + 16 * t] = ov[t][i];
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
