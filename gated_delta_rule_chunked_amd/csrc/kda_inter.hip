@@ -97,7 +97,15 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   constexpr int NRB = C / 16, NCB = Ops::NCB, CK = Ops::CK, KD = Ops::KD, KC = Ops::KC;
   constexpr int CBW = Ops::CBW, NS = D / (16 * CT);
 
-  __shared__ V4 sS[CT][NCB][64];     // S (operand type), one output tile per channel block
+  // S (operand type), one output tile per channel block.  The one-buffer
+  // form (RE_S) keeps two copies, the chunk's entering S and the updated one,
+  // and its output product reads S again from LDS instead of holding it in
+  // registers through the step: 20 registers fewer at 16-column slices,
+  // which lets four workgroups share a CU instead of three (1,100 short
+  // sequences: 967 -> 873 us).  The ring keeps S in registers, measured
+  // faster there (less LDS traffic on its longer steps).
+  constexpr bool RE_S = PF == 1;
+  __shared__ V4 sS[RE_S ? 2 : 1][CT][NCB][64];
   __shared__ V4 sU[CT][2 * KC][64];  // Unew (operand type), one tile per token block
   // Wide output stores (WIDE_O): each wave turns its 16 output rows into
   // 16-byte row pieces through LDS.  The direct form stores 4 CT narrow
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
           for (int i = 0; i < 4; ++i)
             x[i] = s0[sbase + 16 * t + (int64_t)(16 * cb + 4 * lg + i) * D];
         }
-        sS[t][cb][lane] = vec4_from_f32<T>(x);
+        sS[0][t][cb][lane] = vec4_from_f32<T>(x);
       }
       S[j][t] = x;
     }
@@ -257,12 +265,15 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     const int rows = FULL ? C : min(C, len - ci * C);
 
     // S entering the chunk, as K-step operands over channels, per column tile
+    const int cur = RE_S ? (ci & 1) : 0;
+    auto s_operand = [&](int t, int ks) {
+      return join4(sS[cur][t][2 * ks][lane], sS[cur][t][2 * ks + 1][lane]);
+    };
     F sb[CT][KD];
 #pragma unroll
     for (int t = 0; t < CT; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks)
-        sb[t][ks] = join4(sS[t][2 * ks][lane], sS[t][2 * ks + 1][lane]);
+      for (int ks = 0; ks < KD; ++ks) sb[t][ks] = s_operand(t, ks);
 
     // Unew = U - W S for the wave's token block (two accumulators per tile)
     if (has_rb) {
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 #pragma unroll
           for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[t][ks], acc);
           S[j][t] = acc;
-          sS[t][cb][lane] = vec4_from_f32<T>(acc);
+          sS[RE_S ? cur ^ 1 : 0][t][cb][lane] = vec4_from_f32<T>(acc);
         }
       }
     }
@@ -321,7 +332,8 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
       for (int t = 0; t < CT; ++t) {
         f32x4 oc = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[t][ks], oc);
+        for (int ks = 0; ks < KD; ++ks)
+          oc = mma_k32(B.qA[ks], RE_S ? s_operand(t, ks) : sb[t][ks], oc);
 #pragma unroll
         for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[t][ks], oc);
         // read (and convert) before any branch: matrix-core results are read
@@ -478,10 +490,12 @@ static hipError_t launch_inter_ct(const FwdArgs &a) {
 //
 // Sequences of at most two chunks on average (many short prompts) take the
 // one-buffer form: no operand ring fills on them, and its lower register
-// count runs two or three workgroups per CU where the ring allows one.  Their
-// slices stay at most 32 columns wide, since 64-column slices keep one
-// workgroup per CU in either form.  Measured on 1,100 packed sequences of
-// 1-100 tokens, 16 heads: 1,310 -> 986 us; on longer chains the ring wins.
+// count (bf16, d = 128: 128 at 16-column and 166 at 32-column slices) runs
+// four or three workgroups per CU where the ring allows one.  Their slices
+// stay at most 32 columns wide, since 64-column slices keep one workgroup
+// per CU in either form.  Measured on 1,100 packed sequences of 1-100
+// tokens, 16 heads: 1,310 us with the ring, 873 us in this form; on longer
+// chains the ring wins.
 template <typename T, int D, int C>
 static hipError_t launch_inter_c(const FwdArgs &a) {
   constexpr int MAX_CT = (sizeof(T) == 4 && D == 128) ? 1 : (D >= 64 ? 4 : 2);
