@@ -114,9 +114,17 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   // at 64-column slices a step would hold 35 of them.  16-column slices of
   // the ring (4 stores per step) keep the direct form, measured no slower.
   constexpr bool WIDE_O = CT >= 2 || PF == 1;
+  // Deferred output stores (DEFER_O), for 16-column slices of the ring
+  // without warm-up loads (short and mid-length chains): the waves leave
+  // their rows in LDS, and after the step's last barrier the whole tile goes
+  // out as 16-byte row pieces at the top of the next step, off the output
+  // product's path.  B=2 H=8 T=2048: chain 25.8 -> 25.4 us; B=1 H=32 T=4096:
+  // 49.8 -> 48.8 us.  With warm-up loads (long chains) it was 9% slower.
+  constexpr bool DEFER_O = CT == 1 && PF == 3 && !WARM;
   constexpr int OW = 16 * CT, PE = 16 / (int)sizeof(T), LDO = OW + PE;
   constexpr int PPR = OW / PE, WP = 16 * PPR, WPL = (WP + 63) / 64;
-  __shared__ __align__(16) T sO[WIDE_O ? C : 1][LDO];
+  constexpr int NPC = C * PPR, PPT = (NPC + 255) / 256;  // pieces of the tile, per thread
+  __shared__ __align__(16) T sO[(WIDE_O || DEFER_O) ? C : 1][LDO];
 
   if (inputs_rejected(in)) return;
   const int b = blockIdx.x;
@@ -258,11 +266,30 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
 
   // FULL: a chunk of C rows (every chunk but a sequence's last), whose o
   // stores need no row mask.
+  // DEFER_O: the previous step's output tile, from LDS to o
+  int prev_tc = 0, prev_rows = 0;
+  auto flush_o = [&]() {
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int e = tid + 256 * p;
+      if (NPC % 256 == 0 || e < NPC) {
+        const int r = e / PPR, c = (e % PPR) * PE;
+        if (r < prev_rows)
+          *reinterpret_cast<uint4 *>(o + (int64_t)(prev_tc + r) * rs + (int64_t)h * D + col0 + c) =
+              *reinterpret_cast<const uint4 *>(&sO[r][c]);
+      }
+    }
+  };
   auto step = [&](Buf &B, int ci, auto full) {
     constexpr bool FULL = decltype(full)::value;
     const int nxt = min(ci + PF, nch - 1);
     const int tc = t0 + ci * C;
     const int rows = FULL ? C : min(C, len - ci * C);
+    if constexpr (DEFER_O) {  // the last step's barrier made its rows visible
+      flush_o();
+      prev_tc = tc;
+      prev_rows = rows;
+    }
 
     // S entering the chunk, as K-step operands over channels, per column tile
     const int cur = RE_S ? (ci & 1) : 0;
@@ -359,6 +386,11 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
                                          c) = *reinterpret_cast<const uint4 *>(&sO[row][c]);
           }
         }
+      } else if constexpr (DEFER_O) {
+        // rewritten only after this step's first barrier, which every
+        // wave passes after its flush of the previous tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sO[16 * rb + 4 * lg + i][lr] = ov[0][i];
       } else {
         T *op = o + (int64_t)(tc + 16 * rb + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
         if (FULL || rows == C) {
@@ -435,6 +467,7 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
     }
   }
 
+  if constexpr (DEFER_O) flush_o();  // the last chunk's tile
   if (s_final && has_state) {
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
