@@ -15,15 +15,16 @@
 //
 // Every product multiplies S from the left, so the d_v columns of S evolve
 // independently: a workgroup owns one (sequence, head, column slice of 16,
-// 32 or 64 columns) and walks that sequence's chunks.  Its four wavefronts split the rows: wave w
-// computes token block w of Unew and O and channel blocks w*CBW.. of S, so
-// all four SIMDs issue matrix-core work and each wave loads only its quarter
-// of W, Qt, P and Ke.  The blocks meet through two tiny LDS exchanges per
-// chunk (Unew after its product, S after the update), each a plain lane-for-
-// lane copy: the intra-chunk kernel stores W, Qt (channels) and Ke^T, P
-// (tokens) with their contraction index in the kperm order of
-// kda_common.hpp, in which a 16x16 output tile held by one wave is already
-// half of another wave's K-step operand.  The fp32 state stays in registers.
+// 32 or 64 columns) and walks that sequence's chunks.  Its four wavefronts
+// split the rows: wave w computes token block w of Unew and O and channel
+// blocks w*CBW.. of S, so all four SIMDs issue matrix-core work and each
+// wave loads only its quarter of W, Qt, P and Ke.  The blocks meet through
+// two tiny LDS exchanges per chunk (Unew after its product, S after the
+// update), each a plain lane-for-lane copy: the intra-chunk kernel stores W,
+// Qt (channels) and Ke^T, P (tokens) with their contraction index in the
+// kperm order of kda_common.hpp, in which a 16x16 output tile held by one
+// wave is already half of another wave's K-step operand.  The fp32 state
+// stays in registers.
 //
 // The intra-chunk kernel stores all of these operands fragment-major
 // (frag_off / tile_off), so every load below is one contiguous run per wave.
@@ -35,6 +36,12 @@
 // and fenced with scheduling barriers so the compiler keeps them in place.
 // Workgroups of one (sequence, head) share blockIdx % 8 and therefore one
 // XCD and its L2, which serves the same W/Qt/Ke/P rows to all slices.
+// The output tile leaves in one of three forms (WIDE_O, DEFER_O below):
+// 16-byte row pieces of each wave's rows through LDS on wider slices and in
+// the one-buffer form; 16-byte row pieces of the whole tile, deferred to
+// the top of the next step, on the other 16-column ring slices without
+// warm-up loads; two-byte stores straight from the output tiles on the
+// long chains that take warm-up loads.
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
