@@ -442,7 +442,14 @@ __global__ __launch_bounds__((IntraCfg<T, D, C>::NT)) void intra_chunk_kernel(
       accP0[i] = (32 * m + 4 * lg + i <= prow) ? accP0[i] : 0.f;
       accP1[i] = (32 * m + 16 + 4 * lg + i <= prow) ? accP1[i] : 0.f;
     }
-    store8_f32<T>(p_tile + frag_off(prow, 32 * m + 8 * lg, CK), accP0, accP1);
+    // A pair of key blocks that starts past the token block's last row is
+    // zero; the inter-chunk kernel never loads it, so it is not stored
+    // (a quarter of P's bytes when C = 64).  The empty asm makes the masked
+    // results exist before the branch, so the compiler cannot move the reads
+    // of the matrix-core registers behind it.
+    asm volatile("" ::"v"(accP0), "v"(accP1));
+    if (32 * m <= 16 * rb + 15)
+      store8_f32<T>(p_tile + frag_off(prow, 32 * m + 8 * lg, CK), accP0, accP1);
   }
   };
   if constexpr (NRB > 1) {
