@@ -9,8 +9,8 @@
 // its device address is looked up once per device with hipGetSymbolAddress
 // (that device current) and only that address is ever passed to a kernel.
 // Calls on one GPU share its array, so calls that overlap on one GPU race;
-// the prefill writes every workspace byte it reads within the call, so the
-// previous call's contents need no clearing.
+// the prefill writes every workspace value it uses within the call before
+// using it, so the previous call's contents need no clearing.
 #include <atomic>
 #include <hip/hip_runtime.h>
 

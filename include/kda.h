@@ -322,8 +322,8 @@ kda_status kda_decode_step_ex(const kda_options *options, const void *q, const v
  *   errors are kda_fwd_chunked's.
  *   Calls on one GPU share its array: calls that overlap on one GPU (several
  *   streams or host threads at once) race and must be serialised by the
- *   caller.  Each call writes every workspace byte it reads, so nothing
- *   left by an earlier call is used.
+ *   caller.  Each call writes every workspace value it uses before using
+ *   it, so nothing left by an earlier call affects the results.
  */
 #define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
