@@ -474,6 +474,14 @@ __device__ __forceinline__ void row_dots(float *out, const float *X, const float
   __syncthreads();
 }
 
+// Rounds four fp32 values to bf16 (round to nearest even).
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
+  return r;
+}
+
 struct TilePtr {
   float *kt, *kh, *qt, *ke, *w, *u, *vr, *gc, *tm, *pm, *mm, *gam, *bt, *px, *qy;
 };
@@ -558,6 +566,10 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
   }
   for (int r = tid; r < C; r += NT) p.bt[r] = r < n ? beta[(int64_t)(t0 + r) * H + h] : 0.f;
   __syncthreads();
+  // For bf16 inputs Ke is needed only as the chains' bf16 copies, so its
+  // row-major copy is written here (after T Diag(beta) in the scratch) and
+  // no fp32 Ke is stored.
+  bf16 *keb = reinterpret_cast<bf16 *>(tb + C * C) + C * D;
   for (int e4 = tid; e4 < C * D / 4; e4 += NT) {
     const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
     const float live = r < n ? 1.f : 0.f;
@@ -578,7 +590,10 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
     *reinterpret_cast<f32x4 *>(p.kt + e) = kv * eg;
     *reinterpret_cast<f32x4 *>(p.kh + e) = kv * emg;
     *reinterpret_cast<f32x4 *>(p.qt + e) = qv * eg;
-    *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<bf16x4 *>(keb + e) = to_bf16x4(kv * egn);
+    else
+      *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
     *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
     *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
@@ -637,17 +652,21 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
       const int c4 = 4 * (e % (D / 4)), r8 = 8 * (e / (D / 4));
 #pragma unroll
       for (int mtx = 0; mtx < 2; ++mtx) {
-        const float *src = mtx == 0 ? p.w : p.ke;
         bf16 *dst = wb + mtx * C * D;
         f32x4 x[8];
+        if (mtx == 0) {  // W: fp32 rows, rounded here
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const f32x4 *>(src + (r8 + i) * D + c4);
+          for (int i = 0; i < 8; ++i)
+            x[i] = *reinterpret_cast<const f32x4 *>(p.w + (r8 + i) * D + c4);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          bf16x4 b4;
+          for (int i = 0; i < 8; ++i) *reinterpret_cast<bf16x4 *>(dst + (r8 + i) * D + c4) = to_bf16x4(x[i]);
+        } else {  // Ke: its bf16 rows, written in the element-wise pass
 #pragma unroll
-          for (int u = 0; u < 4; ++u) b4[u] = (bf16)x[i][u];
-          *reinterpret_cast<bf16x4 *>(dst + (r8 + i) * D + c4) = b4;
+          for (int i = 0; i < 8; ++i) {
+            const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(dst + (r8 + i) * D + c4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[i][u] = (float)b4[u];
+          }
         }
         if constexpr (C >= 32) {
           bf16 *dt = wb + (2 + mtx) * C * D;  // [D][C]
@@ -804,13 +823,6 @@ struct StageB {
     }
   }
 };
-
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) {
-  bf16x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (bf16)v[i];
-  return r;
-}
 
 // ---- 2. chunk start states ------------------------------------------------
 // One block per (sequence, head, 16-column slice); each chunk's W and Ke are
