@@ -24,9 +24,11 @@
 //   dG = dKt*Kt - dKh*Kh + dQt*Qt - dKe*Ke, dG_n = colsum(dKe*Ke) + dgam*gam,
 //   dg_s = sum_{r >= s} dG_r + dG_n.
 //
-// Three or four launches, all in fp32 over a per-tile fp32 workspace
-// (BwdLayout), each instantiated per (head dim d, chunk C) so that every loop
-// bound and register block is a compile-time constant:
+// Three or four launches over a per-tile fp32 workspace (BwdLayout; with
+// bf16 inputs and C >= 32 the chunk states and state gradients are stored in
+// bf16, as the products that read them round them), each instantiated per
+// (head dim d, chunk C) so that every loop bound and register block is a
+// compile-time constant:
 //   bwd_prep_kernel   per (chunk, head): G, Kt, Kh, Qt, Ke, gam, M, P, T, W, U,
 //                     and the chain-independent terms X = P^T dO, Y = Qt^T dO
 //   bwd_state_kernel  per (sequence, head, 16-column slice): chunk start states
@@ -44,6 +46,8 @@
 // 16-byte loads, the next slice in flight while the current one is used),
 // the two chains on chunk operands staged whole in LDS, the next chunk's
 // being loaded into registers while the current one is computed.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_internal.hpp"
 
@@ -107,9 +111,19 @@ constexpr int mm_lds() {
 // 32: each K slice of 32 is rounded to bf16 as it is staged (rows of stride
 // 40, 4 banks apart over 8 rows), and a 16 x 16 tile takes one
 // v_mfma_f32_16x16x32_bf16 per slice.  Accumulation stays fp32.
-template <int M, int N, int K, int NA, int NT, int CAP>
-__device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *const *A, int lda,
-                                                 const float *B, int ldb, float (&lds)[CAP]) {
+// Four consecutive operand values as fp32, from fp32 or bf16 storage.
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 ld4(const bf16 *p) {
+  const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+  f32x4 r;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r[u] = (float)b[u];
+  return r;
+}
+
+template <int M, int N, int K, int NA, int NT, int CAP, typename AT, typename BT>
+__device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const AT *const *A, int lda,
+                                                 const BT *B, int ldb, float (&lds)[CAP]) {
   constexpr int NW = NT / 64;
   static_assert(K % 32 == 0, "contraction");
   constexpr int KB = 32, LB = KB + 8;
@@ -129,13 +143,13 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *c
     for (int p = 0; p < QA; ++p) {
       const int f = tid + NT * p;
       if (GA % NT == 0 || f < GA)
-        ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + (f / 8) * lda + k0 + 4 * (f % 8));
+        ra[a][p] = ld4(A[a] + (f / 8) * lda + k0 + 4 * (f % 8));
     }
 #pragma unroll
     for (int p = 0; p < QB; ++p) {
       const int f = tid + NT * p;
       if (GB % NT == 0 || f < GB)
-        rb[p] = *reinterpret_cast<const f32x4 *>(B + (f / 8) * ldb + k0 + 4 * (f % 8));
+        rb[p] = ld4(B + (f / 8) * ldb + k0 + 4 * (f % 8));
     }
   };
   auto cvt = [](f32x4 v) {
@@ -201,9 +215,10 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const float *c
   }
 }
 
-template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int NT = 256, int CAP>
-__device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *const *A, int lda,
-                                                const float *B, int ldb, float (&lds)[CAP]) {
+template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int NT = 256, int CAP,
+          typename AT, typename BT>
+__device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const AT *const *A, int lda,
+                                                const BT *B, int ldb, float (&lds)[CAP]) {
   constexpr int NW = NT / 64;
   static_assert(K % 16 == 0, "contraction");
   if constexpr (BF && !TA && TB && K % 32 == 0) {
@@ -233,10 +248,10 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
       if (FA % NT == 0 || f < FA) {
         if (TA) {
           const int kk = f / (M / 4), i4 = f % (M / 4);
-          ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + (k0 + kk) * lda + 4 * i4);
+          ra[a][p] = ld4(A[a] + (k0 + kk) * lda + 4 * i4);
         } else {
           const int i = f / (KS / 4), k4 = f % (KS / 4);
-          ra[a][p] = *reinterpret_cast<const f32x4 *>(A[a] + i * lda + k0 + 4 * k4);
+          ra[a][p] = ld4(A[a] + i * lda + k0 + 4 * k4);
         }
       }
     }
@@ -246,10 +261,10 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
       if (FB % NT == 0 || f < FB) {
         if (TB) {
           const int j = f / (KS / 4), k4 = f % (KS / 4);
-          rb[p] = *reinterpret_cast<const f32x4 *>(B + j * ldb + k0 + 4 * k4);
+          rb[p] = ld4(B + j * ldb + k0 + 4 * k4);
         } else {
           const int kk = f / (N / 4), j4 = f % (N / 4);
-          rb[p] = *reinterpret_cast<const f32x4 *>(B + (k0 + kk) * ldb + 4 * j4);
+          rb[p] = ld4(B + (k0 + kk) * ldb + 4 * j4);
         }
       }
     }
@@ -350,11 +365,12 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const float *co
 }
 
 // c[q] += the wave's tiles of A B (one left operand), as above.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
-__device__ __forceinline__ void mm_accumulate(f32x4 *c, const float *A, int lda, const float *B,
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
+          typename AT, typename BT>
+__device__ __forceinline__ void mm_accumulate(f32x4 *c, const AT *A, int lda, const BT *B,
                                               int ldb, float (&lds)[CAP]) {
   f32x4 *const cs[1] = {c};
-  const float *const as[1] = {A};
+  const AT *const as[1] = {A};
   mm_accumulate_n<M, N, K, TA, TB, 1, BF, NT>(cs, as, lda, B, ldb, lds);
 }
 
@@ -386,9 +402,10 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
 
 // out = alpha A B (+ out when acc).  `lds` holds at least mm_lds<M, N, K>()
 // floats.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
-__device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, int lda,
-                                         const float *B, int ldb, float alpha, bool acc,
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
+          typename AT, typename BT>
+__device__ __forceinline__ void block_mm(float *out, int ldo, const AT *A, int lda,
+                                         const BT *B, int ldb, float alpha, bool acc,
                                          float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
@@ -398,9 +415,10 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const float *A, in
 }
 
 // out = init + alpha A B (init has leading dimension ldo).
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
+          typename AT, typename BT>
 __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
-                                              const float *A, int lda, const float *B, int ldb,
+                                              const AT *A, int lda, const BT *B, int ldb,
                                               float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
@@ -411,10 +429,10 @@ __device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *
 
 // out = A1 B1 + A2 B2, both products accumulated in registers.
 template <int M, int N, int K1, bool TA1, bool TB1, int K2, bool TA2, bool TB2, bool BF = false,
-          int NT = 256, int CAP>
-__device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, int lda1,
-                                          const float *B1, int ldb1, const float *A2, int lda2,
-                                          const float *B2, int ldb2, float (&lds)[CAP]) {
+          int NT = 256, int CAP, typename A1T, typename B1T, typename A2T, typename B2T>
+__device__ __forceinline__ void block_mm2(float *out, int ldo, const A1T *A1, int lda1,
+                                          const B1T *B1, int ldb1, const A2T *A2, int lda2,
+                                          const B2T *B2, int ldb2, float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N, NT>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c[q] = zero4();
@@ -425,15 +443,16 @@ __device__ __forceinline__ void block_mm2(float *out, int ldo, const float *A1, 
 
 // out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
 // dimension), staging B once.
-template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP>
-__device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const float *A1,
-                                              const float *A2, int lda, const float *B, int ldb,
+template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
+          typename AT, typename BT>
+__device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const AT *A1,
+                                              const AT *A2, int lda, const BT *B, int ldb,
                                               float (&lds)[CAP]) {
   f32x4 c1[MmTiles<M, N, NT>::TPW], c2[MmTiles<M, N, NT>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c1[q] = c2[q] = zero4();
   f32x4 *const cs[2] = {c1, c2};
-  const float *const as[2] = {A1, A2};
+  const AT *const as[2] = {A1, A2};
   mm_accumulate_n<M, N, K, TA, TB, 2, BF, NT>(cs, as, lda, B, ldb, lds);
   mm_store<M, N, NT>(out1, ldo, nullptr, 1.f, c1);
   mm_store<M, N, NT>(out2, ldo, nullptr, 1.f, c2);
@@ -444,9 +463,8 @@ __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo,
 // TPR consecutive threads share a row, each reading float4s part, part +
 // TPR, ...; a thread's rows are r0, r0 + NT / TPR, ..., all loaded before
 // any of the sums is reduced.  Ends with a barrier.
-template <int R, int L, int NT = 256>
-__device__ __forceinline__ void row_dots(float *out, const float *X, const float *Y, int ld,
-                                         bool acc) {
+template <int R, int L, int NT = 256, typename XT, typename YT>
+__device__ __forceinline__ void row_dots(float *out, const XT *X, const YT *Y, int ld, bool acc) {
   constexpr int TPR = L / 4 < 16 ? L / 4 : 16;  // threads per row
   constexpr int V = L / (4 * TPR);              // float4 per thread and row
   constexpr int RPP = NT / TPR;                 // rows per pass of the block
@@ -460,8 +478,8 @@ __device__ __forceinline__ void row_dots(float *out, const float *X, const float
     s[pp] = 0.f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(X + r * ld + 4 * (part + TPR * v));
-      const f32x4 y = *reinterpret_cast<const f32x4 *>(Y + r * ld + 4 * (part + TPR * v));
+      const f32x4 x = ld4(X + r * ld + 4 * (part + TPR * v));
+      const f32x4 y = ld4(Y + r * ld + 4 * (part + TPR * v));
       s[pp] += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
     }
   }
@@ -1087,10 +1105,27 @@ __device__ __forceinline__ void dstate_chain(int b, const int *__restrict__ cu, 
 // Same walks, grids and outputs as above, for bf16 inputs with C >= 32.  The
 // chains stage W (or Ke) row-major and Ke^T (or W^T) as bf16, and round the
 // state (or state gradient) and the Unew (or dUnew) tile to bf16 where they
-// enter a product, as the forward's chain rounds its state.  The state, its
-// gradient and every stored result stay fp32.  Each product is D / 32 or
+// enter a product, as the forward's chain rounds its state.  The state and
+// its gradient are carried in fp32; what they store per chunk for the
+// gradient kernel is that bf16 rounding (16-byte row pieces from the LDS
+// operand copy), and dUnew is stored in fp32.  Each product is D / 32 or
 // C / 32 steps of v_mfma_f32_16x16x32_bf16 per 16 x 16 tile, where the fp32
 // form needs eight times as many fp32 instructions of twice the cycles.
+// Rows 0 .. R-1, columns col0 .. col0 + 15 of a row-major bf16 matrix (row
+// stride ld), from their transposed copy in LDS (tr[c][r] at tr + c * ldt + r):
+// two 16-byte row pieces per row, one per thread.
+template <int R>
+__device__ __forceinline__ void store_rows_bf16(bf16 *dst, int ld, int col0, const bf16 *tr,
+                                                int ldt) {
+  for (int e = threadIdx.x; e < 2 * R; e += NTC) {
+    const int r = e >> 1, c8 = 8 * (e & 1);
+    bf16x8 v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = tr[(c8 + u) * ldt + r];
+    *reinterpret_cast<bf16x8 *>(dst + (int64_t)r * ld + col0 + c8) = v;
+  }
+}
+
 template <int D, int C>
 __device__ __forceinline__ void state_chain_bf(int b, const int *__restrict__ cu, int N, int H,
                                                int seq_len, const float *__restrict__ s0,
@@ -1149,18 +1184,15 @@ __device__ __forceinline__ void state_chain_bf(int b, const int *__restrict__ cu
   };
   auto step = [&](Buf &B, int ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
-    float *sc = reinterpret_cast<float *>(ws + L.sc) + tile * D * D;
+    bf16 *sc = reinterpret_cast<bf16 *>(ws + L.sc) + tile * D * D;
     __syncthreads();  // the previous chunk is done with the LDS operands
     B.w.store(sW);
     B.k.store(sKT);
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
-      if (cb < NCB) {
+      if (cb < NCB)
         *reinterpret_cast<bf16x4 *>(sSt + lr * LB + 16 * cb + 4 * lg) = to_bf16x4(S[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[(16 * cb + 4 * lg + i) * D + col0 + lr] = S[j][i];
-      }
     }
     const f32x4 u0 = B.u;
     f32x4 gam[CBW];
@@ -1168,6 +1200,7 @@ __device__ __forceinline__ void state_chain_bf(int b, const int *__restrict__ cu
     for (int j = 0; j < CBW; ++j) gam[j] = B.g[j];
     __syncthreads();
     fetch(B, ci + 2);
+    store_rows_bf16<D>(sc, D, col0, sSt, LB);  // the chunk's start state, as the products use it
     // Unew = U - W S for the wave's token block
     if (has_rb) {
       f32x4 a0 = zero4();
@@ -1262,7 +1295,7 @@ __device__ __forceinline__ void dstate_chain_bf(int b, const int *__restrict__ c
   };
   auto step = [&](Buf &B, int ci) {
     const int64_t tile = (int64_t)(first + ci) * H + h;
-    float *dse = reinterpret_cast<float *>(ws + L.dse) + tile * D * D;
+    bf16 *dse = reinterpret_cast<bf16 *>(ws + L.dse) + tile * D * D;
     float *dun = reinterpret_cast<float *>(ws + L.dun) + tile * C * D;
     __syncthreads();  // the previous chunk is done with the LDS operands
     B.k.store(sK);
@@ -1270,11 +1303,8 @@ __device__ __forceinline__ void dstate_chain_bf(int b, const int *__restrict__ c
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
       const int cb = wv * CBW + j;
-      if (cb < NCB) {
+      if (cb < NCB)
         *reinterpret_cast<bf16x4 *>(sDt + lr * LB + 16 * cb + 4 * lg) = to_bf16x4(dS[j]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dse[(16 * cb + 4 * lg + i) * D + col0 + lr] = dS[j][i];
-      }
     }
     const f32x4 x0 = B.x;
     f32x4 gam[CBW], y0[CBW];
@@ -1285,6 +1315,7 @@ __device__ __forceinline__ void dstate_chain_bf(int b, const int *__restrict__ c
     }
     __syncthreads();
     fetch(B, ci - 2);
+    store_rows_bf16<D>(dse, D, col0, sDt, LB);  // the state gradient after the chunk
     // dUnew = P^T dO + Ke dS_next for the wave's token block
     if (has_rb) {
       f32x4 a0 = zero4();
@@ -1428,8 +1459,12 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   if (n == 0) return;
   const int64_t tile = (int64_t)c * H + h;
   const TilePtr p = tile_ptrs(L, ws, tile, C, D);
-  const float *sc = reinterpret_cast<const float *>(ws + L.sc) + tile * D * D;
-  const float *dse = reinterpret_cast<const float *>(ws + L.dse) + tile * D * D;
+  // chunk start states and state gradients: bf16 where the chains run on
+  // the bf16 matrix cores (rounded as their products use them), else fp32.
+  // dUnew stays fp32: dv = Diag(beta) T^T dUnew sums it with cancellation.
+  using ST = typename std::conditional<chain_bf16<C, T>(), bf16, float>::type;
+  const ST *sc = reinterpret_cast<const ST *>(ws + L.sc) + tile * D * D;
+  const ST *dse = reinterpret_cast<const ST *>(ws + L.dse) + tile * D * D;
   const float *dun = reinterpret_cast<const float *>(ws + L.dun) + tile * CD;
   float *x = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
   float *unew = x, *dot = x + CD, *dqt = x + 2 * CD, *dke = x + 3 * CD, *dw = x + 4 * CD;

@@ -112,9 +112,10 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
-// Backward workspace (kda_bwd_chunked), fp32 throughout, per (chunk, head)
-// tile: the recomputed chunk factors (row-major [C][D] or [C][C]), the chunk
-// start state and the gradient of the state after the chunk ([D][D]), the
+// Backward workspace (kda_bwd_chunked), fp32, per (chunk, head) tile: the
+// recomputed chunk factors (row-major [C][D] or [C][C]), the chunk start
+// state and the gradient of the state after the chunk ([D][D]; bf16 in the
+// first half of their slots for bf16 inputs with C >= 32), the
 // gradient of U - W S ([C][D]) and the per-tile scratch of the gradient
 // kernel; seq_first [num_seqs] as in the forward.
 struct BwdLayout {
