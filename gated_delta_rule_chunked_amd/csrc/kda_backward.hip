@@ -375,9 +375,9 @@ __device__ __forceinline__ void mm_accumulate(f32x4 *c, const AT *A, int lda, co
 }
 
 // out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
-// leading dimension ldo for both).  Ends with a barrier.
-template <int M, int N, int NT = 256>
-__device__ __forceinline__ void mm_store(float *out, int ldo, const float *init, float alpha,
+// leading dimension ldo for both), rounded to out's type.  Ends with a barrier.
+template <int M, int N, int NT = 256, typename OT, typename IT>
+__device__ __forceinline__ void mm_store(OT *out, int ldo, const IT *init, float alpha,
                                          f32x4 *c) {
   constexpr int NW = NT / 64;
   constexpr int TN = MmTiles<M, N, NT>::TN, TT = MmTiles<M, N, NT>::TT, TPW = MmTiles<M, N, NT>::TPW;
@@ -394,7 +394,7 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
       const int at = (16 * (t / TN) + 4 * lg) * ldo + 16 * (t % TN) + lr;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        out[at + i * ldo] = alpha * c[q][i] + (init ? init[at + i * ldo] : 0.f);
+        out[at + i * ldo] = (OT)(alpha * c[q][i] + (init ? (float)init[at + i * ldo] : 0.f));
     }
   }
   __syncthreads();
@@ -403,8 +403,8 @@ __device__ __forceinline__ void mm_store(float *out, int ldo, const float *init,
 // out = alpha A B (+ out when acc).  `lds` holds at least mm_lds<M, N, K>()
 // floats.
 template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
-          typename AT, typename BT>
-__device__ __forceinline__ void block_mm(float *out, int ldo, const AT *A, int lda,
+          typename OT, typename AT, typename BT>
+__device__ __forceinline__ void block_mm(OT *out, int ldo, const AT *A, int lda,
                                          const BT *B, int ldb, float alpha, bool acc,
                                          float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N, NT>::TPW];
@@ -416,8 +416,8 @@ __device__ __forceinline__ void block_mm(float *out, int ldo, const AT *A, int l
 
 // out = init + alpha A B (init has leading dimension ldo).
 template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
-          typename AT, typename BT>
-__device__ __forceinline__ void block_mm_init(float *out, int ldo, const float *init, float alpha,
+          typename OT, typename AT, typename BT>
+__device__ __forceinline__ void block_mm_init(OT *out, int ldo, const float *init, float alpha,
                                               const AT *A, int lda, const BT *B, int ldb,
                                               float (&lds)[CAP]) {
   f32x4 c[MmTiles<M, N, NT>::TPW];
@@ -438,7 +438,7 @@ __device__ __forceinline__ void block_mm2(float *out, int ldo, const A1T *A1, in
   for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c[q] = zero4();
   mm_accumulate<M, N, K1, TA1, TB1, BF, NT>(c, A1, lda1, B1, ldb1, lds);
   mm_accumulate<M, N, K2, TA2, TB2, BF, NT>(c, A2, lda2, B2, ldb2, lds);
-  mm_store<M, N, NT>(out, ldo, nullptr, 1.f, c);
+  mm_store<M, N, NT>(out, ldo, static_cast<const float *>(nullptr), 1.f, c);
 }
 
 // out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
@@ -454,8 +454,8 @@ __device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo,
   f32x4 *const cs[2] = {c1, c2};
   const AT *const as[2] = {A1, A2};
   mm_accumulate_n<M, N, K, TA, TB, 2, BF, NT>(cs, as, lda, B, ldb, lds);
-  mm_store<M, N, NT>(out1, ldo, nullptr, 1.f, c1);
-  mm_store<M, N, NT>(out2, ldo, nullptr, 1.f, c2);
+  mm_store<M, N, NT>(out1, ldo, static_cast<const float *>(nullptr), 1.f, c1);
+  mm_store<M, N, NT>(out2, ldo, static_cast<const float *>(nullptr), 1.f, c2);
 }
 
 // out[r] = sum_j X[r][j] Y[r][j] (+ out[r] when acc) for r < R rows of
@@ -1467,15 +1467,22 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   const ST *dse = reinterpret_cast<const ST *>(ws + L.dse) + tile * D * D;
   const float *dun = reinterpret_cast<const float *>(ws + L.dun) + tile * CD;
   float *x = reinterpret_cast<float *>(ws + L.scratch) + tile * L.scratch_per_tile;
-  float *unew = x, *dot = x + CD, *dqt = x + 2 * CD, *dke = x + 3 * CD, *dw = x + 4 * CD;
+  // U - W S and the staged dO feed only bf16 products for bf16 inputs, which
+  // round them to bf16 as they stage them: stored in bf16 there (same bits)
+  using XT = typename std::conditional<sizeof(T) == 2, bf16, float>::type;
+  XT *unew = reinterpret_cast<XT *>(x), *dot = reinterpret_cast<XT *>(x + CD);
+  float *dqt = x + 2 * CD, *dke = x + 3 * CD, *dw = x + 4 * CD;
   float *dbkt = x + 5 * CD, *dbv = x + 6 * CD, *dkt = x + 7 * CD, *dkh = x + 8 * CD;
   const int tid = threadIdx.x;
   const int64_t rs = (int64_t)H * D;
   for (int e4 = tid; e4 < CD / 4; e4 += NT) {
     const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
     const float live = r < n ? 1.f : 0.f;
-    *reinterpret_cast<f32x4 *>(dot + 4 * e4) =
-        load4_f32<T>(d_o + (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i) * live;
+    const f32x4 v4 = load4_f32<T>(d_o + (int64_t)(t0 + min(r, n - 1)) * rs + (int64_t)h * D + i) * live;
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<bf16x4 *>(dot + 4 * e4) = to_bf16x4(v4);
+    else
+      *reinterpret_cast<f32x4 *>(dot + 4 * e4) = v4;
   }
   __syncthreads();
   block_mm_init<C, D, D, false, false, false, NT>(unew, D, p.u, -1.f, p.w, D, sc, D, s_mm);  // U - W S
