@@ -588,6 +588,8 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
   // row-major copy is written here (after T Diag(beta) in the scratch) and
   // no fp32 Ke is stored.
   bf16 *keb = reinterpret_cast<bf16 *>(tb + C * C) + C * D;
+  // V is kept in the input type: the copy is exact, and half the bytes for bf16
+  T *vr = reinterpret_cast<T *>(p.vr);
   for (int e4 = tid; e4 < C * D / 4; e4 += NT) {
     const int r = e4 / (D / 4), i = 4 * (e4 % (D / 4));
     const float live = r < n ? 1.f : 0.f;
@@ -612,7 +614,10 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
       *reinterpret_cast<bf16x4 *>(keb + e) = to_bf16x4(kv * egn);
     else
       *reinterpret_cast<f32x4 *>(p.ke + e) = kv * egn;
-    *reinterpret_cast<f32x4 *>(p.vr + e) = vv;
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<bf16x4 *>(vr + e) = to_bf16x4(vv);
+    else
+      *reinterpret_cast<f32x4 *>(vr + e) = vv;
     *reinterpret_cast<f32x4 *>(s_do + e) = ov;
   }
   __syncthreads();
@@ -650,7 +655,7 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_prep_kernel(
   }
   __syncthreads();
   block_mm<C, D, C, false, false, false, NT>(p.w, D, tb, C, p.kt, D, 1.f, false, s_mm);  // W = (T Diag(beta)) Kt
-  block_mm<C, D, C, false, false, false, NT>(p.u, D, tb, C, p.vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
+  block_mm<C, D, C, false, false, false, NT>(p.u, D, tb, C, vr, D, 1.f, false, s_mm);  // U = (T Diag(beta)) V
   // the two terms of the state-gradient recursion that do not depend on it,
   // X = P^T dO and Y = Qt^T dO, so that its serial steps need only W and Ke.
   // They are stored transposed (X^T = dO^T P, Y^T = dO^T Qt): a chain lane's
@@ -1498,7 +1503,8 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   block_mm<C, D, D, false, true, BF, NT>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
   block_mm<C, D, D, false, true, BF, NT>(dw, D, dun, D, sc, D, -1.f, false, s_mm);  // -dUnew S^T
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
-  block_mm2<C, C, D, false, true, D, false, true, BF, NT>(s_dt, C, dw, D, p.kt, D, dun, D, p.vr, D,
+  block_mm2<C, C, D, false, true, D, false, true, BF, NT>(s_dt, C, dw, D, p.kt, D, dun, D,
+                                                      reinterpret_cast<const T *>(p.vr), D,
                                                       s_mm);
   for (int e = tid; e < CC; e += NT) s_dt[e] *= p.bt[e % C];
   __syncthreads();
