@@ -121,9 +121,10 @@ __device__ __forceinline__ f32x4 ld4(const bf16 *p) {
   return r;
 }
 
-template <int M, int N, int K, int NA, int NT, int CAP, typename AT, typename BT>
-__device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const AT *const *A, int lda,
-                                                 const BT *B, int ldb, float (&lds)[CAP]) {
+template <int M, int N, int K, int NA, int NT, int CAP, typename A0T, typename A1T, typename BT>
+__device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const A0T *A0, const A1T *A1,
+                                                 int lda, const BT *B, int ldb,
+                                                 float (&lds)[CAP]) {
   constexpr int NW = NT / 64;
   static_assert(K % 32 == 0, "contraction");
   constexpr int KB = 32, LB = KB + 8;
@@ -143,7 +144,8 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const AT *cons
     for (int p = 0; p < QA; ++p) {
       const int f = tid + NT * p;
       if (GA % NT == 0 || f < GA)
-        ra[a][p] = ld4(A[a] + (f / 8) * lda + k0 + 4 * (f % 8));
+        ra[a][p] = a == 0 ? ld4(A0 + (f / 8) * lda + k0 + 4 * (f % 8))
+                          : ld4(A1 + (f / 8) * lda + k0 + 4 * (f % 8));
     }
 #pragma unroll
     for (int p = 0; p < QB; ++p) {
@@ -216,13 +218,14 @@ __device__ __forceinline__ void mm_accumulate_bf(f32x4 *const *c, const AT *cons
 }
 
 template <int M, int N, int K, bool TA, bool TB, int NA, bool BF = false, int NT = 256, int CAP,
-          typename AT, typename BT>
-__device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const AT *const *A, int lda,
-                                                const BT *B, int ldb, float (&lds)[CAP]) {
+          typename A0T, typename A1T, typename BT>
+__device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const A0T *A0, const A1T *A1,
+                                                int lda, const BT *B, int ldb,
+                                                float (&lds)[CAP]) {
   constexpr int NW = NT / 64;
   static_assert(K % 16 == 0, "contraction");
   if constexpr (BF && !TA && TB && K % 32 == 0) {
-    mm_accumulate_bf<M, N, K, NA, NT>(c, A, lda, B, ldb, lds);
+    mm_accumulate_bf<M, N, K, NA, NT>(c, A0, A1, lda, B, ldb, lds);
     return;
   }
   constexpr int KS = K < 32 ? K : 32, LK = KS + 4;  // slice depth, row stride by rows
@@ -232,8 +235,10 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const AT *const
   constexpr int PA = (FA + NT - 1) / NT, PB = (FB + NT - 1) / NT;
   constexpr int SA = TA ? KS * LMA : M * LK, SB = TB ? N * LK : KS * LNB;
   static_assert(NA == 1 || NA == 2, "one or two left operands");
-  static_assert(SA + SB <= mm_lds<M, N, K>() && NA * SA + SB <= CAP &&
-                    (NA > 1 || mm_lds<M, N, K>() <= CAP),
+  // (the bf16 form above returned already; its own check is in mm_accumulate_bf)
+  static_assert((BF && !TA && TB && K % 32 == 0) ||
+                    (SA + SB <= mm_lds<M, N, K>() && NA * SA + SB <= CAP &&
+                     (NA > 1 || mm_lds<M, N, K>() <= CAP)),
                 "the caller's LDS buffer holds this product's staging");
   float *sb = lds + NA * SA;  // A[a]'s slice at lds + a * SA
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -248,10 +253,10 @@ __device__ __forceinline__ void mm_accumulate_n(f32x4 *const *c, const AT *const
       if (FA % NT == 0 || f < FA) {
         if (TA) {
           const int kk = f / (M / 4), i4 = f % (M / 4);
-          ra[a][p] = ld4(A[a] + (k0 + kk) * lda + 4 * i4);
+          ra[a][p] = a == 0 ? ld4(A0 + (k0 + kk) * lda + 4 * i4) : ld4(A1 + (k0 + kk) * lda + 4 * i4);
         } else {
           const int i = f / (KS / 4), k4 = f % (KS / 4);
-          ra[a][p] = ld4(A[a] + i * lda + k0 + 4 * k4);
+          ra[a][p] = a == 0 ? ld4(A0 + i * lda + k0 + 4 * k4) : ld4(A1 + i * lda + k0 + 4 * k4);
         }
       }
     }
@@ -370,8 +375,7 @@ template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, 
 __device__ __forceinline__ void mm_accumulate(f32x4 *c, const AT *A, int lda, const BT *B,
                                               int ldb, float (&lds)[CAP]) {
   f32x4 *const cs[1] = {c};
-  const AT *const as[1] = {A};
-  mm_accumulate_n<M, N, K, TA, TB, 1, BF, NT>(cs, as, lda, B, ldb, lds);
+  mm_accumulate_n<M, N, K, TA, TB, 1, BF, NT>(cs, A, A, lda, B, ldb, lds);
 }
 
 // out = alpha c + (init ? init : 0), tile by tile (init may be out itself;
@@ -444,16 +448,15 @@ __device__ __forceinline__ void block_mm2(float *out, int ldo, const A1T *A1, in
 // out1 = A1 B and out2 = A2 B (A1, A2 of the same shape and leading
 // dimension), staging B once.
 template <int M, int N, int K, bool TA, bool TB, bool BF = false, int NT = 256, int CAP,
-          typename AT, typename BT>
-__device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const AT *A1,
-                                              const AT *A2, int lda, const BT *B, int ldb,
+          typename A1T, typename A2T, typename BT>
+__device__ __forceinline__ void block_mm_pair(float *out1, float *out2, int ldo, const A1T *A1,
+                                              const A2T *A2, int lda, const BT *B, int ldb,
                                               float (&lds)[CAP]) {
   f32x4 c1[MmTiles<M, N, NT>::TPW], c2[MmTiles<M, N, NT>::TPW];
 #pragma unroll
   for (int q = 0; q < MmTiles<M, N, NT>::TPW; ++q) c1[q] = c2[q] = zero4();
   f32x4 *const cs[2] = {c1, c2};
-  const AT *const as[2] = {A1, A2};
-  mm_accumulate_n<M, N, K, TA, TB, 2, BF, NT>(cs, as, lda, B, ldb, lds);
+  mm_accumulate_n<M, N, K, TA, TB, 2, BF, NT>(cs, A1, A2, lda, B, ldb, lds);
   mm_store<M, N, NT>(out1, ldo, static_cast<const float *>(nullptr), 1.f, c1);
   mm_store<M, N, NT>(out2, ldo, static_cast<const float *>(nullptr), 1.f, c2);
 }
@@ -1497,11 +1500,25 @@ __global__ __launch_bounds__((bwd_threads<D, C>())) void bwd_grad_kernel(
   for (int e = tid; e < CC; e += NT)
     if (e % C > e / C) s_dp[e] = 0.f;  // dP: lower incl. diagonal
   __syncthreads();
-  // dQt = dO S^T + dP Kh
-  block_mm2<C, D, D, false, true, C, false, false, BF, NT>(dqt, D, dot, D, sc, D, s_dp, C, p.kh, D,
-                                                       s_mm);
+  // dQt = dO S^T + dP Kh and dW = -dUnew S^T; on the bf16 matrix cores one
+  // staging of S serves both (the fp32 form's staging of two left operands
+  // does not fit the LDS buffer)
+  if constexpr (BF) {
+    constexpr int TPW = MmTiles<C, D, NT>::TPW;
+    f32x4 cq[TPW], cw[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) cq[q] = cw[q] = zero4();
+    f32x4 *const cs[2] = {cq, cw};
+    mm_accumulate_n<C, D, D, false, true, 2, BF, NT>(cs, dot, dun, D, sc, D, s_mm);
+    mm_accumulate<C, D, C, false, false, BF, NT>(cq, s_dp, C, p.kh, D, s_mm);
+    mm_store<C, D, NT>(dqt, D, static_cast<const float *>(nullptr), 1.f, cq);
+    mm_store<C, D, NT>(dw, D, static_cast<const float *>(nullptr), -1.f, cw);
+  } else {
+    block_mm2<C, D, D, false, true, C, false, false, BF, NT>(dqt, D, dot, D, sc, D, s_dp, C, p.kh,
+                                                         D, s_mm);
+    block_mm<C, D, D, false, true, BF, NT>(dw, D, dun, D, sc, D, -1.f, false, s_mm);
+  }
   block_mm<C, D, D, false, true, BF, NT>(dke, D, unew, D, dse, D, 1.f, false, s_mm);  // Unew dS_next^T
-  block_mm<C, D, D, false, true, BF, NT>(dw, D, dun, D, sc, D, -1.f, false, s_mm);  // -dUnew S^T
   // dT = (dW Kt^T + dUnew V^T) Diag(beta)
   block_mm2<C, C, D, false, true, D, false, true, BF, NT>(s_dt, C, dw, D, p.kt, D, dun, D,
                                                       reinterpret_cast<const T *>(p.vr), D,
