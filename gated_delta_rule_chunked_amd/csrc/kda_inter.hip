@@ -36,6 +36,9 @@
 // and fenced with scheduling barriers so the compiler keeps them in place.
 // Workgroups of one (sequence, head) share blockIdx % 8 and therefore one
 // XCD and its L2, which serves the same W/Qt/Ke/P rows to all slices.
+// For bf16 operands with d = 128 and C = 64 on 16-column ring slices the
+// launch takes inter_split_kernel instead: the same chain with eight
+// wavefronts, four for Unew and O and four that own S (see there).
 // The output tile leaves in one of three forms (WIDE_O, DEFER_O below):
 // 16-byte row pieces of each wave's rows through LDS on wider slices and in
 // the one-buffer form; 16-byte row pieces of the whole tile, deferred to
@@ -490,6 +493,279 @@ __global__ __launch_bounds__(256) void inter_chunk_kernel(
   }
 }
 
+// Split-role form of the same chain, for 16-column slices of bf16 operands
+// with d = 128 and C = 64.  Eight wavefronts: waves 0-3 (the output role)
+// each own a token block rb and compute Unew = U - W S and O = Qt S + P Unew
+// for it; waves 4-7 (the state role) each own two channel blocks of S and
+// compute S <- Diag(e^{G_n}) S + Ke^T Unew.  The output product and the
+// state update then run side by side after the step's first barrier
+// instead of one after the other in the same waves, and eight waves issue
+// the step's loads.  The LDS exchanges, their barriers (two per step,
+// executed by every wave) and the fragment loads are those of
+// inter_chunk_kernel.
+template <typename T, int D, int C, bool WARM>
+__global__ __launch_bounds__(512) void inter_split_kernel(
+    const T *__restrict__ qt, const T *__restrict__ w, const T *__restrict__ ut,
+    const T *__restrict__ ket, const T *__restrict__ pm,
+    const float *__restrict__ gam, const int *__restrict__ cu,
+    const int *__restrict__ seq_first, int N, int H, int seq_len,
+    const float *__restrict__ s0, float *__restrict__ s_final,
+    const int *__restrict__ slots, int num_slots, const OptArgs in, T *__restrict__ o) {
+  using F = typename Frag<T>::type;
+  using V4 = typename Vec4<T>::type;
+  constexpr int NRB = C / 16, NCB = D / 16, CK = C, KD = D / 32, KC = C / 32;
+  constexpr int CBW = NCB / 4, NS = D / 16;
+  static_assert(NRB == 4 && NCB % 4 == 0 && C == 64, "four token blocks, whole channel blocks");
+  __shared__ V4 sS[NCB][64];  // S (operand type), one tile per channel block
+  __shared__ V4 sU[NRB][64];  // Unew (operand type), one tile per token block
+
+  if (inputs_rejected(in)) return;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int slice = local % NS, unit = local / NS;
+  const int pair = unit * 8 + xcd;
+  if (pair >= N * H) return;
+  const int seq = pair / H, h = pair % H;
+  const int lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());  // 0 .. 7
+  const bool out_role = wv < 4;
+  const int rw = out_role ? wv : wv - 4;  // token block (output) or channel-block group (state)
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col0 = slice * 16;
+
+  int t0, len, first;
+  if (cu) {
+    t0 = cu[seq];
+    len = cu[seq + 1] - t0;
+    first = len > 0 ? seq_first[seq] : 0;
+  } else {
+    t0 = seq * seq_len;
+    len = seq_len;
+    first = seq * ((seq_len + C - 1) / C);
+  }
+  const int nch = (len + C - 1) / C;
+  const int64_t rs = (int64_t)H * D;
+  int64_t spair = pair;
+  bool has_state = true;
+  if (slots) {
+    const int sl = slots[seq];
+    has_state = sl >= 0 && sl < num_slots;  // padding: zero start, no final write
+    spair = has_state ? (int64_t)sl * H + h : 0;
+  }
+
+  // the state role's channel blocks: S[j][i] = S[16 cb + 4 lg + i][col0 + lr], cb = rw CBW + j
+  f32x4 S[CBW];
+  const int64_t sbase = spair * D * D + col0 + lr;
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) {
+    S[j] = zero4();
+    if (!out_role) {
+      const int cb = rw * CBW + j;
+      if (s0 && has_state) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[j][i] = s0[sbase + (int64_t)(16 * cb + 4 * lg + i) * D];
+      }
+      sS[cb][lane] = vec4_from_f32<T>(S[j]);
+    }
+  }
+  __syncthreads();
+
+  // One chunk's operands for one wave: the output role's W, U, Qt and P rows
+  // of its token block, or the state role's Ke^T rows and e^{G_n}.  Each
+  // role runs its own copy of the chunk loop below (same steps, same two
+  // barriers per step), so that its register ring holds only its operands.
+  struct BufO {
+    F wA[KD], qA[KD], pA[KC];
+    V4 uv;
+  };
+  struct BufS {
+    F kA[CBW][KC];
+    float gl;
+    int warm;
+  };
+  auto tile_of = [&](int ci) { return (int64_t)(first + ci) * H + h; };
+  auto load_wu = [&](BufO &B, int ci) {
+    const int64_t tile = tile_of(ci);
+    const T *wt = w + tile * (C * D) + (rw * KD * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) B.wA[ks] = load8<T>(wt + ks * 512);
+    B.uv = load4<T>(ut + tile * (D * C) + ((slice * NRB + rw) * 64 + lane) * 4);
+  };
+  auto load_qp = [&](BufO &B, int ci) {
+    const int64_t tile = tile_of(ci);
+    const T *qq = qt + tile * (C * D) + (rw * KD * 64 + lane) * 8;
+    const T *pp = pm + tile * (C * CK) + (rw * KC * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) B.qA[ks] = load8<T>(qq + ks * 512);
+#pragma unroll
+    for (int ks = 0; ks < KC; ++ks) {  // P's zero K-steps past the block's last row are not loaded
+      if (32 * ks <= 16 * rw + 15) B.pA[ks] = load8<T>(pp + ks * 512);
+      else B.pA[ks] = F{};
+    }
+  };
+  auto load_kg = [&](BufS &B, int ci) {
+    const int64_t tile = tile_of(ci);
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const T *kk = ket + tile * (D * CK) + ((rw * CBW + j) * KC * 64 + lane) * 8;
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) B.kA[j][ks] = load8<T>(kk + ks * 512);
+    }
+    B.gl = gam[tile * D + 16 * (rw * CBW + min(lane >> 4, CBW - 1)) + (lane & 15)];
+  };
+  // L2 warm-up (WARM): the state role reads one dword of each line of its
+  // slice's share of a later chunk's W, Qt, Ke^T and P lines
+  constexpr int LQ = C * D * (int)sizeof(T) / 128, LK = D * CK * (int)sizeof(T) / 128,
+                LP = C * CK * (int)sizeof(T) / 128, NL = 2 * LQ + LK + LP;
+  constexpr int NLW = (NL + NS - 1) / NS, NLV = (NLW + 3) / 4;
+  static_assert(!WARM || NLV <= 64, "one warm-up load per wave and chunk");
+  const int wli = min(slice * NLW + rw * NLV + min(lane, NLV - 1), NL - 1);
+  auto warm_load = [&](int ci) -> int {
+    const int64_t tile = tile_of(ci);
+    const char *p;
+    if (wli < LQ)
+      p = reinterpret_cast<const char *>(w + tile * (C * D)) + wli * 128;
+    else if (wli < 2 * LQ)
+      p = reinterpret_cast<const char *>(qt + tile * (C * D)) + (wli - LQ) * 128;
+    else if (wli < 2 * LQ + LK)
+      p = reinterpret_cast<const char *>(ket + tile * (D * CK)) + (wli - 2 * LQ) * 128;
+    else
+      p = reinterpret_cast<const char *>(pm + tile * (C * CK)) + (wli - 2 * LQ - LK) * 128;
+    return *reinterpret_cast<const int *>(p);
+  };
+
+  // Full chunks three at a time with nothing conditional in the loop body,
+  // then the last one to three chunks (the partial one included).
+  const int nfull = len / C;
+  auto chunk_loop = [&](auto &B0, auto &B1, auto &B2, auto step) {
+    int ci = 0;
+    for (; ci + 3 <= nfull; ci += 3) {
+      step(B0, ci, StepKind<true>{});
+      step(B1, ci + 1, StepKind<true>{});
+      step(B2, ci + 2, StepKind<true>{});
+    }
+    if (ci < nch) step(B0, ci, StepKind<false>{});
+    if (ci + 1 < nch) step(B1, ci + 1, StepKind<false>{});
+    if (ci + 2 < nch) step(B2, ci + 2, StepKind<false>{});
+  };
+
+  if (out_role) {
+    auto step = [&](BufO &B, int ci, auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const int nxt = min(ci + 3, nch - 1);
+      const int tc = t0 + ci * C;
+      const int rows = FULL ? C : min(C, len - ci * C);
+      // Unew = U - W S for the token block (two accumulators)
+      F sb[KD];
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) sb[ks] = join4(sS[2 * ks][lane], sS[2 * ks + 1][lane]);
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) {
+        if (ks & 1) a1 = mma_k32(B.wA[ks], sb[ks], a1);
+        else a0 = mma_k32(B.wA[ks], sb[ks], a0);
+      }
+      sU[rw][lane] = vec4_from_f32<T>(to_f32x4(B.uv) - (a0 + a1));
+      __builtin_amdgcn_sched_barrier(0);
+      load_wu(B, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      // O = Qt S + P Unew for the token block, stored straight from the tile
+      F ub[KC];
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) ub[ks] = join4(sU[2 * ks][lane], sU[2 * ks + 1][lane]);
+      f32x4 oc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KD; ++ks) oc = mma_k32(B.qA[ks], sb[ks], oc);
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
+      const V4 ov = vec4_from_f32<T>(oc + 0.f);  // a real VALU read before any branch
+      T *op = o + (int64_t)(tc + 16 * rw + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
+      if (FULL || rows == C) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[i * rs] = ov[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * rw + 4 * lg + i < rows) op[i * rs] = ov[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_qp(B, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+    };
+    BufO B0, B1, B2;
+    if (nch > 0) {
+      load_wu(B0, 0);
+      load_qp(B0, 0);
+      load_wu(B1, min(1, nch - 1));
+      load_qp(B1, min(1, nch - 1));
+      load_wu(B2, min(2, nch - 1));
+      load_qp(B2, min(2, nch - 1));
+    }
+    chunk_loop(B0, B1, B2, step);
+  } else {
+    int warm_sink = 0;
+    auto step = [&](BufS &B, int ci, auto full) {
+      const int nxt = min(ci + 3, nch - 1);
+      lds_barrier();  // Unew of the chunk is in LDS
+      F ub[KC];
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) ub[ks] = join4(sU[2 * ks][lane], sU[2 * ks + 1][lane]);
+      // S <- Diag(e^{G_n}) S + Ke^T Unew for the wave's channel blocks
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        const int cb = rw * CBW + j;
+        f32x4 gj;  // e^{G_n} of rows 16 cb + 4 lg + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          gj[i] = __int_as_float(
+              __builtin_amdgcn_ds_bpermute((16 * j + 4 * lg + i) * 4, __float_as_int(B.gl)));
+        f32x4 acc = S[j] * gj;
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks) acc = mma_k32(B.kA[j][ks], ub[ks], acc);
+        S[j] = acc + 0.f;  // a real VALU read before any branch
+        sS[cb][lane] = vec4_from_f32<T>(S[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_kg(B, nxt);
+      if constexpr (WARM) {  // the warm-up load issued three steps ago has landed
+        warm_sink ^= B.warm;
+        B.warm = warm_load(min(ci + 3 + WARM_AHEAD, nch - 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      (void)full;
+    };
+    BufS B0, B1, B2;
+    B0.warm = B1.warm = B2.warm = 0;
+    if (nch > 0) {
+      load_kg(B0, 0);
+      load_kg(B1, min(1, nch - 1));
+      load_kg(B2, min(2, nch - 1));
+      if constexpr (WARM) {
+        B0.warm = warm_load(min(3, nch - 1));
+        B1.warm = warm_load(min(4, nch - 1));
+        B2.warm = warm_load(min(5, nch - 1));
+      }
+    }
+    chunk_loop(B0, B1, B2, step);
+    if constexpr (WARM) {
+      warm_sink ^= B0.warm ^ B1.warm ^ B2.warm;
+      asm volatile("" ::"v"(warm_sink));
+    }
+  }
+
+  if (!out_role && s_final && has_state) {
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int cb = rw * CBW + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_final[sbase + (int64_t)(16 * cb + 4 * lg + i) * D] = S[j][i];
+    }
+  }
+}
+
 // Compute units of the current device (0 if unknown), looked up once per
 // device ordinal.
 int device_cus() {
@@ -511,6 +787,26 @@ static hipError_t launch_inter_ct(const FwdArgs &a) {
   const dim3 grid((unsigned)(8 * units * NS));
   char *ws = a.ws;
   hipLaunchKernelGGL((inter_chunk_kernel<T, D, C, PF, CT, WARM>), grid, dim3(256), 0, a.stream,
+                     reinterpret_cast<const T *>(ws + a.lay.qt),
+                     reinterpret_cast<const T *>(ws + a.lay.w),
+                     reinterpret_cast<const T *>(ws + a.lay.ut),
+                     reinterpret_cast<const T *>(ws + a.lay.ket),
+                     reinterpret_cast<const T *>(ws + a.lay.p),
+                     reinterpret_cast<const float *>(ws + a.lay.gam), a.cu_seqlens,
+                     reinterpret_cast<const int *>(ws + a.lay.seq_first), a.num_seqs,
+                     a.num_heads, a.seq_len, a.s0, a.s_final, a.in.slots, a.in.num_slots,
+                     a.in, reinterpret_cast<T *>(a.o));
+  return hipGetLastError();
+}
+
+template <typename T, int D, int C, bool WARM>
+static hipError_t launch_inter_split(const FwdArgs &a) {
+  constexpr int NS = D / 16;
+  const int pairs = a.num_seqs * a.num_heads;
+  const int units = (pairs + 7) / 8;
+  const dim3 grid((unsigned)(8 * units * NS));
+  char *ws = a.ws;
+  hipLaunchKernelGGL((inter_split_kernel<T, D, C, WARM>), grid, dim3(512), 0, a.stream,
                      reinterpret_cast<const T *>(ws + a.lay.qt),
                      reinterpret_cast<const T *>(ws + a.lay.w),
                      reinterpret_cast<const T *>(ws + a.lay.ut),
@@ -562,8 +858,15 @@ static hipError_t launch_inter_c(const FwdArgs &a) {
   // L2 warm-up loads on 16-column slices of long chains (mean sequence
   // length of at least WARM_MIN_CHUNKS chunks)
   constexpr int64_t WARM_MIN_CHUNKS = 128;
-  if (a.total_tokens >= WARM_MIN_CHUNKS * C * (int64_t)a.num_seqs)
-    return launch_inter_ct<T, D, C, 1, 3, true>(a);
+  const bool warm = a.total_tokens >= WARM_MIN_CHUNKS * C * (int64_t)a.num_seqs;
+  // bf16, d = 128, C = 64: the split-role form (measured on MI355X: the
+  // B=1 H=32 T=32768 chain 512 -> 497 us, B=2 H=8 T=2048 25.6 -> 23.3 us,
+  // outputs bitwise equal)
+  if constexpr (sizeof(T) == 2 && D == 128 && C == 64) {
+    if (warm) return launch_inter_split<T, D, C, true>(a);
+    return launch_inter_split<T, D, C, false>(a);
+  }
+  if (warm) return launch_inter_ct<T, D, C, 1, 3, true>(a);
   return launch_inter_ct<T, D, C, 1, 3, false>(a);
 }
 
