@@ -62,21 +62,26 @@ def test_decode_state_slots(dtype, d):
     assert relerr(got, ref) <= TOL[dtype]
 
 
-def test_prefill_state_slots_in_place():
+@pytest.mark.parametrize("d,chunk,lengths", [
+    (64, 32, [70, 33, 50, 1]),
+    # the split-role chain (bf16, d = 128, C = 64), without and with L2 warm-up loads
+    (128, 64, [700, 330, 500, 10]),
+    (128, 64, [9000, 8700, 8400, 8300]),
+], ids=["d64_c32", "d128_c64", "d128_c64_long"])
+def test_prefill_state_slots_in_place(d, chunk, lengths):
     """Four packed sequences whose states live in slots 5, 0, (padding -1)
     and 2 of a pool of 6, updated in place.  The padding sequence starts from
     zero and writes no state; slots 1, 3, 4 are untouched."""
-    print("[serving] prefill slots", flush=True)
+    print(f"[serving] prefill slots d={d} chunk={chunk} lengths={lengths}", flush=True)
     kda = _kda()
-    H, d, NS = 2, 64, 6
-    w = kin.make_prefill(31, H=H, d=d, dtype=kin.BF16, chunk_size=32,
-                         lengths=[70, 33, 50, 1])
+    H, NS = 2, 6
+    w = kin.make_prefill(31, H=H, d=d, dtype=kin.BF16, chunk_size=chunk, lengths=lengths)
     pool0 = kin.decode_states(NS, H, d, seed=31)
     slots = np.array([5, 0, -1, 2], dtype=np.int32)
     dd = upload_prefill(w)
     pool = f32_device(pool0)
     o, _ = kda.fwd_chunked(dd["q"], dd["k"], dd["v"], dd["log_alpha"], dd["beta"],
-                           cu_seqlens=dd["cu_seqlens"], initial_state=pool, chunk_size=32,
+                           cu_seqlens=dd["cu_seqlens"], initial_state=pool, chunk_size=chunk,
                            state_slots=torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
     q, k, v, g, b, _ = w.f64()
