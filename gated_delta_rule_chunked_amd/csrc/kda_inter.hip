@@ -620,10 +620,19 @@ __global__ __launch_bounds__(512) void inter_split_kernel(
   constexpr int NLW = (NL + NS - 1) / NS, NLV = (NLW + 3) / 4;
   static_assert(!WARM || NLV <= 64, "one warm-up load per wave and chunk");
   const int wli = min(slice * NLW + rw * NLV + min(lane, NLV - 1), NL - 1);
+  // and the slice's own U lines (2 KiB per chunk: 16 lines, 4 per state
+  // wave) in lanes NLV ..; no other slice reads them, so without this their
+  // every load waits for HBM (long chain 496 -> 481 us)
+  constexpr int LUW = C * 16 * (int)sizeof(T) / 128 / 4;
+  static_assert(NLV + LUW <= 64, "warm-up lanes");
+  const bool wu_lane = lane >= NLV && lane < NLV + LUW;
+  const int wul = rw * LUW + (lane - NLV);
   auto warm_load = [&](int ci) -> int {
     const int64_t tile = tile_of(ci);
     const char *p;
-    if (wli < LQ)
+    if (wu_lane)
+      p = reinterpret_cast<const char *>(ut + tile * (D * C) + slice * NRB * 64 * 4) + wul * 128;
+    else if (wli < LQ)
       p = reinterpret_cast<const char *>(w + tile * (C * D)) + wli * 128;
     else if (wli < 2 * LQ)
       p = reinterpret_cast<const char *>(qt + tile * (C * D)) + (wli - LQ) * 128;
