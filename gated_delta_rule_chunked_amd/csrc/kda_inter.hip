@@ -518,6 +518,13 @@ __global__ __launch_bounds__(512) void inter_split_kernel(
   static_assert(NRB == 4 && NCB % 4 == 0 && C == 64, "four token blocks, whole channel blocks");
   __shared__ V4 sS[NCB][64];  // S (operand type), one tile per channel block
   __shared__ V4 sU[NRB][64];  // Unew (operand type), one tile per token block
+  // Long chains (WARM) store each wave's output tile as 16-byte row pieces
+  // through LDS: a quarter of the store instructions through the vector-
+  // memory path that bounds the step (long chain 481.8 -> 478.2 us); on
+  // shorter chains the direct two-byte stores measured faster (23.3 vs 24.3 us).
+  constexpr bool WO = WARM;
+  constexpr int LDO = 16 + 16 / (int)sizeof(T);  // padded row of a wave's output tile
+  __shared__ __align__(16) T sO[WO ? 4 : 1][16][WO ? LDO : 1];
 
   if (inputs_rejected(in)) return;
   const int b = blockIdx.x;
@@ -689,14 +696,27 @@ __global__ __launch_bounds__(512) void inter_split_kernel(
 #pragma unroll
       for (int ks = 0; ks < KC; ++ks) oc = mma_k32(B.pA[ks], ub[ks], oc);
       const V4 ov = vec4_from_f32<T>(oc + 0.f);  // a real VALU read before any branch
-      T *op = o + (int64_t)(tc + 16 * rw + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
-      if (FULL || rows == C) {
+      if constexpr (WO) {
+        // the wave's 16 x 16 tile through its own LDS rows, out as 16-byte pieces
 #pragma unroll
-        for (int i = 0; i < 4; ++i) op[i * rs] = ov[i];
+        for (int i = 0; i < 4; ++i) sO[rw][4 * lg + i][lr] = ov[i];
+        __builtin_amdgcn_wave_barrier();
+        if (lane < 32) {
+          const int r = lane >> 1, c8 = 8 * (lane & 1);
+          if (FULL || 16 * rw + r < rows)
+            *reinterpret_cast<uint4 *>(o + (int64_t)(tc + 16 * rw + r) * rs + (int64_t)h * D + col0 +
+                                       c8) = *reinterpret_cast<const uint4 *>(&sO[rw][r][c8]);
+        }
       } else {
+        T *op = o + (int64_t)(tc + 16 * rw + 4 * lg) * rs + (int64_t)h * D + col0 + lr;
+        if (FULL || rows == C) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * rw + 4 * lg + i < rows) op[i * rs] = ov[i];
+          for (int i = 0; i < 4; ++i) op[i * rs] = ov[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * rw + 4 * lg + i < rows) op[i * rs] = ov[i];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       load_qp(B, nxt);
